@@ -1,0 +1,227 @@
+"""fp64 reference for the cache write, decode attention and causal packed prefill.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Parity is pinned by
+tests/test_oracle_attention.py.
+
+Layouts ([vllm] §3.3):
+  NHD  cache[num_blocks, block_size, num_kv_heads, head_size]
+  HND  cache[num_blocks, num_kv_heads, block_size, head_size]  (head-major)
+
+Caches are handled as raw bit arrays (uint32 for float32, uint16 for
+bfloat16/float16) so the write is a bit copy; attention upcasts the bits to
+float64 exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NHD, HND = 0, 1
+
+
+def bits_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of stored values to float64.
+
+    dtype "f32": float32 values (or their uint32 bits); "bf16": uint16 bit
+    patterns of bfloat16 (the upper half of a float32); "f16": uint16 bits of
+    IEEE half.
+    """
+    if dtype == "f32":
+        return np.asarray(a).view(np.float32).astype(np.float64) if a.dtype != np.float32 \
+            else a.astype(np.float64)
+    if dtype == "bf16":
+        return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)) \
+            .view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _raw(a: np.ndarray) -> np.ndarray:
+    """View float arrays as same-width unsigned bits (bit-copy semantics)."""
+    if a.dtype == np.float32:
+        return a.view(np.uint32)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    return a
+
+
+# --------------------------------------------------------------------- write
+def write_ref(key_cache, value_cache, key, value, slot_mapping, block_size, layout=NHD):
+    """Scatter new tokens' K/V rows into copies of the block pool.
+
+    [vllm] §3.2 and §7.4: each token i carries a global slot
+    ``slot = block_number * block_size + block_offset``; a negative slot marks
+    a padding token, which is skipped.  Row i ([num_kv_heads, head_size]) is
+    copied bit for bit to (block = slot // block_size, offset = slot %
+    block_size); every other slot of the pool is left as it was.  Non-negative
+    slots must be distinct (asserted).
+
+    Returns (new_key_cache, new_value_cache) as raw bit arrays.
+    """
+    kc = _raw(np.array(key_cache, copy=True))
+    vc = _raw(np.array(value_cache, copy=True))
+    k = _raw(np.asarray(key))
+    v = _raw(np.asarray(value))
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    live = slots[slots >= 0]
+    assert len(np.unique(live)) == len(live), "duplicate slots"
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        b, o = divmod(int(s), block_size)
+        if layout == NHD:
+            kc[b, o] = k[i]
+            vc[b, o] = v[i]
+        else:
+            kc[b, :, o] = k[i]
+            vc[b, :, o] = v[i]
+    return kc, vc
+
+
+# -------------------------------------------------------------------- gather
+def gather_seq(cache, block_table_row, L, block_size, layout=NHD):
+    """Logical rows 0..L-1 of one sequence, read through its block table.
+
+    [k4i] #the-block-table and [vllm] §3.1: token t lives in physical block
+    ``block_table[t // block_size]`` at offset ``t % block_size``.  Entries of
+    the table past ceil(L / block_size) are never read.  Returns raw rows
+    [L, num_kv_heads, head_size].
+    """
+    t = np.arange(int(L))
+    blk = np.asarray(block_table_row)[t // block_size]
+    off = t % block_size
+    if layout == NHD:
+        return cache[blk, off]
+    return cache[blk, :, off]
+
+
+# ----------------------------------------------------------------- attention
+def attention_dense(q, K, V, scale):
+    """softmax(scale * K q) V for one query over contiguous K, V (float64).
+
+    This is the plain definition the paged kernels must reproduce ([tut] §3.4:
+    paging does not change the attention math; [k4i] #paged-attention-kernel:
+    the block-wise computation equals softmax over the concatenated sequence).
+    Returns (out [D], p [L]).  With no keys (L = 0) the output is 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[-1]), np.zeros(0)
+    z = scale * (K @ q)
+    w = np.exp(z - z.max())
+    p = w / w.sum()
+    return p @ V, p
+
+
+def decode_ref(query, key_cache, value_cache, block_tables, context_lens, scale,
+               block_size, dtype, layout=NHD, return_probs=False):
+    """Decode attention over the paged cache, float64.
+
+    For sequence s and query head h: kv head ``h // (H / Hkv)`` (contiguous
+    GQA groups), keys/values are the first ``context_lens[s]`` logical tokens
+    gathered through ``block_tables[s]`` ([vllm] §3.1, §6.2 with
+    ``seqlen_k = seq_lens``), and the output is ``attention_dense``.
+    ``query`` is [S, H, D] raw; returns out [S, H, D] (and the probability
+    vectors per (s, h) if asked).
+    """
+    qf = bits_to_f64(np.asarray(query), dtype)
+    S, H, D = qf.shape
+    Hkv = key_cache.shape[2] if layout == NHD else key_cache.shape[1]
+    G = H // Hkv
+    out = np.zeros((S, H, D))
+    probs = {}
+    for s in range(S):
+        L = int(context_lens[s])
+        K = bits_to_f64(gather_seq(key_cache, block_tables[s], L, block_size, layout), dtype)
+        V = bits_to_f64(gather_seq(value_cache, block_tables[s], L, block_size, layout), dtype)
+        for h in range(H):
+            o, p = attention_dense(qf[s, h], K[:, h // G], V[:, h // G], scale)
+            out[s, h] = o
+            if return_probs:
+                probs[(s, h)] = p
+    return (out, probs) if return_probs else out
+
+
+def prefill_ref(query, key_cache, value_cache, block_tables, query_start_loc, context_lens,
+                scale, block_size, dtype, layout=NHD):
+    """Causal packed-sequence prefill over the paged cache, float64.
+
+    Queries of all sequences are packed without padding; sequence s owns rows
+    ``query_start_loc[s] .. query_start_loc[s+1]-1`` ([packed] §2.3; [vllm]
+    §5.4 ``query_start_loc``).  With n = that row count and L =
+    ``context_lens[s]`` (all L tokens already cached), row j is the token at
+    absolute position ``L - n + j`` and attends to keys 0 .. L - n + j (causal,
+    aligned to the end of the context: [vllm] §6.2 ``causal=True`` with
+    ``seqlen_k = seq_lens``).  Returns out [num_tokens, H, D].
+    """
+    qf = bits_to_f64(np.asarray(query), dtype)
+    T, H, D = qf.shape
+    Hkv = key_cache.shape[2] if layout == NHD else key_cache.shape[1]
+    G = H // Hkv
+    out = np.zeros((T, H, D))
+    qsl = np.asarray(query_start_loc)
+    for s in range(len(qsl) - 1):
+        n = int(qsl[s + 1] - qsl[s])
+        L = int(context_lens[s])
+        assert n <= L
+        K = bits_to_f64(gather_seq(key_cache, block_tables[s], L, block_size, layout), dtype)
+        V = bits_to_f64(gather_seq(value_cache, block_tables[s], L, block_size, layout), dtype)
+        for j in range(n):
+            a = L - n + j  # absolute position of query row j
+            for h in range(H):
+                o, _ = attention_dense(qf[qsl[s] + j, h], K[:a + 1, h // G], V[:a + 1, h // G], scale)
+                out[qsl[s] + j, h] = o
+    return out
+
+
+# ------------------------------------------------ block-wise form (cross-check)
+def online_softmax_blocks(q, K, V, scale, block):
+    """Block-by-block online softmax ([k4i] #paged-attention-kernel).
+
+    Running max m, normaliser l and unnormalised output o start at
+    (-inf, 0, 0).  For each block j of ``block`` consecutive keys: a_j =
+    scale * K_j q, m_j = max a_j, l_j = sum exp(a_j - m_j), o_j = exp(a_j -
+    m_j) V_j; then with m' = max(m, m_j): l <- e^(m-m') l + e^(m_j-m') l_j,
+    o <- e^(m-m') o + e^(m_j-m') o_j, m <- m'.  The result is o / l.
+    Written out in float64 only to pin the identity with ``attention_dense``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    m, l, o = -np.inf, 0.0, np.zeros(V.shape[-1])
+    for b0 in range(0, K.shape[0], block):
+        a = scale * (K[b0:b0 + block] @ q)
+        m_j = a.max()
+        e = np.exp(a - m_j)
+        l_j = e.sum()
+        o_j = e @ V[b0:b0 + block]
+        m_new = max(m, m_j)
+        c_old = np.exp(m - m_new) if m != -np.inf else 0.0
+        c_new = np.exp(m_j - m_new)
+        l = c_old * l + c_new * l_j
+        o = c_old * o + c_new * o_j
+        m = m_new
+    return o / l if l > 0 else o
+
+
+def partition_stats(q, K, V, scale):
+    """Per-partition statistics (m_p, l_p, o_p) of split-K decode ([vllm] §7.3,
+    V2): m_p = max of the partition's scores, l_p = sum exp(score - m_p),
+    o_p = sum exp(score - m_p) v (unnormalised)."""
+    q = np.asarray(q, dtype=np.float64)
+    a = scale * (np.asarray(K, dtype=np.float64) @ q)
+    m = a.max()
+    e = np.exp(a - m)
+    return m, e.sum(), e @ np.asarray(V, dtype=np.float64)
+
+
+def merge_partitions(stats):
+    """Reduce step of split-K ([vllm] §7.3: rescale each partition by its max
+    and merge with the online-softmax correction): M = max_p m_p, out =
+    sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p."""
+    M = max(m for m, _, _ in stats)
+    num = sum(np.exp(m - M) * o for m, _, o in stats)
+    den = sum(np.exp(m - M) * l for m, l, _ in stats)
+    return num / den
