@@ -131,14 +131,14 @@ def test_mean_internal_fragmentation_is_half_a_block():
     """[k4i] memory utilization: the last block is on average half full."""
     rng = np.random.default_rng(2)
     bs = 16
-    lens = rng.integers(1, 5000, 20000)
+    lens = rng.integers(1, 1000, 6000)
     m = _model(int(sum(-(-L // bs) for L in lens)), bs)
     waste = []
     for L in lens:
         s = m.add_seq()
         m.append(s, int(L))
         waste.append(len(m.block_table(s)) * bs - L)
-    assert abs(np.mean(waste) - (bs - 1) / 2) < 0.15
+    assert abs(np.mean(waste) - (bs - 1) / 2) < 0.3
 
 
 def test_shared_prefix_workload_refcounts():

@@ -10,9 +10,10 @@ the oracle through its own allocator model) and the tests compare the two.
 Values follow the workloads named for the method (decode of 7B-like and
 70B-like layers, long-context split-K decode, shared-prefix + packed prefill):
 N(0, 1) drawn in float32, rounded to bfloat16 (round-to-nearest-even) for the
-bf16 workloads.  Large per-sequence K/V arrays come from child streams
-``default_rng([seed, tag, seq])`` so that any one sequence can be re-drawn
-alone, at any size, without drawing the others.
+bf16 workloads.  Per-sequence K/V values come from child streams
+``default_rng([seed, tag, seq, chunk])``, one per CHUNK positions, and the
+queries from ``default_rng([seed, tag])``, so any slice of any sequence can be
+re-drawn alone, at any size, without drawing the rest.
 """
 from __future__ import annotations
 
@@ -25,6 +26,7 @@ import numpy as np
 # stream tags for the child generators
 _TAG_K, _TAG_V, _TAG_PAD, _TAG_Q = 1, 2, 3, 4
 _TAG_PREFIX = 1 << 20  # sequence index used for the shared prefix stream
+CHUNK = 128            # positions per K/V child stream
 
 F32, BF16 = "f32", "bf16"
 
@@ -66,7 +68,7 @@ class Workload:
     NB: int                   # usable blocks; the pool tensor has NB + 1 blocks (last = poison)
     context_lens: np.ndarray  # int32 [S]: tokens attended (decode: includes the new token)
     free_order: np.ndarray    # int32 [NB]: order in which the allocator hands out blocks
-    query: np.ndarray         # [S, H, D] (decode) or [T, H, D] packed (prefill)
+    query_shape: Tuple[int, int, int]  # [S, H, D] (decode) or [T, H, D] packed (prefill)
     # decode: write rows (new tokens + padding); prefill: packed new tokens
     row_seq: np.ndarray       # int32 [T]: sequence of each new-token row, -1 for padding
     row_pos: np.ndarray       # int32 [T]: absolute position of the row's token, -1 for padding
@@ -76,37 +78,60 @@ class Workload:
     prefix_len: int = 0       # shared prefix length (all sequences share it), 0 = none
     partition_size: int = 0   # split-K partition size named by the workload (0 = none)
     notes: Dict[str, object] = field(default_factory=dict)
+    _query: Optional[np.ndarray] = field(default=None, repr=False)
 
     # ------------------------------------------------------------------ K/V
     def kv(self, s: int, lo: int = 0, hi: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
         """Logical K and V of sequence s for positions [lo, hi): arrays [n, Hkv, D].
 
-        Positions below ``prefix_len`` come from the shared prefix stream, the
-        rest from the sequence's own stream (position prefix_len is its row 0).
+        Positions below ``prefix_len`` come from the shared prefix streams, the
+        rest from the sequence's own streams (position prefix_len is its row 0).
+        Each stream covers CHUNK positions, so a slice draws only what it needs.
         """
         L = int(self.context_lens[s])
-        hi = L if hi is None else hi
+        hi = L if hi is None else int(hi)
+        lo = int(lo)
         assert 0 <= lo <= hi <= L
-        parts_k, parts_v = [], []
         P = self.prefix_len
+        parts_k, parts_v = [], []
         if lo < P:
-            k, v = self._stream(_TAG_PREFIX, P)
-            parts_k.append(k[lo:min(hi, P)])
-            parts_v.append(v[lo:min(hi, P)])
+            k, v = self._range(_TAG_PREFIX, lo, min(hi, P))
+            parts_k.append(k)
+            parts_v.append(v)
         if hi > P:
-            k, v = self._stream(s, L - P)
-            a = max(lo, P) - P
-            parts_k.append(k[a:hi - P])
-            parts_v.append(v[a:hi - P])
+            k, v = self._range(s, max(lo, P) - P, hi - P)
+            parts_k.append(k)
+            parts_v.append(v)
         if len(parts_k) == 1:
             return parts_k[0], parts_v[0]
+        if not parts_k:
+            return self._range(s, 0, 0)
         return np.concatenate(parts_k), np.concatenate(parts_v)
 
-    def _stream(self, idx: int, n: int):
-        shape = (n, self.Hkv, self.D)
-        k = _normal(np.random.default_rng([self.seed, _TAG_K, idx]), shape, self.dtype)
-        v = _normal(np.random.default_rng([self.seed, _TAG_V, idx]), shape, self.dtype)
-        return k, v
+    def _range(self, idx: int, lo: int, hi: int):
+        dt = np.float32 if self.dtype == F32 else np.uint16
+        n = hi - lo
+        K = np.empty((n, self.Hkv, self.D), dt)
+        V = np.empty((n, self.Hkv, self.D), dt)
+        c = lo // CHUNK
+        while c * CHUNK < hi:
+            a, b = c * CHUNK, (c + 1) * CHUNK
+            shape = (CHUNK, self.Hkv, self.D)
+            k = _normal(np.random.default_rng([self.seed, _TAG_K, idx, c]), shape, self.dtype)
+            v = _normal(np.random.default_rng([self.seed, _TAG_V, idx, c]), shape, self.dtype)
+            x0, x1 = max(a, lo), min(b, hi)
+            K[x0 - lo:x1 - lo] = k[x0 - a:x1 - a]
+            V[x0 - lo:x1 - lo] = v[x0 - a:x1 - a]
+            c += 1
+        return K, V
+
+    @property
+    def query(self) -> np.ndarray:
+        """Queries, drawn from their own stream (cached after the first use)."""
+        if self._query is None:
+            self._query = _normal(np.random.default_rng([self.seed, _TAG_Q]), self.query_shape,
+                                  self.dtype)
+        return self._query
 
     # ------------------------------------------------------------ new rows
     def new_rows(self) -> Tuple[np.ndarray, np.ndarray]:
@@ -207,9 +232,7 @@ def _build_decode(cfg, seed, sp) -> Workload:
     # 2. pool and the allocator's free order
     NB = sp.get("pool_blocks") or _pool_blocks(lens, sp["bs"], sp.get("pool_factor", 1.2))
     free_order = rng.permutation(NB).astype(np.int32)
-    # 3. queries (one new token per sequence)
-    q = _normal(rng, (S, sp["H"], sp["D"]), sp["dtype"])
-    # 4./5. new-token rows and padding rows
+    # 3. new-token rows and padding rows (queries and K/V come from child streams)
     n_pad = int(sp.get("n_pad", 0))
     row_seq, row_pos = _decode_rows(rng, S, lens, n_pad)
     prng = np.random.default_rng([seed, _TAG_PAD])
@@ -217,7 +240,7 @@ def _build_decode(cfg, seed, sp) -> Workload:
     pad_v = _normal(prng, (n_pad, sp["Hkv"], sp["D"]), sp["dtype"])
     return Workload(cfg=cfg, name=sp["name"], kind="decode", dtype=sp["dtype"], seed=seed,
                     S=S, H=sp["H"], Hkv=sp["Hkv"], D=sp["D"], bs=sp["bs"], NB=NB,
-                    context_lens=lens, free_order=free_order, query=q,
+                    context_lens=lens, free_order=free_order, query_shape=(S, sp["H"], sp["D"]),
                     row_seq=row_seq, row_pos=row_pos, pad_k=pad_k, pad_v=pad_v,
                     partition_size=int(sp.get("partition_size", 0)))
 
@@ -256,13 +279,12 @@ def _build_shared(cfg, seed, sp) -> Workload:
     qsl = np.zeros(S + 1, np.int32)
     qsl[1:] = np.cumsum(qlens)
     if variant == "5a":
-        q = _normal(rng, (S, H, D), sp["dtype"])
+        qshape = (S, H, D)
         row_seq = np.arange(S, dtype=np.int32)
         row_pos = (lens - 1).astype(np.int32)
         kind, q_start = "decode", None
     else:
-        T = int(qsl[-1])
-        q = _normal(rng, (T, H, D), sp["dtype"])
+        qshape = (int(qsl[-1]), H, D)
         row_seq = np.repeat(np.arange(S, dtype=np.int32), qlens)
         row_pos = np.concatenate([np.arange(L - n, L, dtype=np.int32)
                                   for L, n in zip(lens, qlens)]) if S else np.zeros(0, np.int32)
@@ -270,7 +292,7 @@ def _build_shared(cfg, seed, sp) -> Workload:
     empty = np.zeros((0, Hkv, D), np.uint16 if sp["dtype"] == BF16 else np.float32)
     return Workload(cfg=cfg, name=sp["name"], kind=kind, dtype=sp["dtype"], seed=seed,
                     S=S, H=H, Hkv=Hkv, D=D, bs=bs, NB=NB, context_lens=lens,
-                    free_order=free_order, query=q, row_seq=row_seq, row_pos=row_pos,
+                    free_order=free_order, query_shape=qshape, row_seq=row_seq, row_pos=row_pos,
                     pad_k=empty, pad_v=empty, query_start_loc=q_start, prefix_len=prefix,
                     notes={"suffix_lens": qlens})
 
