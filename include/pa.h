@@ -1,0 +1,252 @@
+/*
+ * pa.h -- C ABI of libpagedattn.so, a paged KV-cache attention library for
+ * AMD MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [vllm]   "PagedAttention 在 vLLM 中的实现分析" (blog.chen3feng.top):
+ *            §3.1 block table, §3.2 slot mapping, §3.3 KV cache layouts,
+ *            §4.1 block pool, §5.4 CommonAttentionMetadata, §6.2 forward with
+ *            flash_attn_varlen_func(block_table=..., causal=True), §6.3
+ *            reshape_and_cache_flash, §7.3 V1/V2 kernels, §7.4 cache write.
+ *   [k4i]    "Paged attention" post (k4i.top): block table, block manager,
+ *            attention over non-contiguous blocks (online softmax), copy-on-write.
+ *   [atb]    ATB PagedAttention + virtual memory article (2048ai.net):
+ *            reference counting, copy-on-write.
+ *   [packed] cann-recipes-infer Paged KV Cache + Packed Sequence notes
+ *            (m.xxqk.cn): §2.3 packed sequences and their offsets.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are HIP device memory owned by the caller; the
+ *     library never allocates, frees or keeps them.  Pointers marked (host)
+ *     are host memory, read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Device
+ *     work is enqueued on it and the call returns without synchronising.
+ *   - Arguments are checked on the host before anything is enqueued; a
+ *     failed check returns a status and enqueues nothing.  Device-resident
+ *     metadata (block ids, slots, lengths) is NOT checked on the hot path:
+ *     out-of-range values are undefined behaviour; pa_check_metadata checks
+ *     them synchronously for tests and debugging.
+ *   - Element types: PA_F32, PA_BF16, PA_F16.  K/V caches, keys, values and
+ *     queries of one call share one type.
+ *   - Sizes are in elements unless the name says bytes.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1, /* a size, pointer or combination is invalid      */
+  PA_ERR_UNSUPPORTED = 2,      /* valid, but not a shape/type this build handles */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PA_ERR_OUT_OF_BLOCKS = 4,    /* block pool: not enough free blocks (no change) */
+  PA_ERR_HIP = 5,              /* a HIP runtime call or launch failed            */
+  PA_ERR_METADATA = 6          /* pa_check_metadata found a violated precondition*/
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
+
+/* Cache layouts ([vllm] §3.3).  A block is contiguous in both. */
+typedef enum {
+  PA_LAYOUT_NHD = 0, /* [num_blocks, block_size, num_kv_heads, head_size]        */
+  PA_LAYOUT_HND = 1  /* [num_blocks, num_kv_heads, block_size, head_size] (head-major) */
+} pa_layout;
+
+/* Human-readable name of a status code (static string). */
+const char* pa_status_string(pa_status status);
+
+/* Text of the last failure in the calling thread (static per-thread buffer). */
+const char* pa_last_error(void);
+
+/*
+ * pa_reshape_and_cache -- scatter this step's new K/V rows into the block pool
+ * ([vllm] §3.2, §6.3, §7.4).
+ *
+ * Row i of key/value ([num_kv_heads, head_size], contiguous; rows
+ * `key_row_stride` / `value_row_stride` elements apart) is copied bit for bit
+ * to slot s = slot_mapping[i] of the pool: block s / block_size, offset
+ * s % block_size, laid out as `layout`.  A negative slot marks a padding row
+ * and the row is skipped.  All other slots of the pool are left untouched.
+ *   key, value          (device) [num_tokens, ...] rows of `dtype`
+ *   key_cache, value_cache (device) pools of num_blocks blocks
+ *   slot_mapping        (device) int64 [num_tokens]
+ * Preconditions (not checked on the device): non-negative slots are distinct
+ * and < num_blocks * block_size.  head_size * sizeof(dtype) must be a
+ * multiple of 16 bytes and all pointers and row strides 16-byte aligned.
+ * num_tokens == 0 is a no-op.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value,
+                               int64_t key_row_stride, int64_t value_row_stride,
+                               void* key_cache, void* value_cache,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_size,
+                               int32_t block_size, int32_t num_blocks,
+                               pa_dtype dtype, pa_layout layout, void* stream);
+
+/*
+ * pa_copy_blocks -- whole-block copies of both pools (copy-on-write, [k4i]
+ * copy-on-write step 2, [atb] copy-on-write section).
+ *   block_pairs (device) int32 [num_pairs][2] = (source block, destination block)
+ * Every destination must be distinct and no destination may be a source
+ * (not checked on the device).  num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void* key_cache, void* value_cache,
+                         const int32_t* block_pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                         void* stream);
+
+/*
+ * pa_decode -- one query token per sequence attends to its cached context
+ * through its block table ([vllm] §3.1, §6.2, §7.2; [k4i] attention over
+ * non-contiguous blocks).
+ *
+ * For sequence s, query head h, kv head g = h / (num_heads / num_kv_heads)
+ * (contiguous GQA groups) and L = context_lens[s]:
+ *   out[s,h,:] = softmax_t(scale * q[s,h,:] . K_t) V_t,  t = 0 .. L-1,
+ * where K_t/V_t are read at block block_tables[s][t / block_size], offset
+ * t % block_size of the pools.  L includes this step's token, which must
+ * already be written (pa_reshape_and_cache).  L == 0 gives a zero row.
+ *   out          (device) [num_seqs, num_heads, head_size] of out_dtype
+ *                (PA_F32, or kv_dtype)
+ *   query        (device) [num_seqs, num_heads, head_size] of kv_dtype
+ *   block_tables (device) int32 [num_seqs, max_blocks_per_seq]; entries past
+ *                ceil(L / block_size) are never read
+ *   context_lens (device) int32 [num_seqs], each in [0, max_context_len] and
+ *                <= max_blocks_per_seq * block_size
+ *   partition_size  0  = one pass per (sequence, kv head) ("V1", [vllm] §7.3)
+ *                   >0 = split-K over partitions of that many tokens, then a
+ *                        reduce ("V2", [vllm] §7.3); a multiple of 16
+ *                   -1 = chosen by the library from the shape
+ *   workspace    (device) >= pa_decode_workspace_size(...) bytes when split-K
+ *                is used (may be NULL for partition_size 0)
+ * Supported: head_size 64 or 128; num_heads / num_kv_heads in {1,2,4,8,16};
+ * block_size a power of two in [1, 1024]; PA_LAYOUT_NHD or PA_LAYOUT_HND.
+ * Results are bitwise deterministic for a fixed launch configuration and do
+ * not depend on which physical blocks hold the context.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                int32_t head_size, int32_t max_context_len,
+                                int32_t partition_size);
+
+/* Partition size that partition_size = -1 resolves to for this shape. */
+int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                 int32_t max_context_len);
+
+pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
+                    const void* key_cache, const void* value_cache,
+                    pa_dtype kv_dtype, pa_layout layout,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_size, int32_t block_size, int32_t num_blocks,
+                    float scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill -- causal attention of packed query rows over the paged cache
+ * ([vllm] §6.2 flash_attn_varlen_func with cu_seqlens_q = query_start_loc,
+ * seqlen_k = seq_lens, block_table, causal = True; [packed] §2.3).
+ *
+ * Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1]-1
+ * (n rows, packed without padding); with L = context_lens[s] >= n, row j is
+ * the token at position L - n + j and attends to positions 0 .. L - n + j
+ * (causal mask aligned to the end of the context).  K/V of all L positions
+ * must already be in the pool.
+ *   out             (device) [num_tokens, num_heads, head_size] of out_dtype
+ *                   (PA_F32, or kv_dtype)
+ *   query           (device) [num_tokens, num_heads, head_size] of kv_dtype
+ *   query_start_loc (device) int32 [num_seqs + 1], query_start_loc[0] = 0,
+ *                   non-decreasing, query_start_loc[num_seqs] = num_tokens
+ *   max_query_len   >= every n (host value)
+ * Supported: kv_dtype PA_BF16 or PA_F16 (matrix cores), head_size 64 or 128,
+ * num_heads / num_kv_heads in {1,2,4,8,16}, block_size a power of two.
+ */
+pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query,
+                     const void* key_cache, const void* value_cache,
+                     pa_dtype kv_dtype, pa_layout layout,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* query_start_loc, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                     int32_t max_context_len, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                     int32_t num_blocks, float scale, void* stream);
+
+/*
+ * pa_check_metadata -- synchronous host-side check of device metadata (tests
+ * and debugging; copies the arrays to the host after synchronising `stream`).
+ * Checks: 0 <= context_lens[s] <= max_blocks_per_seq * block_size; every
+ * block-table entry a sequence reads (t < context_lens[s]) lies in
+ * [0, num_blocks); non-negative slots are distinct and < num_blocks *
+ * block_size.  Any pointer may be NULL to skip its checks.  Returns PA_OK or
+ * PA_ERR_METADATA (details in pa_last_error()).
+ */
+pa_status pa_check_metadata(const int32_t* block_tables,
+                            const int32_t* context_lens,
+                            const int64_t* slot_mapping, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t num_tokens,
+                            int32_t block_size, int32_t num_blocks, void* stream);
+
+/*
+ * Block pool -- host-side block manager that hands out physical blocks and
+ * builds block tables and slot mappings ([k4i] block manager, copy-on-write;
+ * [vllm] §4.1 free queue; [atb] reference counting).  Host memory only; not
+ * thread-safe (one pool per thread or external locking).
+ *
+ * Free blocks wait in a FIFO queue: allocation takes from the front, blocks
+ * whose count drops to zero go to the back.  `free_order` (host, int32
+ * [num_blocks], a permutation of 0..num_blocks-1; NULL = ascending) is the
+ * initial queue.  Every operation is all-or-nothing: PA_ERR_OUT_OF_BLOCKS
+ * leaves the pool unchanged.
+ */
+typedef struct pa_pool pa_pool;
+
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size,
+                         const int32_t* free_order, pa_pool** out);
+void pa_pool_destroy(pa_pool* pool);
+
+/* New empty sequence; its id is written to *seq_id. */
+pa_status pa_pool_add_seq(pa_pool* pool, int32_t* seq_id);
+
+/* New sequence sharing every block of `parent` (each count + 1). */
+pa_status pa_pool_fork(pa_pool* pool, int32_t parent, int32_t* child);
+
+/*
+ * Append n tokens to a sequence.  slots_out (host, int64 [n], may be NULL)
+ * receives block * block_size + offset of each new position.  When the first
+ * new token lands in a partly filled block shared with other sequences, the
+ * block is copied first (copy-on-write): a free block is taken, the old
+ * block's count drops by one and the table is repointed; the (source,
+ * destination) pair is written to cow_pairs (host, int32 [cow_cap][2]) and
+ * *n_cow counts the pairs (0 or 1).  The caller copies the pair's contents
+ * (pa_copy_blocks) before writing the new tokens.  cow_cap < 1 with a copy
+ * needed returns PA_ERR_INVALID_ARGUMENT with no change.
+ */
+pa_status pa_pool_append(pa_pool* pool, int32_t seq_id, int32_t n,
+                         int64_t* slots_out, int32_t* cow_pairs,
+                         int32_t cow_cap, int32_t* n_cow);
+
+/* Release a sequence: every block's count drops by one; blocks at zero return
+ * to the back of the free queue in table order. */
+pa_status pa_pool_free_seq(pa_pool* pool, int32_t seq_id);
+
+/* Copy a sequence's block table to out (host, int32 [cap]); *n = its length. */
+pa_status pa_pool_block_table(const pa_pool* pool, int32_t seq_id, int32_t* out,
+                              int32_t cap, int32_t* n);
+
+/* Number of tokens of a sequence, or -1 for an unknown id. */
+int32_t pa_pool_seq_len(const pa_pool* pool, int32_t seq_id);
+int32_t pa_pool_num_free(const pa_pool* pool);
+/* Reference count of a block, or -1 when out of range. */
+int32_t pa_pool_refcount(const pa_pool* pool, int32_t block);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H_ */

@@ -1,0 +1,309 @@
+"""Python binding of libpagedattn.so (paged KV-cache attention for MI355X / gfx950).
+
+Argument marshalling only: every function passes tensor data pointers, sizes
+and the current HIP stream to the C entry point of the same name (declared in
+include/pa.h) and raises on a non-OK status.  PyTorch is used for device
+memory and streams; all compute runs in the library's HIP kernels.  There is
+no fallback: importing this package fails if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m paged_kv_cache_134_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+# Load torch first so that the library binds to the HIP runtime torch already
+# loaded (same soname): device memory, streams and kernels then live in one
+# runtime.  Without torch only the host-side block pool is usable.
+try:
+    import torch as _torch_mod  # noqa: F401
+except ImportError:  # pragma: no cover
+    _torch_mod = None
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---------------------------------------------------------------- constants
+PA_OK = 0
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARGUMENT", 2: "PA_ERR_UNSUPPORTED",
+                3: "PA_ERR_WORKSPACE_TOO_SMALL", 4: "PA_ERR_OUT_OF_BLOCKS", 5: "PA_ERR_HIP",
+                6: "PA_ERR_METADATA"}
+PA_F32, PA_BF16, PA_F16 = 0, 1, 2
+NHD, HND = 0, 1
+
+EXPORTED = [
+    "pa_status_string", "pa_last_error", "pa_reshape_and_cache", "pa_copy_blocks",
+    "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode", "pa_prefill",
+    "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
+    "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
+    "pa_pool_num_free", "pa_pool_refcount",
+]
+
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+_pi64 = ctypes.POINTER(ctypes.c_int64)
+
+_sig = {
+    "pa_status_string": (ctypes.c_char_p, [_i32]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_reshape_and_cache": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32]),
+    "pa_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
+                         _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_prefill": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
+                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
+    "pa_check_metadata": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_pool_create": (_i32, [_i32, _i32, _pi32, ctypes.POINTER(_vp)]),
+    "pa_pool_destroy": (None, [_vp]),
+    "pa_pool_add_seq": (_i32, [_vp, _pi32]),
+    "pa_pool_fork": (_i32, [_vp, _i32, _pi32]),
+    "pa_pool_append": (_i32, [_vp, _i32, _i32, _pi64, _pi32, _i32, _pi32]),
+    "pa_pool_free_seq": (_i32, [_vp, _i32]),
+    "pa_pool_block_table": (_i32, [_vp, _i32, _pi32, _i32, _pi32]),
+    "pa_pool_seq_len": (_i32, [_vp, _i32]),
+    "pa_pool_num_free": (_i32, [_vp]),
+    "pa_pool_refcount": (_i32, [_vp, _i32]),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        self.status_name = STATUS_NAMES.get(status, str(status))
+        detail = _lib.pa_last_error().decode(errors="replace")
+        super().__init__(f"{fn}: {self.status_name}: {detail}")
+
+
+class OutOfBlocks(PagedAttnError):
+    pass
+
+
+def _check(fn: str, st: int) -> None:
+    if st != PA_OK:
+        raise (OutOfBlocks if st == 4 else PagedAttnError)(fn, st)
+
+
+# ------------------------------------------------------------ torch helpers
+def _torch():
+    import torch  # imported lazily: the block pool needs no torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.float16: PA_F16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(t, name: str, dtype=None, contiguous: bool = True):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _geom(key_cache, layout: int) -> Tuple[int, int, int, int]:
+    """(num_blocks, block_size, num_kv_heads, head_size) of a pool tensor."""
+    if key_cache.dim() != 4:
+        raise ValueError("cache must be 4-D")
+    nb, a, b, d = key_cache.shape
+    return (nb, a, b, d) if layout == NHD else (nb, b, a, d)
+
+
+# ---------------------------------------------------------------- entry points
+def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, layout: int = NHD,
+                         stream=None) -> None:
+    """Scatter rows key/value [T, Hkv, D] into the pools at slot_mapping [T] (int64)."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    if key.dim() != 3 or key.shape[1:] != (hkv, d) or value.shape != key.shape:
+        raise ValueError("key/value must be [T, num_kv_heads, head_size] matching the cache")
+    if key.stride(2) != 1 or key.stride(1) != d or value.stride(2) != 1 or value.stride(1) != d:
+        raise ValueError("key/value rows must be contiguous")
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype:
+        raise TypeError("key/value dtype must equal the cache dtype")
+    T = key.shape[0]
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    _check("pa_reshape_and_cache", _lib.pa_reshape_and_cache(
+        _dev(key, "key", contiguous=False), _dev(value, "value", contiguous=False),
+        key.stride(0), value.stride(0), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
+        T, hkv, d, bs, nb, _dtype_code(key_cache), layout, _stream(stream)))
+
+
+def pa_copy_blocks(key_cache, value_cache, block_pairs, layout: int = NHD, stream=None) -> None:
+    """Copy whole blocks: block_pairs int32 [n, 2] = (source, destination)."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    n = int(block_pairs.shape[0]) if block_pairs.numel() else 0
+    _check("pa_copy_blocks", _lib.pa_copy_blocks(
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_pairs, "block_pairs", torch.int32) if n else None, n, hkv, d, bs, nb,
+        _dtype_code(key_cache), _stream(stream)))
+
+
+def pa_decode_workspace_size(num_seqs: int, num_heads: int, head_size: int, max_context_len: int,
+                             partition_size: int) -> int:
+    return int(_lib.pa_decode_workspace_size(num_seqs, num_heads, head_size, max_context_len,
+                                             partition_size))
+
+
+def pa_decode_auto_partition(num_seqs: int, num_kv_heads: int, max_context_len: int) -> int:
+    return int(_lib.pa_decode_auto_partition(num_seqs, num_kv_heads, max_context_len))
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len: int,
+              scale: float, layout: int = NHD, partition_size: int = -1, workspace=None,
+              stream=None) -> None:
+    """Decode attention; out [S, H, D] (float32 or the cache dtype)."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    S, H, D = query.shape
+    if D != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_seqs, num_heads, head_size]")
+    if query.dtype != key_cache.dtype:
+        raise TypeError("query dtype must equal the cache dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables [S, max_blocks] and context_lens [S] required")
+    ws_ptr, ws_bytes = (None, 0)
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    _check("pa_decode", _lib.pa_decode(
+        _dev(out, "out"), _dtype_code(out), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dtype_code(key_cache), layout,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, H, hkv, d, bs,
+        nb, float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_prefill(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens,
+               max_query_len: int, max_context_len: int, scale: float, layout: int = NHD,
+               stream=None) -> None:
+    """Causal packed prefill; query/out [num_tokens, H, D]."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    T, H, D = query.shape
+    S = context_lens.shape[0]
+    if D != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_tokens, num_heads, head_size]")
+    if query.dtype != key_cache.dtype:
+        raise TypeError("query dtype must equal the cache dtype")
+    if query_start_loc.shape != (S + 1,) or block_tables.shape[0] != S:
+        raise ValueError("query_start_loc [S+1] and block_tables [S, max_blocks] required")
+    _check("pa_prefill", _lib.pa_prefill(
+        _dev(out, "out"), _dtype_code(out), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dtype_code(key_cache), layout,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(query_start_loc, "query_start_loc", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, T, int(max_query_len),
+        int(max_context_len), H, hkv, d, bs, nb, float(scale), _stream(stream)))
+
+
+def pa_check_metadata(block_tables, context_lens, slot_mapping, num_blocks: int, block_size: int,
+                      stream=None) -> None:
+    """Synchronous host check of device metadata; raises PagedAttnError(PA_ERR_METADATA)."""
+    S = context_lens.shape[0] if context_lens is not None else (
+        block_tables.shape[0] if block_tables is not None else 0)
+    mb = block_tables.shape[1] if block_tables is not None else 0
+    T = slot_mapping.shape[0] if slot_mapping is not None else 0
+    p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    _check("pa_check_metadata", _lib.pa_check_metadata(
+        p(block_tables), p(context_lens), p(slot_mapping), S, mb, T, block_size, num_blocks,
+        _stream(stream)))
+
+
+# ------------------------------------------------------------------ block pool
+class BlockPool:
+    """Host block manager (pa_pool_*): FIFO free queue, reference counts,
+    fork and append with copy-on-write."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        self.block_size = int(block_size)
+        self.num_blocks = int(num_blocks)
+        h = _vp()
+        if free_order is None:
+            st = _lib.pa_pool_create(num_blocks, block_size, None, ctypes.byref(h))
+        else:
+            arr = np.ascontiguousarray(free_order, dtype=np.int32)
+            st = _lib.pa_pool_create(num_blocks, block_size, arr.ctypes.data_as(_pi32),
+                                     ctypes.byref(h))
+        _check("pa_pool_create", st)
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            _lib.pa_pool_destroy(h)
+            self._h = None
+
+    def add_seq(self) -> int:
+        sid = ctypes.c_int32()
+        _check("pa_pool_add_seq", _lib.pa_pool_add_seq(self._h, ctypes.byref(sid)))
+        return sid.value
+
+    def fork(self, parent: int) -> int:
+        c = ctypes.c_int32()
+        _check("pa_pool_fork", _lib.pa_pool_fork(self._h, parent, ctypes.byref(c)))
+        return c.value
+
+    def append(self, seq: int, n: int) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
+        """Append n tokens; returns (slots int64 [n], copy-on-write pairs)."""
+        slots = np.empty(n, np.int64)
+        pairs = np.empty(2, np.int32)
+        ncow = ctypes.c_int32()
+        _check("pa_pool_append", _lib.pa_pool_append(
+            self._h, seq, n, slots.ctypes.data_as(_pi64), pairs.ctypes.data_as(_pi32), 1,
+            ctypes.byref(ncow)))
+        return slots, [(int(pairs[0]), int(pairs[1]))] if ncow.value else []
+
+    def free_seq(self, seq: int) -> None:
+        _check("pa_pool_free_seq", _lib.pa_pool_free_seq(self._h, seq))
+
+    def block_table(self, seq: int) -> np.ndarray:
+        n = ctypes.c_int32()
+        _check("pa_pool_block_table", _lib.pa_pool_block_table(self._h, seq, None, 0,
+                                                               ctypes.byref(n)))
+        out = np.empty(n.value, np.int32)
+        _check("pa_pool_block_table", _lib.pa_pool_block_table(
+            self._h, seq, out.ctypes.data_as(_pi32), n.value, ctypes.byref(n)))
+        return out
+
+    def seq_len(self, seq: int) -> int:
+        return int(_lib.pa_pool_seq_len(self._h, seq))
+
+    def num_free(self) -> int:
+        return int(_lib.pa_pool_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(_lib.pa_pool_refcount(self._h, block))

@@ -1,0 +1,92 @@
+// Cache write (slot_mapping scatter) and whole-block copies.
+//
+// The scatter follows the cache-write kernels of "PagedAttention 在 vLLM 中的实现
+// 分析" (§6.3, §7.4): every new token carries a global slot
+// block * block_size + offset, a negative slot marks padding and is skipped.
+// Here one workgroup moves one token row ([num_kv_heads, head_size] of K and
+// of V) with 16-byte vector loads and stores; the row is contiguous in the
+// source, and in the pool it is contiguous (NHD) or split into num_kv_heads
+// head rows of head_size elements (HND).  The copy is a bit copy, so only the
+// element width matters.
+#include <hip/hip_runtime.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWriteThreads = 256;
+
+// 16-byte chunk index helpers: a head row has `hc` chunks (head_size * elem / 16).
+template <int LAYOUT>
+__global__ __launch_bounds__(kWriteThreads) void reshape_and_cache_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value, int64_t key_stride16,
+    int64_t value_stride16, uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    const int64_t* __restrict__ slot_mapping, int32_t num_kv_heads, int32_t hc, int32_t block_size) {
+  const int64_t token = blockIdx.x;
+  const int64_t slot = slot_mapping[token];
+  if (slot < 0) return;  // padding row
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int32_t row_chunks = num_kv_heads * hc;
+  const uint4* k_src = key + token * key_stride16;
+  const uint4* v_src = value + token * value_stride16;
+  for (int32_t c = threadIdx.x; c < row_chunks; c += kWriteThreads) {
+    int64_t dst;
+    if (LAYOUT == PA_LAYOUT_NHD) {
+      dst = (blk * block_size + off) * row_chunks + c;
+    } else {
+      const int32_t h = c / hc;
+      const int32_t d = c - h * hc;
+      dst = ((blk * num_kv_heads + h) * block_size + off) * hc + d;
+    }
+    const uint4 kv = k_src[c];
+    const uint4 vv = v_src[c];
+    key_cache[dst] = kv;
+    value_cache[dst] = vv;
+  }
+}
+
+// One workgroup per (pair, pool): copies block src to block dst.
+__global__ __launch_bounds__(kWriteThreads) void copy_blocks_kernel(
+    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    const int32_t* __restrict__ pairs, int64_t block_chunks) {
+  const int32_t i = blockIdx.x;
+  uint4* pool = blockIdx.y == 0 ? key_cache : value_cache;
+  const int64_t src = (int64_t)pairs[2 * i] * block_chunks;
+  const int64_t dst = (int64_t)pairs[2 * i + 1] * block_chunks;
+  for (int64_t c = threadIdx.x; c < block_chunks; c += kWriteThreads) pool[dst + c] = pool[src + c];
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t key_row_stride,
+                                    int64_t value_row_stride, void* key_cache, void* value_cache,
+                                    const int64_t* slot_mapping, int32_t num_tokens,
+                                    const PoolGeom& g, int elem_bytes, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int32_t hc = g.head_size * elem_bytes / 16;
+  const int64_t ks = key_row_stride * elem_bytes / 16;
+  const int64_t vs = value_row_stride * elem_bytes / 16;
+  dim3 grid(num_tokens), block(kWriteThreads);
+  if (g.layout == PA_LAYOUT_NHD)
+    hipLaunchKernelGGL(reshape_and_cache_kernel<PA_LAYOUT_NHD>, grid, block, 0, stream,
+                       (const uint4*)key, (const uint4*)value, ks, vs, (uint4*)key_cache,
+                       (uint4*)value_cache, slot_mapping, g.num_kv_heads, hc, g.block_size);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_kernel<PA_LAYOUT_HND>, grid, block, 0, stream,
+                       (const uint4*)key, (const uint4*)value, ks, vs, (uint4*)key_cache,
+                       (uint4*)value_cache, slot_mapping, g.num_kv_heads, hc, g.block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                              int32_t num_pairs, int64_t block_bytes, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  dim3 grid(num_pairs, 2), block(kWriteThreads);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, block, 0, stream, (uint4*)key_cache,
+                     (uint4*)value_cache, pairs, block_bytes / 16);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,138 @@
+// Device helpers shared by the attention kernels: element formats, lane
+// reductions and float <-> storage conversions.  gfx950 (wave64) only.
+#ifndef PA_KERNEL_COMMON_H_
+#define PA_KERNEL_COMMON_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Elements per 16-byte chunk.
+template <pa_dtype DT>
+struct Fmt {
+  static constexpr int kBytes = DT == PA_F32 ? 4 : 2;
+  static constexpr int kVec = 16 / kBytes;
+};
+
+// acc + dot(q, k) over one 16-byte chunk (fp32 accumulation; bf16/f16
+// products are exact in fp32).
+template <pa_dtype DT>
+__device__ __forceinline__ float dot_chunk(const uint4& q, const uint4& k, float acc) {
+  if constexpr (DT == PA_F32) {
+    acc = __builtin_fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  } else if constexpr (DT == PA_BF16) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x),
+                                          __builtin_bit_cast(bf16x2_t, k.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y),
+                                          __builtin_bit_cast(bf16x2_t, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z),
+                                          __builtin_bit_cast(bf16x2_t, k.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w),
+                                          __builtin_bit_cast(bf16x2_t, k.w), acc, false);
+  } else {
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q.x), __builtin_bit_cast(f16x2_t, k.x),
+                                 acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q.y), __builtin_bit_cast(f16x2_t, k.y),
+                                 acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q.z), __builtin_bit_cast(f16x2_t, k.z),
+                                 acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q.w), __builtin_bit_cast(f16x2_t, k.w),
+                                 acc, false);
+  }
+  return acc;
+}
+
+// Element e of one 16-byte chunk as float (exact).
+template <pa_dtype DT>
+__device__ __forceinline__ float chunk_elem(const uint4& v, int e) {
+  constexpr int kPerWord = 4 / Fmt<DT>::kBytes;
+  const int wi = e / kPerWord;
+  const uint32_t w = wi == 0 ? v.x : wi == 1 ? v.y : wi == 2 ? v.z : v.w;
+  if constexpr (DT == PA_F32) {
+    return __uint_as_float(w);
+  } else if constexpr (DT == PA_BF16) {
+    return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+  } else {
+    const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
+    return (float)h;
+  }
+}
+
+// Unpack a chunk to kVec floats.
+template <pa_dtype DT>
+__device__ __forceinline__ void chunk_to_f32(const uint4& v, float* out) {
+#pragma unroll
+  for (int e = 0; e < Fmt<DT>::kVec; ++e) out[e] = chunk_elem<DT>(v, e);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N = 1..64, power of two); every lane of
+// the group receives the group sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<0xB1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<0x4E>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<0x141>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<0x140>(x));
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// 2^(a - b) where a = -inf (an empty running state) gives 0 even if b = -inf.
+__device__ __forceinline__ float exp2_diff(float a, float b) {
+  return a == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a - b);
+}
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Store one float as the output type (PA_F32, PA_BF16 or PA_F16).
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v, pa_dtype t) {
+  if (t == PA_F32)
+    reinterpret_cast<float*>(out)[idx] = v;
+  else if (t == PA_BF16)
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
+  else
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_f16(v);
+}
+
+}  // namespace pa
+
+#endif  // PA_KERNEL_COMMON_H_

@@ -1,0 +1,327 @@
+// C entry points: argument checks, workspace sizing, dispatch to the kernels.
+// Everything here runs on the host; device work is only enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bool pow2_in(int32_t v, int32_t lo, int32_t hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+
+bool valid_dtype(pa_dtype t) { return t == PA_F32 || t == PA_BF16 || t == PA_F16; }
+
+bool valid_group(int32_t h, int32_t hkv) {
+  if (h <= 0 || hkv <= 0 || h % hkv != 0) return false;
+  const int32_t g = h / hkv;
+  return g == 1 || g == 2 || g == 4 || g == 8 || g == 16;
+}
+
+pa_status hip_fail(hipError_t e, const char* where) {
+  std::string msg = std::string(where) + ": " + hipGetErrorString(e);
+  return pa_fail(PA_ERR_HIP, msg.c_str());
+}
+
+constexpr int32_t kAutoSmallestPartition = 256;
+
+int64_t partitions_for(int32_t max_context_len, int32_t partition_size) {
+  return partition_size > 0 ? (max_context_len + (int64_t)partition_size - 1) / partition_size : 0;
+}
+
+size_t workspace_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_size, int64_t parts) {
+  const size_t out_b = (size_t)(num_seqs * num_heads * parts * head_size) * sizeof(float);
+  const size_t ml_b = (size_t)(num_seqs * num_heads * parts * 2) * sizeof(float);
+  return ((out_b + 255) / 256) * 256 + ml_b;
+}
+
+}  // namespace
+
+pa_status pa_fail(pa_status st, const char* msg) {
+  g_last_error = msg ? msg : "";
+  return st;
+}
+
+extern "C" const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_METADATA: return "PA_ERR_METADATA";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+extern "C" const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+// ------------------------------------------------------------------ write
+extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value,
+                                          int64_t key_row_stride, int64_t value_row_stride,
+                                          void* key_cache, void* value_cache,
+                                          const int64_t* slot_mapping, int32_t num_tokens,
+                                          int32_t num_kv_heads, int32_t head_size,
+                                          int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                                          pa_layout layout, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: non-positive size");
+  if (!valid_dtype(dtype)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: bad dtype");
+  if (layout != PA_LAYOUT_NHD && layout != PA_LAYOUT_HND)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: bad layout");
+  const int eb = elem_bytes(dtype);
+  if ((head_size * eb) % 16 != 0)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache: head_size * element size must be a multiple of 16 bytes");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: null pointer");
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (key_row_stride < row || value_row_stride < row || (key_row_stride * eb) % 16 ||
+      (value_row_stride * eb) % 16)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: row stride too small or not 16-byte aligned");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: pointers must be 16-byte aligned");
+  pa::PoolGeom g{num_kv_heads, head_size, block_size, num_blocks, layout};
+  hipError_t e = pa::launch_reshape_and_cache(key, value, key_row_stride, value_row_stride,
+                                              key_cache, value_cache, slot_mapping, num_tokens, g,
+                                              eb, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_reshape_and_cache");
+}
+
+extern "C" pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs,
+                                    int32_t num_pairs, int32_t num_kv_heads, int32_t head_size,
+                                    int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                                    void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_copy_blocks: non-positive size");
+  if (!valid_dtype(dtype)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_copy_blocks: bad dtype");
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_pairs)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_copy_blocks: null pointer");
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_size * elem_bytes(dtype);
+  if (block_bytes % 16 || !aligned16(key_cache) || !aligned16(value_cache))
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: blocks must be 16-byte multiples and aligned");
+  hipError_t e = pa::launch_copy_blocks(key_cache, value_cache, block_pairs, num_pairs, block_bytes,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_copy_blocks");
+}
+
+// ----------------------------------------------------------------- decode
+extern "C" int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                            int32_t max_context_len) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  return max_context_len <= 512 ? 0 : 512;
+}
+
+extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                           int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || max_context_len <= 0) return 0;
+  const int32_t ps = partition_size < 0 ? kAutoSmallestPartition : partition_size;
+  if (ps == 0) return 0;
+  return workspace_bytes(num_seqs, num_heads, head_size, partitions_for(max_context_len, ps));
+}
+
+extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
+                               const void* key_cache, const void* value_cache, pa_dtype kv_dtype,
+                               pa_layout layout, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                               int32_t num_blocks, float scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes_, void* stream) {
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: negative size or no blocks");
+  if (!valid_dtype(kv_dtype) || (out_dtype != PA_F32 && out_dtype != kv_dtype))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: bad kv/out dtype");
+  if (layout != PA_LAYOUT_NHD && layout != PA_LAYOUT_HND)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: bad layout");
+  if (!valid_group(num_heads, num_kv_heads))
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: num_heads / num_kv_heads must be 1, 2, 4, 8 or 16");
+  if (head_size != 64 && head_size != 128)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: head_size must be 64 or 128");
+  if (!pow2_in(block_size, 1, 1024))
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size must be a power of two in [1, 1024]");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: max_context_len exceeds max_blocks_per_seq * block_size");
+  if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: partition_size must be -1, 0 or a positive multiple of 16");
+  if (!(scale == scale)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: scale is NaN");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: null pointer");
+  if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: query and caches must be 16-byte aligned");
+  if ((int64_t)num_seqs * num_kv_heads > 0x7FFFFFFF)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: too many (sequence, kv head) pairs");
+  int32_t ps = partition_size < 0 ? pa_decode_auto_partition(num_seqs, num_kv_heads, max_context_len)
+                                  : partition_size;
+  const int64_t parts = partitions_for(max_context_len, ps);
+  if (ps > 0 && parts == 0) ps = 0;  // empty contexts: nothing to split
+  if (ps > 0 && parts > 65535)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 65535 partitions per sequence");
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.kv_dtype = kv_dtype;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.geom = pa::PoolGeom{num_kv_heads, head_size, block_size, num_blocks, layout};
+  a.scale = scale;
+  a.partition_size = ps;
+  if (ps > 0) {
+    const size_t need = workspace_bytes(num_seqs, num_heads, head_size, parts);
+    if (!workspace || workspace_bytes_ < need) {
+      char msg[160];
+      std::snprintf(msg, sizeof msg, "pa_decode: split-K needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes_ : (size_t)0);
+      return pa_fail(PA_ERR_WORKSPACE_TOO_SMALL, msg);
+    }
+    if (!aligned16(workspace))
+      return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: workspace must be 16-byte aligned");
+    a.max_partitions = (int32_t)parts;
+    const size_t out_b = (size_t)num_seqs * num_heads * parts * head_size * sizeof(float);
+    a.part_out = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((out_b + 255) / 256) * 256);
+  }
+  hipError_t e = pa::launch_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode");
+}
+
+// ---------------------------------------------------------------- prefill
+extern "C" pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query,
+                                const void* key_cache, const void* value_cache, pa_dtype kv_dtype,
+                                pa_layout layout, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* query_start_loc,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
+                                int32_t max_query_len, int32_t max_context_len, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                int32_t num_blocks, float scale, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
+      max_blocks_per_seq < 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: negative size or no blocks");
+  if (kv_dtype != PA_BF16 && kv_dtype != PA_F16)
+    return pa_fail(valid_dtype(kv_dtype) ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARGUMENT,
+                   "pa_prefill: kv dtype must be bf16 or f16");
+  if (out_dtype != PA_F32 && out_dtype != kv_dtype)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: out dtype must be f32 or the kv dtype");
+  if (layout != PA_LAYOUT_NHD && layout != PA_LAYOUT_HND)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: bad layout");
+  if (!valid_group(num_heads, num_kv_heads))
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill: num_heads / num_kv_heads must be 1, 2, 4, 8 or 16");
+  if (head_size != 64 && head_size != 128)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_size must be 64 or 128");
+  if (!pow2_in(block_size, 1, 1024))
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size must be a power of two in [1, 1024]");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: max_context_len exceeds max_blocks_per_seq * block_size");
+  if (max_query_len > max_context_len)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: max_query_len exceeds max_context_len");
+  if (num_heads > 65535 || num_seqs > 65535)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill: at most 65535 heads and 65535 sequences");
+  if (!(scale == scale)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: scale is NaN");
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !query_start_loc ||
+      !context_lens)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: null pointer");
+  if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: query and caches must be 16-byte aligned");
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.kv_dtype = kv_dtype;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.query_start_loc = query_start_loc;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.max_query_len = max_query_len;
+  a.num_heads = num_heads;
+  a.geom = pa::PoolGeom{num_kv_heads, head_size, block_size, num_blocks, layout};
+  a.scale = scale;
+  hipError_t e = pa::launch_prefill(a, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_prefill");
+}
+
+// ----------------------------------------------------------- metadata check
+extern "C" pa_status pa_check_metadata(const int32_t* block_tables, const int32_t* context_lens,
+                                       const int64_t* slot_mapping, int32_t num_seqs,
+                                       int32_t max_blocks_per_seq, int32_t num_tokens,
+                                       int32_t block_size, int32_t num_blocks, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || num_tokens < 0 || block_size <= 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_check_metadata: bad sizes");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pa_check_metadata: synchronize");
+  char msg[200];
+  std::vector<int32_t> lens;
+  if (context_lens && num_seqs) {
+    lens.resize(num_seqs);
+    e = hipMemcpy(lens.data(), context_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "pa_check_metadata: copy context_lens");
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      if (lens[s] < 0 || (int64_t)lens[s] > (int64_t)max_blocks_per_seq * block_size) {
+        std::snprintf(msg, sizeof msg, "context_lens[%d] = %d outside [0, %lld]", s, lens[s],
+                      (long long)max_blocks_per_seq * block_size);
+        return pa_fail(PA_ERR_METADATA, msg);
+      }
+    }
+  }
+  if (block_tables && num_seqs && max_blocks_per_seq) {
+    std::vector<int32_t> bt((size_t)num_seqs * max_blocks_per_seq);
+    e = hipMemcpy(bt.data(), block_tables, sizeof(int32_t) * bt.size(), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "pa_check_metadata: copy block_tables");
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const int64_t used = lens.empty() ? max_blocks_per_seq
+                                        : ((int64_t)lens[s] + block_size - 1) / block_size;
+      for (int64_t i = 0; i < used; ++i) {
+        const int32_t b = bt[(size_t)s * max_blocks_per_seq + i];
+        if (b < 0 || b >= num_blocks) {
+          std::snprintf(msg, sizeof msg, "block_tables[%d][%lld] = %d outside [0, %d)", s,
+                        (long long)i, b, num_blocks);
+          return pa_fail(PA_ERR_METADATA, msg);
+        }
+      }
+    }
+  }
+  if (slot_mapping && num_tokens) {
+    std::vector<int64_t> sl(num_tokens);
+    e = hipMemcpy(sl.data(), slot_mapping, sizeof(int64_t) * num_tokens, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "pa_check_metadata: copy slot_mapping");
+    const int64_t nslots = (int64_t)num_blocks * block_size;
+    std::vector<char> seen((size_t)nslots, 0);
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      if (sl[i] < 0) continue;
+      if (sl[i] >= nslots || seen[sl[i]]) {
+        std::snprintf(msg, sizeof msg, "slot_mapping[%d] = %lld %s", i, (long long)sl[i],
+                      sl[i] >= nslots ? "out of range" : "repeats an earlier slot");
+        return pa_fail(PA_ERR_METADATA, msg);
+      }
+      seen[sl[i]] = 1;
+    }
+  }
+  return PA_OK;
+}

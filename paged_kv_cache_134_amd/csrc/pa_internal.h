@@ -1,0 +1,82 @@
+// Internal declarations shared by the library's translation units.
+#ifndef PA_INTERNAL_H_
+#define PA_INTERNAL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+// Records `msg` as the calling thread's last error and returns `st`.
+pa_status pa_fail(pa_status st, const char* msg);
+
+#ifdef __HIPCC__
+#include <hip/hip_runtime.h>
+
+namespace pa {
+
+// Geometry of a paged K/V pool, in elements.
+struct PoolGeom {
+  int32_t num_kv_heads;
+  int32_t head_size;
+  int32_t block_size;
+  int32_t num_blocks;
+  pa_layout layout;
+};
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t key_row_stride,
+                                    int64_t value_row_stride, void* key_cache, void* value_cache,
+                                    const int64_t* slot_mapping, int32_t num_tokens,
+                                    const PoolGeom& g, int elem_bytes, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                              int32_t num_pairs, int64_t block_bytes, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  pa_dtype out_dtype;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  pa_dtype kv_dtype;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;
+  int32_t max_context_len;
+  int32_t num_seqs;
+  int32_t num_heads;
+  PoolGeom geom;
+  float scale;
+  int32_t partition_size;  // 0 = single pass, > 0 = split-K
+  int32_t max_partitions;  // ceil(max_context_len / partition_size) when split
+  float* part_out;         // [num_seqs, num_heads, max_partitions, head_size]
+  float* part_ml;          // [num_seqs, num_heads, max_partitions, 2] (max, sum)
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  pa_dtype out_dtype;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  pa_dtype kv_dtype;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* query_start_loc;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t max_query_len;
+  int32_t num_heads;
+  PoolGeom geom;
+  float scale;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pa
+#endif  // __HIPCC__
+
+#endif  // PA_INTERNAL_H_
