@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Bench of the paged KV-cache hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of the workload:
+  decode workloads:  the cache write of the step's new K/V rows through
+                     slot_mapping (padding rows included), then paged decode
+                     attention (split-K partitions + reduce, or one pass);
+  prefill workloads: the cache write of the packed new rows, then causal
+                     packed prefill over the paged cache.
+Default workload: the 7B-like MHA decode layer (64 sequences, 32 heads,
+head size 128, bf16, block size 16, context lengths U[200, 2048], 71 write
+rows of which 7 are padding).  Inputs are seeded synthetic data already
+resident in device memory when the timed region starts.
+
+Prints ONE JSON line.  `value` = algorithmic KV bytes read per step / step
+time (GB/s) for decode, algorithmic flops / step time (TFLOP/s) for prefill.
+`roofline` covers the dominant kernel, timed with HIP events recorded on the
+stream the kernels run on.  `cpu_baseline` is the fp64 oracle timed on a
+bounded sample of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode KV GB/s (fraction of HBM peak); prefill MFMA util; tokens/s"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16/fp16 MFMA, AMD published
+KERNEL_SOURCES = {"decode": "decode.hip", "prefill": "prefill.hip", "write": "cache_ops.hip"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="2", help="workload: 1, 2, 3, 4, 5a, 5b, 5c")
+    ap.add_argument("--layout", choices=["nhd", "hnd"], default="nhd")
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="decode partition size (-1 auto, 0 single pass)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU work budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_sha(kind: str) -> str:
+    path = os.path.join(ROOT, "paged_kv_cache_134_amd", "csrc", KERNEL_SOURCES[kind])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, kind: str):
+    """HBM bytes per launch of the dominant kernel from a committed counter
+    summary (profiles/<kind>_<workload>_traffic.txt), if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    sha = re.search(r"kernel_source_sha:\s*(\w+)", txt)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not sha or not val or sha.group(1) != source_sha(kind):
+        return None
+    return float(val.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every step of this "
+              "path runs on a single MI355X and no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    import paged_kv_cache_134_amd as P
+    from paged_kv_cache_134_amd import metadata as M
+
+    cfg = args.config if not args.config.isdigit() else int(args.config)
+    w = workloads.make(cfg)
+    layout = P.NHD if args.layout == "nhd" else P.HND
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    dw = M.setup(w, layout=layout)
+    torch.cuda.synchronize()
+    log(f"[bench] set-up of {w.name} took {time.time() - t0:.1f}s")
+    stream = torch.cuda.current_stream()
+
+    S, H, Hkv, D = w.S, w.H, w.Hkv, w.D
+    eb = w.elem_bytes
+    lens = w.context_lens.astype(np.int64)
+    kv_bytes = int(lens.sum()) * Hkv * D * 2 * eb
+    out = torch.empty(w.query_shape, dtype=torch.float32, device="cuda")
+    kinds = []
+
+    if w.kind == "decode":
+        ps = args.partition if args.partition >= 0 else P.pa_decode_auto_partition(
+            S, Hkv, dw.max_context_len)
+        ws = None
+        if ps > 0:
+            ws = torch.empty(P.pa_decode_workspace_size(S, H, D, dw.max_context_len, ps),
+                             dtype=torch.uint8, device="cuda")
+
+        def step(ev):
+            ev[0].record(stream)
+            M.write_step_rows(dw)
+            ev[1].record(stream)
+            if ps > 0:
+                P.pa_decode_partitions(dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                       dw.context_lens, dw.max_context_len, w.scale, ps, ws,
+                                       layout=layout)
+                ev[2].record(stream)
+                P.pa_decode_reduce(out, dw.context_lens, dw.max_context_len, Hkv, ps, ws)
+            else:
+                P.pa_decode(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                            dw.context_lens, dw.max_context_len, w.scale, layout=layout,
+                            partition_size=0)
+                ev[2].record(stream)
+            ev[3].record(stream)
+        kinds = ["reshape_and_cache", "decode_partitions" if ps > 0 else "decode_single_pass",
+                 "decode_reduce"]
+        dominant = 1
+        work_units = S  # tokens decoded per step
+    else:
+        ps = None
+        qlens = w.query_lens.astype(np.int64)
+        ctx = w.context_lens.astype(np.int64)
+        # causal-visible (query, key) pairs: row j of a sequence sees L - n + j + 1 keys
+        pairs = int(sum(n * (L - n) + n * (n + 1) // 2 for n, L in zip(qlens, ctx)))
+        flops = 4 * D * H * pairs
+        max_q = int(qlens.max())
+
+        def step(ev):
+            ev[0].record(stream)
+            M.write_step_rows(dw)
+            ev[1].record(stream)
+            P.pa_prefill(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                         dw.query_start_loc, dw.context_lens, max_q, dw.max_context_len, w.scale,
+                         layout=layout)
+            ev[2].record(stream)
+            ev[3].record(stream)
+        kinds = ["reshape_and_cache", "prefill", None]
+        dominant = 1
+        work_units = int(qlens.sum())
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    for _ in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / max(args.steps, 1)
+    kern_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
+    kernels_us = {k: round(t * 1e3, 3) for k, t in zip(kinds, kern_ms) if k}
+
+    # sampled parity of the last step's output against the oracle's plain definition
+    from oracle import attention as A
+    got = out.cpu().numpy()
+    errs = []
+    sample_seqs = sorted({0, S // 2, S - 1}) if w.kind == "decode" else sorted({0, S - 1})
+    for s in sample_seqs:
+        K, V = w.kv(s)
+        Kf, Vf = A.bits_to_f64(K, w.dtype), A.bits_to_f64(V, w.dtype)
+        qf = A.bits_to_f64(w.query, w.dtype)
+        for h in sorted({0, H - 1}):
+            if w.kind == "decode":
+                ref, _ = A.attention_dense(qf[s, h], Kf[:, h // w.G], Vf[:, h // w.G], w.scale)
+                errs.append(float(np.max(np.abs(got[s, h] - ref))))
+            else:
+                n = int(w.query_lens[s])
+                L = int(w.context_lens[s])
+                for j in sorted({0, n // 2, n - 1}):
+                    a = L - n + j
+                    r = int(w.query_start_loc[s]) + j
+                    ref, _ = A.attention_dense(qf[r, h], Kf[:a + 1, h // w.G], Vf[:a + 1, h // w.G],
+                                               w.scale)
+                    errs.append(float(np.max(np.abs(got[r, h] - ref))))
+    tol = 1e-5 if w.dtype == "f32" else 2e-3
+    parity = {"max_abs": max(errs), "tolerance": tol, "ok": max(errs) <= tol,
+              "sampled": f"sequences {sample_seqs}, heads {sorted({0, H - 1})}"}
+
+    if w.kind == "decode":
+        value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        dom_ms = kern_ms[dominant]
+        achieved = kv_bytes / (dom_ms * 1e-3) / 1e9
+        kind_src = "decode"
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        alg = {"kv_bytes_per_step": kv_bytes}
+    else:
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        dom_ms = kern_ms[dominant]
+        achieved = flops / (dom_ms * 1e-3) / 1e12
+        kind_src = "prefill"
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        alg = {"flops_per_step": flops, "causal_pairs_per_head": pairs}
+    roof["kernel"] = kinds[dominant]
+    roof["traffic"] = traffic_from_profile(w.name, kind_src)
+    roof["kernel_source_sha"] = source_sha(kind_src)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds, unit)
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
+                   "head_size": D, "block_size": w.bs, "layout": args.layout.upper(),
+                   "context_tokens": int(lens.sum()), "write_rows": w.T,
+                   "partition_size": ps, "seed": w.seed},
+        "tokens_per_s": round(work_units / (ms_per_step * 1e-3), 1),
+        "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4) if unit == "GB/s" else None,
+        "kernels_us": kernels_us,
+        **alg,
+        "parity": parity,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, budget_s: float, unit: str):
+    """The fp64 oracle on a bounded sample of the workload, one host thread.
+
+    The oracle's pool is built untimed.  Timed: the oracle cache write of the
+    step's rows (charged pro rata to the sampled sequences) plus the oracle
+    decode / prefill of whole sequences taken in order until the CPU budget
+    is spent.  Reported in the metric's unit over the sample's own work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as A
+    from oracle.state import build_pool, build_state
+
+    st = build_state(w)
+    kc, vc = build_pool(w, st)
+    K, V = w.new_rows()
+    lens = w.context_lens.astype(np.int64)
+    done, secs, work = [], 0.0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kc, vc = A.write_ref(kc, vc, K, V, st.step_slots, w.bs)
+        t_write = time.perf_counter() - t0
+        for s in range(w.S):
+            t0 = time.perf_counter()
+            if w.kind == "decode":
+                A.decode_ref(w.query[s:s + 1], kc, vc, st.block_tables[s:s + 1], lens[s:s + 1],
+                             w.scale, w.bs, w.dtype)
+                work += float(lens[s]) * w.Hkv * w.D * 2 * w.elem_bytes
+            else:
+                a, b = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+                A.prefill_ref(w.query[a:b], kc, vc, st.block_tables[s:s + 1],
+                              np.array([0, b - a]), lens[s:s + 1], w.scale, w.bs, w.dtype)
+                n, L = b - a, int(lens[s])
+                work += 4.0 * w.D * w.H * (n * (L - n) + n * (n + 1) / 2)
+            secs += time.perf_counter() - t0
+            done.append(s)
+            if secs >= budget_s:
+                break
+    secs += t_write * len(done) / w.S
+    value = work / secs / (1e9 if unit == "GB/s" else 1e12)
+    return {"value": round(value, 6), "unit": unit, "cores": 1, "kind": "oracle",
+            "seconds": round(secs, 2),
+            "sample": f"{len(done)} of {w.S} sequences of {w.name} (all heads): oracle {w.kind} "
+                      f"of those sequences + their share of the oracle write of the step rows; "
+                      f"pool built untimed"}
+
+
+if __name__ == "__main__":
+    main()

@@ -150,6 +150,41 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * The two halves of split-K decode, for callers that schedule or time them
+ * separately; pa_decode with partition_size > 0 runs exactly these two.
+ *
+ * pa_decode_partitions -- for every (sequence, query head, partition p) with
+ * tokens t in [p * partition_size, min((p + 1) * partition_size, L)), writes
+ * to `workspace` the partition's running max m_p (log2 units of
+ * scale * q . K), the sum l_p of 2^(z_t - m_p) and the unnormalised output
+ * sum_t 2^(z_t - m_p) V_t (fp32).  Partitions at or past L are not written.
+ * partition_size must be > 0 (or -1 resolving to > 0); other arguments as in
+ * pa_decode.
+ *
+ * pa_decode_reduce -- merges the ceil(L / partition_size) partitions of every
+ * (sequence, head) with the log-sum-exp rule ([vllm] §7.3 V2 reduce):
+ *   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
+ * and writes out (L == 0 gives a zero row).  The workspace, context_lens,
+ * max_context_len and partition_size must be those of the partitions call.
+ */
+pa_status pa_decode_partitions(const void* query, const void* key_cache,
+                               const void* value_cache, pa_dtype kv_dtype,
+                               pa_layout layout, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len,
+                               int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_size,
+                               int32_t block_size, int32_t num_blocks, float scale,
+                               int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+pa_status pa_decode_reduce(void* out, pa_dtype out_dtype,
+                           const int32_t* context_lens, int32_t max_context_len,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_size, int32_t partition_size,
+                           const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill -- causal attention of packed query rows over the paged cache
  * ([vllm] §6.2 flash_attn_varlen_func with cu_seqlens_q = query_start_loc,
  * seqlen_k = seq_lens, block_table, causal = True; [packed] §2.3).

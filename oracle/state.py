@@ -94,8 +94,12 @@ def empty_pool(w, layout=NHD) -> np.ndarray:
     return np.full(shape, np.iinfo(raw).max, dtype=raw)
 
 
-def build_pool(w, st: OracleState, layout=NHD, include_step: bool = False):
-    """Host K and V pools after set-up (and after the step's write if asked)."""
+def build_pool(w, st: OracleState, layout=NHD, include_step: bool = False, seqs=None):
+    """Host K and V pools after set-up (and after the step's write if asked).
+
+    ``seqs`` restricts the per-sequence writes (and the step rows) to those
+    sequences; the shared prefix and the copies are always applied.
+    """
     kc, vc = empty_pool(w, layout), empty_pool(w, layout)
     if st.prefix_slots is not None:
         k, v = w.kv(0, 0, w.prefix_len)
@@ -103,14 +107,23 @@ def build_pool(w, st: OracleState, layout=NHD, include_step: bool = False):
     for src, dst in st.copies:
         kc[dst] = kc[src]
         vc[dst] = vc[src]
-    for s in range(w.S):
+    ks, vs, ss = [], [], []
+    for s in (range(w.S) if seqs is None else seqs):
         pos = st.setup_positions[s]
         if len(pos) == 0:
             continue
         lo, hi = int(pos.min()), int(pos.max()) + 1
         k, v = w.kv(s, lo, hi)
-        kc, vc = write_ref(kc, vc, k[pos - lo], v[pos - lo], st.seq_slots[s][pos], w.bs, layout)
+        ks.append(k[pos - lo])
+        vs.append(v[pos - lo])
+        ss.append(st.seq_slots[s][pos])
+    if ss:
+        kc, vc = write_ref(kc, vc, np.concatenate(ks), np.concatenate(vs), np.concatenate(ss),
+                           w.bs, layout)
     if include_step:
         K, V = w.new_rows()
-        kc, vc = write_ref(kc, vc, K, V, st.step_slots, w.bs, layout)
+        slots = st.step_slots.copy()
+        if seqs is not None:
+            slots[~np.isin(w.row_seq, list(seqs))] = -1
+        kc, vc = write_ref(kc, vc, K, V, slots, w.bs, layout)
     return kc, vc

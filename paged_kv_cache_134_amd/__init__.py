@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m paged_kv_cache_134_amd.build` "
+        f"{LIB_PATH} is not built; run `python paged_kv_cache_134_amd/build.py` "
         "(or __graft_entry__.build()) first")
 
 # Load torch first so that the library binds to the HIP runtime torch already
@@ -42,7 +42,8 @@ NHD, HND = 0, 1
 
 EXPORTED = [
     "pa_status_string", "pa_last_error", "pa_reshape_and_cache", "pa_copy_blocks",
-    "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode", "pa_prefill",
+    "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode", "pa_decode_partitions",
+    "pa_decode_reduce", "pa_prefill",
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
     "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
     "pa_pool_num_free", "pa_pool_refcount",
@@ -62,6 +63,9 @@ _sig = {
     "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_reduce": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "pa_check_metadata": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -205,6 +209,36 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, ma
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, H, hkv, d, bs,
         nb, float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_decode_partitions(query, key_cache, value_cache, block_tables, context_lens,
+                         max_context_len: int, scale: float, partition_size: int, workspace,
+                         layout: int = NHD, stream=None) -> None:
+    """Split-K first half: per-partition (max, sum, unnormalised output) into workspace."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    S, H, D = query.shape
+    if D != d or query.dtype != key_cache.dtype:
+        raise ValueError("query must be [num_seqs, num_heads, head_size] of the cache dtype")
+    _check("pa_decode_partitions", _lib.pa_decode_partitions(
+        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dtype_code(key_cache), layout, _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context_len), S, H, hkv, d, bs, nb, float(scale), int(partition_size),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def pa_decode_reduce(out, context_lens, max_context_len: int, num_kv_heads: int,
+                     partition_size: int, workspace, stream=None) -> None:
+    """Split-K second half: merge the partitions into out [S, H, D]."""
+    torch = _torch()
+    S, H, D = out.shape
+    _check("pa_decode_reduce", _lib.pa_decode_reduce(
+        _dev(out, "out"), _dtype_code(out), _dev(context_lens, "context_lens", torch.int32),
+        int(max_context_len), S, H, int(num_kv_heads), D, int(partition_size),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
 
 
 def pa_prefill(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens,

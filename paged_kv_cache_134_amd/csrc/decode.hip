@@ -280,7 +280,9 @@ hipError_t launch_d(const DecodeParams& p, int D, int G, dim3 grid, hipStream_t 
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+namespace {
+
+DecodeParams make_params(const DecodeArgs& a) {
   const PoolGeom& g = a.geom;
   DecodeParams p{};
   p.out = a.out;
@@ -303,27 +305,40 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.max_blocks_per_seq = a.max_blocks_per_seq;
   p.num_heads = a.num_heads;
   p.num_kv_heads = g.num_kv_heads;
-  p.log2_bs = __builtin_ctz((unsigned)g.block_size);
+  p.log2_bs = g.block_size > 0 ? __builtin_ctz((unsigned)g.block_size) : 0;
   p.partition_size = a.partition_size;
   p.max_partitions = a.max_partitions;
   p.scale_log2e = a.scale * kLog2e;
   p.out_dtype = a.out_dtype;
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
+  const DecodeParams p = make_params(a);
+  const PoolGeom& g = a.geom;
   const int G = a.num_heads / g.num_kv_heads;
   dim3 grid((unsigned)(a.num_seqs * g.num_kv_heads), a.partition_size > 0 ? a.max_partitions : 1);
-  hipError_t e;
   switch (a.kv_dtype) {
-    case PA_F32: e = launch_d<PA_F32>(p, g.head_size, G, grid, stream); break;
-    case PA_BF16: e = launch_d<PA_BF16>(p, g.head_size, G, grid, stream); break;
-    case PA_F16: e = launch_d<PA_F16>(p, g.head_size, G, grid, stream); break;
+    case PA_F32: return launch_d<PA_F32>(p, g.head_size, G, grid, stream);
+    case PA_BF16: return launch_d<PA_BF16>(p, g.head_size, G, grid, stream);
+    case PA_F16: return launch_d<PA_F16>(p, g.head_size, G, grid, stream);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || a.partition_size <= 0) return e;
+}
+
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0 || a.partition_size <= 0) return hipSuccess;
+  const DecodeParams p = make_params(a);
   dim3 rgrid((unsigned)(a.num_seqs * a.num_heads));
-  if (g.head_size == 64)
+  if (a.geom.head_size == 64)
     hipLaunchKernelGGL(decode_reduce_kernel<64>, rgrid, dim3(64), 0, stream, p);
-  else
+  else if (a.geom.head_size == 128)
     hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(128), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -135,6 +135,90 @@ extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, 
   return workspace_bytes(num_seqs, num_heads, head_size, partitions_for(max_context_len, ps));
 }
 
+namespace {
+
+// Checks shared by the decode entry points; fills `a` (workspace pointers
+// included when split) and resolves partition_size -1.
+pa_status decode_prepare(const char* fn, void* out, pa_dtype out_dtype, const void* query,
+                         const void* key_cache, const void* value_cache, pa_dtype kv_dtype,
+                         pa_layout layout, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int32_t num_blocks, float scale,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes_,
+                         bool need_out, bool need_cache, pa::DecodeArgs* a) {
+  char msg[200];
+  auto fail = [&](pa_status st, const char* what) {
+    std::snprintf(msg, sizeof msg, "%s: %s", fn, what);
+    return pa_fail(st, msg);
+  };
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "negative size or no blocks");
+  if (!valid_dtype(kv_dtype) || (out_dtype != PA_F32 && out_dtype != kv_dtype))
+    return fail(PA_ERR_INVALID_ARGUMENT, "bad kv/out dtype");
+  if (layout != PA_LAYOUT_NHD && layout != PA_LAYOUT_HND)
+    return fail(PA_ERR_INVALID_ARGUMENT, "bad layout");
+  if (!valid_group(num_heads, num_kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "num_heads / num_kv_heads must be 1, 2, 4, 8 or 16");
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_size must be 64 or 128");
+  if (!pow2_in(block_size, 1, 1024))
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be a power of two in [1, 1024]");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len exceeds max_blocks_per_seq * block_size");
+  if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0))
+    return fail(PA_ERR_INVALID_ARGUMENT, "partition_size must be -1, 0 or a positive multiple of 16");
+  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale is NaN");
+  if ((int64_t)num_seqs * num_kv_heads > 0x7FFFFFFF || (int64_t)num_seqs * num_heads > 0x7FFFFFFF)
+    return fail(PA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+  int32_t ps = partition_size < 0 ? pa_decode_auto_partition(num_seqs, num_kv_heads, max_context_len)
+                                  : partition_size;
+  const int64_t parts = partitions_for(max_context_len, ps);
+  if (ps > 0 && parts == 0) ps = 0;  // empty contexts: nothing to split
+  if (ps > 0 && parts > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 partitions");
+  *a = pa::DecodeArgs{};
+  a->out = out;
+  a->out_dtype = out_dtype;
+  a->query = query;
+  a->key_cache = key_cache;
+  a->value_cache = value_cache;
+  a->kv_dtype = kv_dtype;
+  a->block_tables = block_tables;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->context_lens = context_lens;
+  a->max_context_len = max_context_len;
+  a->num_seqs = num_seqs;
+  a->num_heads = num_heads;
+  a->geom = pa::PoolGeom{num_kv_heads, head_size, block_size, num_blocks, layout};
+  a->scale = scale;
+  a->partition_size = ps;
+  if (num_seqs == 0) return PA_OK;
+  if (!context_lens || (need_out && !out))
+    return fail(PA_ERR_INVALID_ARGUMENT, "null pointer");
+  if (need_cache) {
+    if (!query || !key_cache || !value_cache || !block_tables)
+      return fail(PA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+      return fail(PA_ERR_INVALID_ARGUMENT, "query and caches must be 16-byte aligned");
+  }
+  if (ps > 0) {
+    const size_t need = workspace_bytes(num_seqs, num_heads, head_size, parts);
+    if (!workspace || workspace_bytes_ < need) {
+      std::snprintf(msg, sizeof msg, "%s: split-K needs %zu workspace bytes, got %zu", fn, need,
+                    workspace ? workspace_bytes_ : (size_t)0);
+      return pa_fail(PA_ERR_WORKSPACE_TOO_SMALL, msg);
+    }
+    if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    a->max_partitions = (int32_t)parts;
+    const size_t out_b = (size_t)num_seqs * num_heads * parts * head_size * sizeof(float);
+    a->part_out = static_cast<float*>(workspace);
+    a->part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((out_b + 255) / 256) * 256);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
                                const void* key_cache, const void* value_cache, pa_dtype kv_dtype,
                                pa_layout layout, const int32_t* block_tables,
@@ -143,69 +227,57 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                                int32_t num_blocks, float scale, int32_t partition_size,
                                void* workspace, size_t workspace_bytes_, void* stream) {
-  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: negative size or no blocks");
-  if (!valid_dtype(kv_dtype) || (out_dtype != PA_F32 && out_dtype != kv_dtype))
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: bad kv/out dtype");
-  if (layout != PA_LAYOUT_NHD && layout != PA_LAYOUT_HND)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: bad layout");
-  if (!valid_group(num_heads, num_kv_heads))
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: num_heads / num_kv_heads must be 1, 2, 4, 8 or 16");
-  if (head_size != 64 && head_size != 128)
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: head_size must be 64 or 128");
-  if (!pow2_in(block_size, 1, 1024))
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size must be a power of two in [1, 1024]");
-  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: max_context_len exceeds max_blocks_per_seq * block_size");
-  if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0))
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: partition_size must be -1, 0 or a positive multiple of 16");
-  if (!(scale == scale)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: scale is NaN");
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: null pointer");
-  if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: query and caches must be 16-byte aligned");
-  if ((int64_t)num_seqs * num_kv_heads > 0x7FFFFFFF)
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: too many (sequence, kv head) pairs");
-  int32_t ps = partition_size < 0 ? pa_decode_auto_partition(num_seqs, num_kv_heads, max_context_len)
-                                  : partition_size;
-  const int64_t parts = partitions_for(max_context_len, ps);
-  if (ps > 0 && parts == 0) ps = 0;  // empty contexts: nothing to split
-  if (ps > 0 && parts > 65535)
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 65535 partitions per sequence");
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.out_dtype = out_dtype;
-  a.query = query;
-  a.key_cache = key_cache;
-  a.value_cache = value_cache;
-  a.kv_dtype = kv_dtype;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.context_lens = context_lens;
-  a.max_context_len = max_context_len;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.geom = pa::PoolGeom{num_kv_heads, head_size, block_size, num_blocks, layout};
-  a.scale = scale;
-  a.partition_size = ps;
-  if (ps > 0) {
-    const size_t need = workspace_bytes(num_seqs, num_heads, head_size, parts);
-    if (!workspace || workspace_bytes_ < need) {
-      char msg[160];
-      std::snprintf(msg, sizeof msg, "pa_decode: split-K needs %zu workspace bytes, got %zu", need,
-                    workspace ? workspace_bytes_ : (size_t)0);
-      return pa_fail(PA_ERR_WORKSPACE_TOO_SMALL, msg);
-    }
-    if (!aligned16(workspace))
-      return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: workspace must be 16-byte aligned");
-    a.max_partitions = (int32_t)parts;
-    const size_t out_b = (size_t)num_seqs * num_heads * parts * head_size * sizeof(float);
-    a.part_out = static_cast<float*>(workspace);
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((out_b + 255) / 256) * 256);
-  }
-  hipError_t e = pa::launch_decode(a, (hipStream_t)stream);
+  pa::DecodeArgs a;
+  pa_status st = decode_prepare("pa_decode", out, out_dtype, query, key_cache, value_cache,
+                                kv_dtype, layout, block_tables, max_blocks_per_seq, context_lens,
+                                max_context_len, num_seqs, num_heads, num_kv_heads, head_size,
+                                block_size, num_blocks, scale, partition_size, workspace,
+                                workspace_bytes_, true, true, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  hipError_t e = pa::launch_decode_main(a, (hipStream_t)stream);
+  if (e == hipSuccess) e = pa::launch_decode_reduce(a, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode");
+}
+
+extern "C" pa_status pa_decode_partitions(const void* query, const void* key_cache,
+                                          const void* value_cache, pa_dtype kv_dtype,
+                                          pa_layout layout, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t max_context_len, int32_t num_seqs,
+                                          int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                          float scale, int32_t partition_size, void* workspace,
+                                          size_t workspace_bytes_, void* stream) {
+  if (partition_size <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_partitions: partition_size must be > 0");
+  pa::DecodeArgs a;
+  pa_status st = decode_prepare("pa_decode_partitions", nullptr, PA_F32, query, key_cache,
+                                value_cache, kv_dtype, layout, block_tables, max_blocks_per_seq,
+                                context_lens, max_context_len, num_seqs, num_heads, num_kv_heads,
+                                head_size, block_size, num_blocks, scale, partition_size, workspace,
+                                workspace_bytes_, false, true, &a);
+  if (st != PA_OK || num_seqs == 0 || a.partition_size == 0) return st;
+  hipError_t e = pa::launch_decode_main(a, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode_partitions");
+}
+
+extern "C" pa_status pa_decode_reduce(void* out, pa_dtype out_dtype, const int32_t* context_lens,
+                                      int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_size,
+                                      int32_t partition_size, const void* workspace,
+                                      size_t workspace_bytes_, void* stream) {
+  if (partition_size <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_reduce: partition_size must be > 0");
+  pa::DecodeArgs a;
+  // the reduce reads no cache: geometry fields are placeholders that pass the checks
+  pa_status st = decode_prepare("pa_decode_reduce", out, out_dtype, nullptr, nullptr, nullptr,
+                                out_dtype == PA_F32 ? PA_F32 : out_dtype, PA_LAYOUT_NHD, nullptr,
+                                max_context_len, context_lens, max_context_len, num_seqs,
+                                num_heads, num_kv_heads, head_size, 1, 1, 1.0f, partition_size,
+                                const_cast<void*>(workspace), workspace_bytes_, true, false, &a);
+  if (st != PA_OK || num_seqs == 0 || a.partition_size == 0) return st;
+  hipError_t e = pa::launch_decode_reduce(a, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode_reduce");
 }
 
 // ---------------------------------------------------------------- prefill

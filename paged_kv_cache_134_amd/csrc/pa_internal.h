@@ -53,7 +53,10 @@ struct DecodeArgs {
   float* part_ml;          // [num_seqs, num_heads, max_partitions, 2] (max, sum)
 };
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Single pass (partition_size == 0) or the split-K partition kernel.
+hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream);
+// Split-K reduce over the partials in part_out / part_ml.
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 
 struct PrefillArgs {
   void* out;
