@@ -7,24 +7,31 @@
 // max/sum rescaling) and the block-wise online softmax of the "Paged
 // attention" post (k4i.top, attention over non-contiguous blocks).
 //
-// Work decomposition (this file's own design for wave64 / CDNA4):
-//   * one workgroup (4 waves) per (sequence, kv head, partition); a kv head's
-//     K/V rows are read once for all G = H / Hkv query heads of its group;
-//   * a token row of one kv head (head_size elements) is spread over LPT lanes
-//     that each own one 16-byte chunk, so every load is a 16-byte vector load
-//     and a wave reads TPW = 64 / LPT whole rows per instruction (coalesced:
-//     the LPT lanes of a row cover its contiguous bytes);
-//   * each lane group keeps its own running (max, sum, acc) per query head;
-//     QK partial dots are summed across the LPT lanes with DPP; the running
-//     max is only moved when a batch's max exceeds it by more than 2^8
-//     (the final result does not depend on where the reference point sits);
-//   * at the end lane groups and waves are merged with the same log-sum-exp
-//     rule, then the workgroup writes either the normalised output or its
-//     partition's (max, sum, unnormalised output) for the reduce kernel.
-// Tokens past the context length are never loaded, so NaN in unused slots or
-// blocks cannot reach the arithmetic.  The order of every floating-point
-// operation depends only on logical positions, so results are bitwise
-// independent of which physical blocks hold the context.
+// Two kernels share one contract; the dispatcher picks by GQA group size G
+// and element type.  Both use one workgroup of 4 waves per (sequence, kv
+// head, partition), read each kv head's K/V rows once for all G query heads
+// of its group, never load a token at or past the context length (so NaN in
+// unused slots cannot reach the arithmetic), and order every floating-point
+// operation by logical position only, so results are bitwise independent of
+// which physical blocks hold the context.  Running maxima are moved lazily:
+// only when a batch exceeds the reference by more than 2^8, since the final
+// quotient does not depend on where the reference sits.
+//
+// Register kernel (G <= 2, and every fp32 case): a token row of one kv head
+// is spread over LPT lanes that each own one 16-byte chunk, so a wave reads
+// TPW = 64 / LPT whole rows per 16-byte load; QK partial dots are summed
+// across the LPT lanes with DPP.  The partition's block-table entries are
+// staged in LDS, and the next batch of rows is loaded while the current one
+// is consumed.
+//
+// LDS kernel (G >= 4, bf16/f16): per chunk of 64 tokens the workgroup copies
+// K and V rows (coalesced 16-byte loads, prefetched one chunk ahead in
+// registers) into LDS.  QK: lane = token, each wave owns G/4 query heads
+// whose query vectors are read as scalar (SGPR) operands of v_dot2, and K
+// rows are read from a swizzled LDS layout (16 lanes hit 16 distinct bank
+// groups); no cross-lane reduction and one exp per (token, head).  PV: lane
+// owns D/32 output columns of all G heads and each wave a quarter of the
+// chunk's tokens; probabilities are broadcast from LDS.
 #include <hip/hip_runtime.h>
 
 #include "kernel_common.h"
@@ -35,8 +42,9 @@ namespace {
 
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = kDecodeWaves * kWave;
-constexpr int kUnroll = 4;          // token rows per lane group per batch
-constexpr float kLazyRescale = 8.f; // log2 headroom before the running max moves
+constexpr float kLazyRescale = 8.f;  // log2 headroom before a running max moves
+
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
 
 struct DecodeParams {
   void* out;
@@ -60,22 +68,57 @@ struct DecodeParams {
   pa_dtype out_dtype;
 };
 
+// Maximum over the 64 lanes of a wave (every lane receives it).
+__device__ __forceinline__ float wave_max(float x) {
+  x = group_max<16>(x);
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Writes one (max, sum, unnormalised output) partial or the final output.
+__device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int part, int d, int D,
+                                     float M, float lsum, float o) {
+  if (p.partition_size > 0) {
+    const int64_t pi = head * p.max_partitions + part;
+    p.part_out[pi * D + d] = o;
+    if (d == 0) {
+      p.part_ml[2 * pi] = M;
+      p.part_ml[2 * pi + 1] = lsum;
+    }
+  } else {
+    store_out(p.out, head * D + d, lsum > 0.f ? o / lsum : 0.f, p.out_dtype);
+  }
+}
+
+// ------------------------------------------------------------ register kernel
+constexpr int kUnroll = 4;    // token rows per lane group per batch
+constexpr int kWindow = 512;  // tokens per block-table staging window
+
 template <pa_dtype DT, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const DecodeParams p) {
   using F = Fmt<DT>;
-  constexpr int VEC = F::kVec;         // elements per lane chunk
-  constexpr int LPT = D / VEC;         // lanes per token row
-  constexpr int TPW = kWave / LPT;     // token rows per wave per step
+  constexpr int VEC = F::kVec;             // elements per lane chunk
+  constexpr int LPT = D / VEC;             // lanes per token row
+  constexpr int TPW = kWave / LPT;         // token rows per wave per step
   constexpr int TPS = TPW * kDecodeWaves;  // token rows per workgroup per step
   static_assert(LPT >= 1 && LPT <= kWave && (kWave % LPT) == 0, "bad head size");
+  __shared__ int32_t s_bt[kWindow + 1];
 
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int s = blockIdx.x / p.num_kv_heads;
   const int part = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int tg = lane / LPT;   // lane group (token row) within the wave
-  const int ch = lane % LPT;   // 16-byte chunk of the row owned by this lane
+  const int tg = lane / LPT;  // lane group (token row) within the wave
+  const int ch = lane % LPT;  // 16-byte chunk of the row owned by this lane
 
   const int L = p.context_lens[s];
   int t0 = 0, t1 = L;
@@ -85,7 +128,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
     t1 = min(L, t0 + p.partition_size);
   }
 
-  // query chunks of the G heads of this kv group
   uint4 q[G];
   {
     const uint4* qp = reinterpret_cast<const uint4*>(p.query) +
@@ -104,68 +146,92 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
   }
 
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-  const int bs_mask = (1 << p.log2_bs) - 1;
+  const int lbs = p.log2_bs;
+  const int bs_mask = (1 << lbs) - 1;
   const int64_t lane_off = (int64_t)kvh * p.head_stride + ch * VEC;
 
-  // wave-uniform trip count: lane groups past the end run with invalid rows
-  for (int wbase = t0 + wave * TPW; wbase < t1; wbase += kUnroll * TPS) {
-    uint4 kr[kUnroll], vr[kUnroll];
-    bool valid[kUnroll];
+  for (int w0 = t0; w0 < t1; w0 += kWindow) {
+    const int w1 = min(t1, w0 + kWindow);
+    const int e0 = w0 >> lbs;
+    const int ne = ((w1 - 1) >> lbs) - e0 + 1;
+    __syncthreads();  // the previous window's readers are done
+    for (int i = threadIdx.x; i < ne; i += kDecodeThreads) s_bt[i] = bt[e0 + i];
+    __syncthreads();
+
+    auto load = [&](int wbase, uint4 (&kr)[kUnroll], uint4 (&vr)[kUnroll], bool (&valid)[kUnroll]) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = wbase + u * TPS + tg;
-      valid[u] = t < t1;
-      if (valid[u]) {
-        const int64_t blk = bt[t >> p.log2_bs];
-        const int64_t off = blk * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride + lane_off;
-        kr[u] = *reinterpret_cast<const uint4*>(p.key_cache + off * F::kBytes);
-        vr[u] = *reinterpret_cast<const uint4*>(p.value_cache + off * F::kBytes);
-      } else {
+      for (int u = 0; u < kUnroll; ++u) {
+        const int t = wbase + u * TPS + tg;
+        valid[u] = t < w1;
         kr[u] = make_uint4(0, 0, 0, 0);
         vr[u] = make_uint4(0, 0, 0, 0);
+        if (valid[u]) {
+          const int64_t blk = s_bt[(t >> lbs) - e0];
+          const int64_t off = blk * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride + lane_off;
+          kr[u] = load_nt(p.key_cache + off * F::kBytes);
+          vr[u] = load_nt(p.value_cache + off * F::kBytes);
+        }
       }
-    }
-    // scores (log2 domain)
-    float z[kUnroll][G];
+    };
+
+    uint4 kr[kUnroll], vr[kUnroll];
+    bool valid[kUnroll];
+    int wbase = w0 + wave * TPW;  // wave-uniform: groups past the end carry invalid rows
+    if (wbase < w1) load(wbase, kr, vr, valid);
+    for (; wbase < w1; wbase += kUnroll * TPS) {
+      uint4 kn[kUnroll], vn[kUnroll];
+      bool validn[kUnroll];
+      const bool more = wbase + kUnroll * TPS < w1;
+      if (more) load(wbase + kUnroll * TPS, kn, vn, validn);
+
+      float z[kUnroll][G];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float d = group_sum<LPT>(dot_chunk<DT>(q[g], kr[u], 0.f));
+          z[u][g] = valid[u] ? d * p.scale_log2e : -INFINITY;
+        }
+      }
+      bool need = false;
+      float mb[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float d = group_sum<LPT>(dot_chunk<DT>(q[g], kr[u], 0.f));
-        z[u][g] = valid[u] ? d * p.scale_log2e : -INFINITY;
+        mb[g] = z[0][g];
+#pragma unroll
+        for (int u = 1; u < kUnroll; ++u) mb[g] = fmaxf(mb[g], z[u][g]);
+        need |= mb[g] > m[g] + kLazyRescale;
       }
-    }
-    // move the running max only when the batch exceeds it by the headroom
-    bool need = false;
-    float mb[G];
+      if (__any(need)) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      mb[g] = z[0][g];
+        for (int g = 0; g < G; ++g) {
+          const float mn = fmaxf(m[g], mb[g]);
+          const float a = exp2_diff(m[g], mn);
+          m[g] = mn;
+          l[g] *= a;
 #pragma unroll
-      for (int u = 1; u < kUnroll; ++u) mb[g] = fmaxf(mb[g], z[u][g]);
-      need |= mb[g] > m[g] + kLazyRescale;
-    }
-    if (__any(need)) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float mn = fmaxf(m[g], mb[g]);
-        const float a = exp2_diff(m[g], mn);
-        m[g] = mn;
-        l[g] *= a;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[g][e] *= a;
+          for (int e = 0; e < VEC; ++e) acc[g][e] *= a;
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float vf[VEC];
-      chunk_to_f32<DT>(vr[u], vf);
+      for (int u = 0; u < kUnroll; ++u) {
+        float vf[VEC];
+        chunk_to_f32<DT>(vr[u], vf);
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float pw = valid[u] ? __builtin_amdgcn_exp2f(z[u][g] - m[g]) : 0.f;
-        l[g] += pw;
+        for (int g = 0; g < G; ++g) {
+          const float pw = valid[u] ? __builtin_amdgcn_exp2f(z[u][g] - m[g]) : 0.f;
+          l[g] += pw;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[g][e] = __builtin_fmaf(pw, vf[e], acc[g][e]);
+          for (int e = 0; e < VEC; ++e) acc[g][e] = __builtin_fmaf(pw, vf[e], acc[g][e]);
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          kr[u] = kn[u];
+          vr[u] = vn[u];
+          valid[u] = validn[u];
+        }
       }
     }
   }
@@ -221,51 +287,307 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodePara
       lsum += a * sm_l[w][g];
       o += a * sm_acc[w][g][d];
     }
-    if (p.partition_size > 0) {
-      const int64_t pi = (head0 + g) * p.max_partitions + part;
-      p.part_out[pi * D + d] = o;
-      if (d == 0) {
-        p.part_ml[2 * pi] = M;
-        p.part_ml[2 * pi + 1] = lsum;
-      }
-    } else {
-      store_out(p.out, (head0 + g) * D + d, lsum > 0.f ? o / lsum : 0.f, p.out_dtype);
-    }
+    emit(p, head0 + g, part, d, D, M, lsum, o);
   }
 }
 
-// Reduce of split-K partials ("V2" reduce): for one (sequence, head),
-// M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the
-// partitions that hold tokens.  One thread per output element.
+// ----------------------------------------------------------------- LDS kernel
+constexpr int kChunk = 64;  // tokens per LDS chunk (one per lane in QK)
+
+// 4 waves per SIMD (<= 128 VGPRs): with ~33 KB of LDS per workgroup that is
+// 4 workgroups, i.e. 128 KB of prefetched K/V in flight, per CU.  (G = 16 at
+// head size 128 needs more accumulators and settles for 2.)
+template <pa_dtype DT, int D, int G>
+__global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void decode_lds_kernel(
+    const DecodeParams p) {
+  static_assert(DT != PA_F32, "LDS kernel takes 16-bit elements");
+  static_assert(G % kDecodeWaves == 0, "G must be a multiple of 4");
+  constexpr int RC = D / 8;                        // 16-byte pieces per row
+  constexpr int PIECES = kChunk * RC;              // pieces per chunk of K (or V)
+  constexpr int PPT = PIECES / kDecodeThreads;     // pieces per thread per tensor
+  constexpr int HPW = G / kDecodeWaves;            // query heads per wave in QK
+  constexpr int DPL = D / 32;                      // output columns per lane in PV
+  static_assert(PPT * kDecodeThreads == PIECES, "chunk must split evenly");
+  __shared__ uint4 sKV[2 * PIECES];                // K (swizzled) then V; reused at the end
+  __shared__ float sP[kChunk][G];                  // probabilities of the chunk
+  __shared__ float sAlpha[G];                      // per-head rescale of this chunk
+  __shared__ float sM[G], sL[G];
+  uint4* sK = sKV;
+  uint4* sV = sKV + PIECES;
+
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int s = blockIdx.x / p.num_kv_heads;
+  const int part = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+
+  const int L = p.context_lens[s];
+  int t0 = 0, t1 = L;
+  if (p.partition_size > 0) {
+    t0 = part * p.partition_size;
+    if (t0 >= L) return;
+    t1 = min(L, t0 + p.partition_size);
+  }
+
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+  const int lbs = p.log2_bs;
+  const int bs_mask = (1 << lbs) - 1;
+  const int64_t head_off = (int64_t)kvh * p.head_stride;
+
+  // query vectors of this wave's heads as scalar operands (bf16/f16 pairs)
+  const const_u32_ptr qc = (const_u32_ptr)((const char*)p.query +
+      (((int64_t)s * p.num_heads + (int64_t)kvh * G + wave * HPW) * D) * 2);
+
+  auto fetch = [&](int c0, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int piece = tid + kDecodeThreads * r;
+      const int row = piece / RC, col = piece % RC;
+      const int t = c0 + row;
+      kr[r] = make_uint4(0, 0, 0, 0);
+      vr[r] = make_uint4(0, 0, 0, 0);
+      if (t < t1) {
+        const int64_t off = (int64_t)bt[t >> lbs] * p.blk_stride +
+                            (int64_t)(t & bs_mask) * p.tok_stride + head_off + col * 8;
+        kr[r] = load_nt(p.key_cache + off * 2);
+        vr[r] = load_nt(p.value_cache + off * 2);
+      }
+    }
+  };
+
+  float m_ref[HPW], l_lane[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    m_ref[hh] = -INFINITY;
+    l_lane[hh] = 0.f;
+  }
+  float acc[G][DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+
+  const int half = lane / 32;  // PV: token parity within a pair
+  const int dl = lane % 32;    // PV: output columns dl*DPL .. +DPL-1
+
+  uint4 kr[PPT], vr[PPT];
+  fetch(t0, kr, vr);
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+    __syncthreads();  // previous chunk fully consumed
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int piece = tid + kDecodeThreads * r;
+      const int row = piece / RC, col = piece % RC;
+      sK[row * RC + (col ^ (row % RC))] = kr[r];
+      sV[piece] = vr[r];
+    }
+    __syncthreads();
+    if (c0 + kChunk < t1) fetch(c0 + kChunk, kr, vr);  // next chunk in flight
+
+    // ---- QK: lane = token row, this wave's HPW heads
+    {
+      const int row = lane;
+      const bool valid = c0 + row < t1;
+      float z[HPW];
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) z[hh] = 0.f;
+#pragma unroll 1
+      for (int pc = 0; pc < RC; pc += 4) {
+        uint4 kk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kk[j] = sK[row * RC + ((pc + j) ^ (row % RC))];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          const const_u32_ptr qh = qc + hh * (D / 2) + pc * 4;
+          float a = z[hh];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint4 qq = make_uint4(qh[4 * j], qh[4 * j + 1], qh[4 * j + 2], qh[4 * j + 3]);
+            a = dot_chunk<DT>(qq, kk[j], a);
+          }
+          z[hh] = a;
+        }
+      }
+      // ---- online softmax of this wave's heads
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const int h = wave * HPW + hh;
+        const float zz = valid ? z[hh] * p.scale_log2e : -INFINITY;
+        const float mc = wave_max(zz);
+        float alpha = 1.f;
+        if (mc > m_ref[hh] + kLazyRescale) {
+          const float mn = fmaxf(m_ref[hh], mc);
+          alpha = exp2_diff(m_ref[hh], mn);
+          m_ref[hh] = mn;
+          l_lane[hh] *= alpha;
+        }
+        const float pw = valid ? __builtin_amdgcn_exp2f(zz - m_ref[hh]) : 0.f;
+        l_lane[hh] += pw;
+        sP[row][h] = pw;
+        if (lane == 0) sAlpha[h] = alpha;
+      }
+    }
+    __syncthreads();
+
+    // ---- PV: wave owns rows 16*wave .. +15, half-waves take alternate rows
+    {
+      float al[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) al[h] = sAlpha[h];
+      bool resc = false;
+#pragma unroll
+      for (int h = 0; h < G; ++h) resc |= al[h] != 1.f;
+      if (resc) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[h][e] *= al[h];
+      }
+      const int rows = min(kChunk, t1 - c0);
+#pragma unroll 2
+      for (int i = 0; i < kChunk / kDecodeWaves / 2; ++i) {
+        const int row = wave * (kChunk / kDecodeWaves) + 2 * i + half;
+        if (wave * (kChunk / kDecodeWaves) + 2 * i >= rows) break;  // wave-uniform
+        float vf[DPL];
+        const char* vrow = reinterpret_cast<const char*>(sV + row * RC) + dl * DPL * 2;
+        uint4 vw = make_uint4(0, 0, 0, 0);
+        if constexpr (DPL == 4) {
+          const uint2 w2 = *reinterpret_cast<const uint2*>(vrow);
+          vw.x = w2.x;
+          vw.y = w2.y;
+        } else {
+          vw.x = *reinterpret_cast<const uint32_t*>(vrow);
+        }
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) vf[e] = chunk_elem<DT>(vw, e);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pw = sP[row][h];
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[h][e] = __builtin_fmaf(pw, vf[e], acc[h][e]);
+        }
+      }
+    }
+  }
+
+  // ---- merge: halves, then waves; statistics from the QK waves
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const float lt = wave_sum(l_lane[hh]);
+    if (lane == 0) {
+      sM[wave * HPW + hh] = m_ref[hh];
+      sL[wave * HPW + hh] = lt;
+    }
+  }
+  __syncthreads();  // last PV done: LDS tiles free for the merge
+  float* sAcc = reinterpret_cast<float*>(sKV);  // [waves][G][D]
+  if (half == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sAcc[(wave * G + h) * D + dl * DPL + e] = acc[h][e];
+  }
+  __syncthreads();
+  const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
+  for (int i = tid; i < G * D; i += kDecodeThreads) {
+    const int h = i / D, d = i % D;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) o += sAcc[(w * G + h) * D + d];
+    emit(p, head0 + h, part, d, D, sM[h], sL[h], o);
+  }
+}
+
+// --------------------------------------------------------------------- reduce
+// Split-K reduce ("V2" reduce): for one (sequence, head), M = max_p m_p and
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the partitions
+// that hold tokens.  Thread (group, d) accumulates column d over every
+// SPLIT-th partition, 8 partitions' loads in flight together.
+constexpr int kReduceThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const DecodeParams p) {
+  constexpr int SPLIT = kReduceThreads / D;
+  __shared__ float red[kReduceThreads / kWave];
+  __shared__ float part_o[SPLIT][D];
+  __shared__ float part_l[SPLIT];
   const int64_t sh = blockIdx.x;  // s * num_heads + h
   const int s = (int)(sh / p.num_heads);
-  const int d = threadIdx.x;
   const int L = p.context_lens[s];
   const int np = (L + p.partition_size - 1) / p.partition_size;
   const float* ml = p.part_ml + sh * p.max_partitions * 2;
-  const float* po = p.part_out + sh * p.max_partitions * D + d;
+  const float* po = p.part_out + sh * p.max_partitions * D;
+  const int tid = threadIdx.x;
+
   float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, ml[2 * i]);
-  float lsum = 0.f, o = 0.f;
-  for (int i = 0; i < np; ++i) {
+  for (int i = tid; i < np; i += kReduceThreads) M = fmaxf(M, ml[2 * i]);
+  M = wave_max(M);
+  if (tid % kWave == 0) red[tid / kWave] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < kReduceThreads / kWave; ++w) M = fmaxf(M, red[w]);
+
+  const int d = tid % D, grp = tid / D;
+  float o = 0.f, lsum = 0.f;
+  int i = grp;
+  for (; i + 7 * SPLIT < np; i += 8 * SPLIT) {
+    float mv[8], lv[8], ov[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      mv[k] = ml[2 * (i + k * SPLIT)];
+      lv[k] = ml[2 * (i + k * SPLIT) + 1];
+      ov[k] = po[(int64_t)(i + k * SPLIT) * D + d];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float a = exp2_diff(mv[k], M);
+      lsum += a * lv[k];
+      o += a * ov[k];
+    }
+  }
+  for (; i < np; i += SPLIT) {
     const float a = exp2_diff(ml[2 * i], M);
     lsum += a * ml[2 * i + 1];
-    o += a * po[(int64_t)i * D];
+    o += a * po[(int64_t)i * D + d];
   }
-  store_out(p.out, sh * D + d, lsum > 0.f ? o / lsum : 0.f, p.out_dtype);
+  part_o[grp][d] = o;
+  if (d == 0) part_l[grp] = lsum;
+  __syncthreads();
+  if (grp == 0) {
+    float ot = 0.f, lt = 0.f;
+#pragma unroll
+    for (int g = 0; g < SPLIT; ++g) {
+      ot += part_o[g][d];
+      lt += part_l[g];
+    }
+    store_out(p.out, sh * D + d, lt > 0.f ? ot / lt : 0.f, p.out_dtype);
+  }
 }
 
+// ------------------------------------------------------------------- dispatch
 template <pa_dtype DT, int D>
 hipError_t launch_g(const DecodeParams& p, int G, dim3 grid, hipStream_t st) {
   dim3 block(kDecodeThreads);
+  if constexpr (DT != PA_F32) {
+    switch (G) {
+      case 4: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 4>), grid, block, 0, st, p); return hipGetLastError();
+      case 8: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 8>), grid, block, 0, st, p); return hipGetLastError();
+      case 16: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 16>), grid, block, 0, st, p); return hipGetLastError();
+      default: break;
+    }
+  }
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<DT, D, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<DT, D, 2>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<DT, D, 4>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<DT, D, 8>), grid, block, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((decode_kernel<DT, D, 16>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 2>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 4>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 8>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 16>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -277,10 +599,6 @@ hipError_t launch_d(const DecodeParams& p, int D, int G, dim3 grid, hipStream_t 
   if (D == 128) return launch_g<DT, 128>(p, G, grid, st);
   return hipErrorInvalidValue;
 }
-
-}  // namespace
-
-namespace {
 
 DecodeParams make_params(const DecodeArgs& a) {
   const PoolGeom& g = a.geom;
@@ -334,9 +652,9 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
   const DecodeParams p = make_params(a);
   dim3 rgrid((unsigned)(a.num_seqs * a.num_heads));
   if (a.geom.head_size == 64)
-    hipLaunchKernelGGL(decode_reduce_kernel<64>, rgrid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_reduce_kernel<64>, rgrid, dim3(kReduceThreads), 0, stream, p);
   else if (a.geom.head_size == 128)
-    hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(kReduceThreads), 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

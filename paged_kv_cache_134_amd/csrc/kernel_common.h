@@ -16,6 +16,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed once: K/V rows in decode).
+__device__ __forceinline__ uint4 load_nt(const void* ptr) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Elements per 16-byte chunk.
 template <pa_dtype DT>
 struct Fmt {
