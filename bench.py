@@ -122,7 +122,7 @@ def main():
             M.write_step_rows(dw)
             ev[1].record(stream)
             if ps > 0:
-                P.pa_decode_partitions(dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                P.pa_decode_partitions(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
                                        dw.context_lens, dw.max_context_len, w.scale, ps, ws,
                                        layout=layout)
                 ev[2].record(stream)

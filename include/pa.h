@@ -158,16 +158,20 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
  * to `workspace` the partition's running max m_p (log2 units of
  * scale * q . K), the sum l_p of 2^(z_t - m_p) and the unnormalised output
  * sum_t 2^(z_t - m_p) V_t (fp32).  Partitions at or past L are not written.
+ * Heads of sequences whose whole context is one partition (L <=
+ * partition_size) get their final row written to `out` directly instead.
  * partition_size must be > 0 (or -1 resolving to > 0); other arguments as in
  * pa_decode.
  *
  * pa_decode_reduce -- merges the ceil(L / partition_size) partitions of every
- * (sequence, head) with the log-sum-exp rule ([vllm] §7.3 V2 reduce):
+ * (sequence, head) with L > partition_size using the log-sum-exp rule
+ * ([vllm] §7.3 V2 reduce):
  *   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
- * and writes out (L == 0 gives a zero row).  The workspace, context_lens,
- * max_context_len and partition_size must be those of the partitions call.
+ * and writes those rows of out; the other rows were written by the
+ * partitions call.  The workspace, out, context_lens, max_context_len and
+ * partition_size must be those of the partitions call.
  */
-pa_status pa_decode_partitions(const void* query, const void* key_cache,
+pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const void* query, const void* key_cache,
                                const void* value_cache, pa_dtype kv_dtype,
                                pa_layout layout, const int32_t* block_tables,
                                int32_t max_blocks_per_seq,

@@ -63,7 +63,7 @@ _sig = {
     "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
-    "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
+    "pa_decode_partitions": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
@@ -211,17 +211,18 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, ma
         nb, float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
 
 
-def pa_decode_partitions(query, key_cache, value_cache, block_tables, context_lens,
+def pa_decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens,
                          max_context_len: int, scale: float, partition_size: int, workspace,
                          layout: int = NHD, stream=None) -> None:
-    """Split-K first half: per-partition (max, sum, unnormalised output) into workspace."""
+    """Split-K first half: per-partition (max, sum, unnormalised output) into
+    workspace; rows of single-partition contexts go straight to out."""
     torch = _torch()
     nb, bs, hkv, d = _geom(key_cache, layout)
     S, H, D = query.shape
-    if D != d or query.dtype != key_cache.dtype:
-        raise ValueError("query must be [num_seqs, num_heads, head_size] of the cache dtype")
+    if D != d or query.dtype != key_cache.dtype or out.shape != query.shape:
+        raise ValueError("query/out must be [num_seqs, num_heads, head_size] of the cache dtype")
     _check("pa_decode_partitions", _lib.pa_decode_partitions(
-        _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(out, "out"), _dtype_code(out), _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
         _dtype_code(key_cache), layout, _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
         int(max_context_len), S, H, hkv, d, bs, nb, float(scale), int(partition_size),

@@ -83,10 +83,11 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Writes one (max, sum, unnormalised output) partial or the final output.
+// Writes one (max, sum, unnormalised output) partial, or the final output
+// when the whole context is one partition (the reduce skips those heads).
 __device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int part, int d, int D,
-                                     float M, float lsum, float o) {
-  if (p.partition_size > 0) {
+                                     float M, float lsum, float o, bool single) {
+  if (p.partition_size > 0 && !single) {
     const int64_t pi = head * p.max_partitions + part;
     p.part_out[pi * D + d] = o;
     if (d == 0) {
@@ -158,32 +159,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
     for (int i = threadIdx.x; i < ne; i += kDecodeThreads) s_bt[i] = bt[e0 + i];
     __syncthreads();
 
+    // Rows past the window are clamped to its last row (finite data loaded
+    // anyway) and masked by `valid`, so the loads are unconditional and none
+    // waits for another.
     auto load = [&](int wbase, uint4 (&kr)[kUnroll], uint4 (&vr)[kUnroll], bool (&valid)[kUnroll]) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int t = wbase + u * TPS + tg;
         valid[u] = t < w1;
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-        if (valid[u]) {
-          const int64_t blk = s_bt[(t >> lbs) - e0];
-          const int64_t off = blk * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride + lane_off;
-          kr[u] = load_nt(p.key_cache + off * F::kBytes);
-          vr[u] = load_nt(p.value_cache + off * F::kBytes);
-        }
+        const int tc = min(t, w1 - 1);
+        const int64_t blk = s_bt[(tc >> lbs) - e0];
+        const int64_t off = blk * p.blk_stride + (int64_t)(tc & bs_mask) * p.tok_stride + lane_off;
+        kr[u] = load_nt(p.key_cache + off * F::kBytes);
+        vr[u] = load_nt(p.value_cache + off * F::kBytes);
       }
     };
 
-    uint4 kr[kUnroll], vr[kUnroll];
-    bool valid[kUnroll];
-    int wbase = w0 + wave * TPW;  // wave-uniform: groups past the end carry invalid rows
-    if (wbase < w1) load(wbase, kr, vr, valid);
-    for (; wbase < w1; wbase += kUnroll * TPS) {
-      uint4 kn[kUnroll], vn[kUnroll];
-      bool validn[kUnroll];
-      const bool more = wbase + kUnroll * TPS < w1;
-      if (more) load(wbase + kUnroll * TPS, kn, vn, validn);
-
+    // consume one batch: scores, lazy rescale, probabilities, V accumulation
+    auto consume = [&](int wbase, const uint4 (&kr)[kUnroll], const uint4 (&vr)[kUnroll]) {
+      bool valid[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) valid[u] = wbase + u * TPS + tg < w1;
       float z[kUnroll][G];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -225,14 +221,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
           for (int e = 0; e < VEC; ++e) acc[g][e] = __builtin_fmaf(pw, vf[e], acc[g][e]);
         }
       }
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          kr[u] = kn[u];
-          vr[u] = vn[u];
-          valid[u] = validn[u];
-        }
-      }
+    };
+
+    // ping-pong buffers: the next batch is always in flight (its rows past
+    // the window are clamped, so the load is unconditional and no wait merges
+    // across a branch)
+    constexpr int kStep = kUnroll * TPS;
+    uint4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
+    bool dummy[kUnroll];
+    int wbase = w0 + wave * TPW;  // wave-uniform: groups past the end carry invalid rows
+    load(wbase, ka, va, dummy);
+    while (wbase < w1) {
+      load(wbase + kStep, kb, vb, dummy);
+      consume(wbase, ka, va);
+      wbase += kStep;
+      if (wbase >= w1) break;
+      load(wbase + kStep, ka, va, dummy);
+      consume(wbase, kb, vb);
+      wbase += kStep;
     }
   }
 
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
       lsum += a * sm_l[w][g];
       o += a * sm_acc[w][g][d];
     }
-    emit(p, head0 + g, part, d, D, M, lsum, o);
+    emit(p, head0 + g, part, d, D, M, lsum, o, L <= p.partition_size);
   }
 }
 
@@ -339,20 +345,25 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
   const const_u32_ptr qc = (const_u32_ptr)((const char*)p.query +
       (((int64_t)s * p.num_heads + (int64_t)kvh * G + wave * HPW) * D) * 2);
 
+  // Rows at or past the end are clamped to the last row (a valid, finite
+  // row the chunk loads anyway) and masked where they are used, so every load
+  // is unconditional and all block-table reads of a fetch go out before the
+  // K/V reads: nothing serialises the 2 * PPT row loads.
   auto fetch = [&](int c0, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
+    int32_t blk[PPT];
+    int tc[PPT];
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {
-      const int piece = tid + kDecodeThreads * r;
-      const int row = piece / RC, col = piece % RC;
-      const int t = c0 + row;
-      kr[r] = make_uint4(0, 0, 0, 0);
-      vr[r] = make_uint4(0, 0, 0, 0);
-      if (t < t1) {
-        const int64_t off = (int64_t)bt[t >> lbs] * p.blk_stride +
-                            (int64_t)(t & bs_mask) * p.tok_stride + head_off + col * 8;
-        kr[r] = load_nt(p.key_cache + off * 2);
-        vr[r] = load_nt(p.value_cache + off * 2);
-      }
+      tc[r] = min(c0 + (tid + kDecodeThreads * r) / RC, t1 - 1);
+      blk[r] = bt[tc[r] >> lbs];
+    }
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int col = (tid + kDecodeThreads * r) % RC;
+      const int64_t off = (int64_t)blk[r] * p.blk_stride +
+                          (int64_t)(tc[r] & bs_mask) * p.tok_stride + head_off + col * 8;
+      kr[r] = load_nt(p.key_cache + off * 2);
+      vr[r] = load_nt(p.value_cache + off * 2);
     }
   };
 
@@ -499,75 +510,66 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
     float o = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) o += sAcc[(w * G + h) * D + d];
-    emit(p, head0 + h, part, d, D, sM[h], sL[h], o);
+    emit(p, head0 + h, part, d, D, sM[h], sL[h], o, L <= p.partition_size);
   }
 }
 
 // --------------------------------------------------------------------- reduce
 // Split-K reduce ("V2" reduce): for one (sequence, head), M = max_p m_p and
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the partitions
-// that hold tokens.  Thread (group, d) accumulates column d over every
-// SPLIT-th partition, 8 partitions' loads in flight together.
+// that hold tokens.  One wave per (sequence, head), D/64 columns per lane,
+// 8 partitions' loads in flight together.  Heads whose context is a single
+// partition were written directly by the partition kernel.
 constexpr int kReduceThreads = 256;
 
 template <int D>
-__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const DecodeParams p) {
-  constexpr int SPLIT = kReduceThreads / D;
-  __shared__ float red[kReduceThreads / kWave];
-  __shared__ float part_o[SPLIT][D];
-  __shared__ float part_l[SPLIT];
-  const int64_t sh = blockIdx.x;  // s * num_heads + h
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const DecodeParams p,
+                                                                       int64_t num_pairs) {
+  constexpr int CPL = D / kWave;  // columns per lane
+  const int64_t sh = (int64_t)blockIdx.x * (kReduceThreads / kWave) + threadIdx.x / kWave;
+  if (sh >= num_pairs) return;
+  const int lane = threadIdx.x % kWave;
   const int s = (int)(sh / p.num_heads);
   const int L = p.context_lens[s];
+  if (L <= p.partition_size) return;
   const int np = (L + p.partition_size - 1) / p.partition_size;
   const float* ml = p.part_ml + sh * p.max_partitions * 2;
-  const float* po = p.part_out + sh * p.max_partitions * D;
-  const int tid = threadIdx.x;
+  const float* po = p.part_out + sh * p.max_partitions * D + lane * CPL;
 
   float M = -INFINITY;
-  for (int i = tid; i < np; i += kReduceThreads) M = fmaxf(M, ml[2 * i]);
+  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[2 * i]);
   M = wave_max(M);
-  if (tid % kWave == 0) red[tid / kWave] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int w = 1; w < kReduceThreads / kWave; ++w) M = fmaxf(M, red[w]);
 
-  const int d = tid % D, grp = tid / D;
-  float o = 0.f, lsum = 0.f;
-  int i = grp;
-  for (; i + 7 * SPLIT < np; i += 8 * SPLIT) {
-    float mv[8], lv[8], ov[8];
+  float o[CPL], lsum = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) o[c] = 0.f;
+  int i = 0;
+  for (; i + 8 <= np; i += 8) {
+    float mv[8], lv[8], ov[8][CPL];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      mv[k] = ml[2 * (i + k * SPLIT)];
-      lv[k] = ml[2 * (i + k * SPLIT) + 1];
-      ov[k] = po[(int64_t)(i + k * SPLIT) * D + d];
+      mv[k] = ml[2 * (i + k)];
+      lv[k] = ml[2 * (i + k) + 1];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ov[k][c] = po[(int64_t)(i + k) * D + c];
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float a = exp2_diff(mv[k], M);
       lsum += a * lv[k];
-      o += a * ov[k];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o[c] += a * ov[k][c];
     }
   }
-  for (; i < np; i += SPLIT) {
+  for (; i < np; ++i) {
     const float a = exp2_diff(ml[2 * i], M);
     lsum += a * ml[2 * i + 1];
-    o += a * po[(int64_t)i * D + d];
-  }
-  part_o[grp][d] = o;
-  if (d == 0) part_l[grp] = lsum;
-  __syncthreads();
-  if (grp == 0) {
-    float ot = 0.f, lt = 0.f;
 #pragma unroll
-    for (int g = 0; g < SPLIT; ++g) {
-      ot += part_o[g][d];
-      lt += part_l[g];
-    }
-    store_out(p.out, sh * D + d, lt > 0.f ? ot / lt : 0.f, p.out_dtype);
+    for (int c = 0; c < CPL; ++c) o[c] += a * po[(int64_t)i * D + c];
   }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) store_out(p.out, sh * D + lane * CPL + c, o[c] * inv, p.out_dtype);
 }
 
 // ------------------------------------------------------------------- dispatch
@@ -650,11 +652,13 @@ hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0 || a.partition_size <= 0) return hipSuccess;
   const DecodeParams p = make_params(a);
-  dim3 rgrid((unsigned)(a.num_seqs * a.num_heads));
+  const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
+  constexpr int per_block = kReduceThreads / kWave;
+  dim3 rgrid((unsigned)((pairs + per_block - 1) / per_block));
   if (a.geom.head_size == 64)
-    hipLaunchKernelGGL(decode_reduce_kernel<64>, rgrid, dim3(kReduceThreads), 0, stream, p);
+    hipLaunchKernelGGL(decode_reduce_kernel<64>, rgrid, dim3(kReduceThreads), 0, stream, p, pairs);
   else if (a.geom.head_size == 128)
-    hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(kReduceThreads), 0, stream, p);
+    hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(kReduceThreads), 0, stream, p, pairs);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

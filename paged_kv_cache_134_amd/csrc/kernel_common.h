@@ -24,6 +24,16 @@ __device__ __forceinline__ uint4 load_nt(const void* ptr) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Plain 16-byte load / LDS store through a vector type (a HIP_vector_type
+// copy lowers to memcpy and can pin whole arrays in scratch).
+__device__ __forceinline__ uint4 load16(const void* ptr) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ptr);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store16(void* ptr, const uint4& v) {
+  *reinterpret_cast<u32x4_t*>(ptr) = u32x4_t{v.x, v.y, v.z, v.w};
+}
+
 // Elements per 16-byte chunk.
 template <pa_dtype DT>
 struct Fmt {

@@ -239,7 +239,8 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode");
 }
 
-extern "C" pa_status pa_decode_partitions(const void* query, const void* key_cache,
+extern "C" pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const void* query,
+                                          const void* key_cache,
                                           const void* value_cache, pa_dtype kv_dtype,
                                           pa_layout layout, const int32_t* block_tables,
                                           int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -251,11 +252,11 @@ extern "C" pa_status pa_decode_partitions(const void* query, const void* key_cac
   if (partition_size <= 0)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_partitions: partition_size must be > 0");
   pa::DecodeArgs a;
-  pa_status st = decode_prepare("pa_decode_partitions", nullptr, PA_F32, query, key_cache,
+  pa_status st = decode_prepare("pa_decode_partitions", out, out_dtype, query, key_cache,
                                 value_cache, kv_dtype, layout, block_tables, max_blocks_per_seq,
                                 context_lens, max_context_len, num_seqs, num_heads, num_kv_heads,
                                 head_size, block_size, num_blocks, scale, partition_size, workspace,
-                                workspace_bytes_, false, true, &a);
+                                workspace_bytes_, true, true, &a);
   if (st != PA_OK || num_seqs == 0 || a.partition_size == 0) return st;
   hipError_t e = pa::launch_decode_main(a, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode_partitions");

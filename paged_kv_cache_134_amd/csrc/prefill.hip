@@ -11,10 +11,15 @@
 //
 // Kernel design (this file's own, for CDNA4 MFMA and wave64):
 //   * a workgroup of 4 waves owns BM = 64 * QB query rows of one (sequence,
-//     head); wave w owns 16 * QB rows, QB blocks of 16;
-//   * key tiles of 64 keys are gathered through the block table into LDS:
-//     K row-major (bf16/f16 as stored) and V transposed to [d][key] in f16;
-//     keys past the tile's last visible position are zero-filled, never loaded;
+//     head); wave w owns 16 * QB rows, QB blocks of 16, so every K and V
+//     fragment read from LDS feeds QB matrix instructions;
+//   * key tiles of 64 keys are gathered through the block table into
+//     registers one tile ahead of use, then into LDS: K row-major (bf16/f16
+//     as stored) and V transposed to [d][key] in f16; keys past the last
+//     visible position are read as the last visible key (finite data) and
+//     masked, so no unwritten slot is ever read;
+//   * workgroup ids are remapped so the query tiles of one (sequence, head)
+//     run on one XCD and share its L2;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16} (A = 16 keys x 32 d
 //     from LDS, B = 32 d x 16 queries held in registers), so each lane holds
 //     scores of ONE query (lane % 16) for 4 keys of every 16-key block;
@@ -24,10 +29,10 @@
 //     consistently in A and B), so the online-softmax statistics and the
 //     output rescaling stay in-lane; the 4 lanes that share a query combine
 //     their maxima with two cross-lane exchanges;
-//   * probabilities are rounded to f16 before the PV product and the
-//     normaliser sums the rounded values, so the output is a weighted mean of
-//     V with weights perturbed by at most 2^-11 relative (values must lie in
-//     f16 range); QK^T uses the stored type with fp32 accumulation.
+//   * probabilities are rounded to f16 before the PV product (relative error
+//     at most 2^-11 per weight; V is converted exactly from bf16 and must lie
+//     in f16 range); the normaliser sums the unrounded fp32 values; QK^T uses
+//     the stored type with fp32 accumulation.
 #include <hip/hip_runtime.h>
 
 #include "kernel_common.h"
@@ -63,6 +68,8 @@ struct PrefillParams {
   int32_t log2_bs;
   float scale_log2e;
   pa_dtype out_dtype;
+  int32_t q_tiles;   // query tiles per sequence (of the longest)
+  int32_t num_work;  // q_tiles * num_heads * num_seqs
 };
 
 template <pa_dtype DT>
@@ -81,26 +88,42 @@ __device__ __forceinline__ f32x4_t mfma_pv(const f16x8_t& a, const f16x8_t& b, f
 
 // D = head size, QB = 16-query blocks per wave.
 template <pa_dtype DT, int D, int QB>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(kPrefillThreads, 3) void prefill_kernel(const PrefillParams p) {
   constexpr int BM = kPrefillWaves * 16 * QB;   // query rows per workgroup
   constexpr int KS = D / 32;                    // 32-wide k-steps over the head dim
   constexpr int DB = D / 16;                    // 16-wide output blocks
   constexpr int KROW = D * 2 + 16;              // LDS bytes per K row (padded)
   constexpr int VROW = kBN * 2 + 8;             // LDS bytes per V^T row (padded)
+  constexpr int KCH = D / 8;                    // 16-byte chunks per K/V row
+  constexpr int KPT = kBN * KCH / kPrefillThreads;        // K chunks per thread per tile
+  constexpr int VITEMS = (kBN / 4) * KCH;      // V items of 4 keys x 8 columns per tile
+  constexpr int VPT = (VITEMS + kPrefillThreads - 1) / kPrefillThreads;
+  static_assert(KPT * kPrefillThreads == kBN * KCH, "K tile must split evenly");
   __shared__ __attribute__((aligned(16))) char sK[kBN * KROW];
   __shared__ __attribute__((aligned(16))) char sV[D * VROW];
 
-  const int qt = blockIdx.x;
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
+  // XCD-aware order: consecutive workgroup ids are spread over the 8 XCDs
+  // (each with its own L2), so the ids are remapped to give every XCD a
+  // contiguous run of work items, i.e. the query tiles of one (sequence,
+  // head), which read the same K/V tiles, share an L2.
+  const int nwork = p.num_work;
+  const int per_xcd = (nwork + 7) / 8;
+  const int b = blockIdx.x;
+  const int work = (b % 8) * per_xcd + b / 8;
+  if (work >= nwork) return;
+  const int qt = work % p.q_tiles;
+  const int h = (work / p.q_tiles) % p.num_heads;
+  const int s = work / (p.q_tiles * p.num_heads);
+
   const int q_begin = p.query_start_loc[s];
   const int n = p.query_start_loc[s + 1] - q_begin;
   const int q0 = qt * BM;
   if (q0 >= n) return;
   const int L = p.context_lens[s];
   const int kvh = h / (p.num_heads / p.num_kv_heads);
-  const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
   const int lq = lane % 16;     // query (column) owned by this lane within a block
   const int lg = lane / 16;     // lane group: 4 keys / 8 k-elements slice
 
@@ -117,10 +140,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillP
     const int j = q0 + wave * 16 * QB + qb * 16 + lq;
     lim[qb] = L - n + j;
     const bool ok = j < n;
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        p.query + (((int64_t)(q_begin + (ok ? j : 0)) * p.num_heads + h) * D) * Fmt<DT>::kBytes);
+    const char* qp =
+        p.query + (((int64_t)(q_begin + (ok ? j : 0)) * p.num_heads + h) * D) * Fmt<DT>::kBytes;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = ok ? qp[ks * 4 + lg] : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks)
+      qf[qb][ks] = ok ? load16(qp + (ks * 4 + lg) * 16) : make_uint4(0, 0, 0, 0);
   }
 
   f32x4_t o[QB][DB];
@@ -134,63 +158,90 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillP
   }
 
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-  const int bs_mask = (1 << p.log2_bs) - 1;
+  const int lbs = p.log2_bs;
+  const int bs_mask = (1 << lbs) - 1;
   const int64_t head_off = (int64_t)kvh * p.head_stride;
 
-  for (int k0 = 0; k0 < kend; k0 += kBN) {
-    // ---- stage K (row-major) and V^T (f16) of keys k0 .. k0+63 into LDS
-    constexpr int KCH = D / 8;  // 16-byte chunks per row
-    for (int c = threadIdx.x; c < kBN * KCH; c += kPrefillThreads) {
-      const int key = c / KCH, ch = c % KCH;
-      const int t = k0 + key;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < kend) {
-        const int64_t off = (int64_t)bt[t >> p.log2_bs] * p.blk_stride +
-                            (int64_t)(t & bs_mask) * p.tok_stride + head_off + ch * 8;
-        v = *reinterpret_cast<const uint4*>(p.key_cache + off * 2);
-      }
-      *reinterpret_cast<uint4*>(sK + key * KROW + ch * 16) = v;
-    }
-    for (int c = threadIdx.x; c < (kBN / 4) * KCH; c += kPrefillThreads) {
-      const int kq = c % (kBN / 4), dq = c / (kBN / 4);
-      uint4 r[4];
+  // Global -> registers for one key tile.  Keys past kend are clamped to the
+  // last visible key (finite data the tile reads anyway); the causal mask
+  // gives them probability 0, so every load is unconditional.  A thread
+  // loads KPT consecutive 16-byte chunks of one K row and, for V, 4
+  // consecutive keys of one 8-column slice: one block-table lookup each
+  // (blocks of >= 4 tokens hold an aligned group of 4 keys).
+  constexpr int KTPR = kPrefillThreads / kBN;  // threads per K row
+  static_assert(KTPR * KPT == KCH, "K row split");
+  const int k_row = tid / KTPR, k_cg = (tid % KTPR) * KPT;
+  const int v_item = min(tid, VITEMS - 1);
+  const int v_kq = v_item % (kBN / 4), v_dq = v_item / (kBN / 4);
+  const bool bs_ge4 = lbs >= 2;
+  struct TileRegs {
+    uint4 k[KPT];
+    uint4 v[4];
+  };
+  auto fetch = [&](int k0) {
+    TileRegs r;
+    {
+      const int t = min(k0 + k_row, kend - 1);
+      const char* src = p.key_cache + ((int64_t)bt[t >> lbs] * p.blk_stride +
+                                       (int64_t)(t & bs_mask) * p.tok_stride + head_off + k_cg * 8) * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = k0 + kq * 4 + i;
-        r[i] = make_uint4(0, 0, 0, 0);
-        if (t < kend) {
-          const int64_t off = (int64_t)bt[t >> p.log2_bs] * p.blk_stride +
-                              (int64_t)(t & bs_mask) * p.tok_stride + head_off + dq * 8;
-          r[i] = *reinterpret_cast<const uint4*>(p.value_cache + off * 2);
-        }
+      for (int i = 0; i < KPT; ++i) r.k[i] = load16(src + i * 16);
+    }
+    {
+      const int tb = min(k0 + v_kq * 4, kend - 1);
+      const int64_t blk0 = (int64_t)bt[tb >> lbs] * p.blk_stride;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = min(k0 + v_kq * 4 + j, kend - 1);
+        const int64_t blk = bs_ge4 ? blk0 : (int64_t)bt[t >> lbs] * p.blk_stride;
+        r.v[j] = load16(p.value_cache +
+                        (blk + (int64_t)(t & bs_mask) * p.tok_stride + head_off + v_dq * 8) * 2);
       }
+    }
+    return r;
+  };
+  // smallest visible-key limit among this wave's query rows
+  const int lim_min = L - n + q0 + wave * 16 * QB;
+
+  TileRegs tr = fetch(0);
+  for (int k0 = 0; k0 < kend; k0 += kBN) {
+    // ---- registers -> LDS: K row-major, V transposed to [d][key] in f16
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) store16(sK + k_row * KROW + (k_cg + i) * 16, tr.k[i]);
+    if (VITEMS % kPrefillThreads == 0 || tid < VITEMS) {  // head size 64: half the threads stage no V
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         f16x4_t col;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) col[i] = (_Float16)chunk_elem<DT>(r[i], e);
-        *reinterpret_cast<f16x4_t*>(sV + (dq * 8 + e) * VROW + kq * 8) = col;
+        for (int j = 0; j < 4; ++j) col[j] = (_Float16)chunk_elem<DT>(tr.v[j], e);
+        *reinterpret_cast<f16x4_t*>(sV + (v_dq * 8 + e) * VROW + v_kq * 8) = col;
       }
     }
     __syncthreads();
+    tr = fetch(k0 + kBN);  // next tile in flight (clamped past the end: never a wait on a branch)
 
     // ---- S^T = K Q^T for 4 key blocks of 16
-    f32x4_t sc[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sc[qb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float sc[QB][4][4];  // [query block][key block][key within lane group]
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+      f32x4_t acc[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(sK + (kb * 16 + lq) * KROW + ks * 64 + lg * 16);
+        const uint4 a = load16(sK + (kb * 16 + lq) * KROW + ks * 64 + lg * 16);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = mfma_qk<DT>(a, qf[qb][ks], sc[qb][kb]);
+        for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma_qk<DT>(a, qf[qb][ks], acc[qb]);
       }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[qb][kb][i] = acc[qb][i];
     }
 
-    // ---- online softmax, in-lane per query; 4 lanes share a query
+    // ---- online softmax, in-lane per query; 4 lanes share a query.  Only
+    // tiles that reach past some row's last visible key need the mask.
+    const bool need_mask = k0 + kBN - 1 > lim_min;  // wave-uniform
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mt = -INFINITY;
@@ -199,7 +250,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillP
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + kb * 16 + lg * 4 + i;
-          const float zz = key <= lim[qb] ? sc[qb][kb][i] * p.scale_log2e : -INFINITY;
+          float zz = sc[qb][kb][i] * p.scale_log2e;
+          if (need_mask && key > lim[qb]) zz = -INFINITY;
           sc[qb][kb][i] = zz;
           mt = fmaxf(mt, zz);
         }
@@ -223,12 +275,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillP
       for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float z0 = sc[qb][2 * ks][i], z1 = sc[qb][2 * ks + 1][i];
-          const _Float16 p0 = (_Float16)(z0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z0 - m[qb]));
-          const _Float16 p1 = (_Float16)(z1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z1 - m[qb]));
-          pb[qb][i] = p0;
-          pb[qb][4 + i] = p1;
-          l[qb] += (float)p0 + (float)p1;
+          // every query sees key 0, so m is finite here and exp2(-inf) = 0
+          const float e0 = __builtin_amdgcn_exp2f(sc[qb][2 * ks][i] - m[qb]);
+          const float e1 = __builtin_amdgcn_exp2f(sc[qb][2 * ks + 1][i] - m[qb]);
+          pb[qb][i] = (_Float16)e0;
+          pb[qb][4 + i] = (_Float16)e1;
+          l[qb] += e0 + e1;
         }
       }
 #pragma unroll
@@ -262,10 +314,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillP
 }
 
 template <pa_dtype DT, int D>
-hipError_t launch_pd(const PrefillParams& p, int num_seqs, int max_q, hipStream_t st) {
+hipError_t launch_pd(PrefillParams p, int num_seqs, int max_q, hipStream_t st) {
   constexpr int QB = 1;
   constexpr int BM = kPrefillWaves * 16 * QB;
-  dim3 grid((max_q + BM - 1) / BM, p.num_heads, num_seqs), block(kPrefillThreads);
+  p.q_tiles = (max_q + BM - 1) / BM;
+  const int64_t nwork = (int64_t)p.q_tiles * p.num_heads * num_seqs;
+  if (nwork > 0x7FFFFFFF - 8) return hipErrorInvalidValue;
+  p.num_work = (int)nwork;
+  dim3 grid((unsigned)(((nwork + 7) / 8) * 8)), block(kPrefillThreads);
   hipLaunchKernelGGL((prefill_kernel<DT, D, QB>), grid, block, 0, st, p);
   return hipGetLastError();
 }

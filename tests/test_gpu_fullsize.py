@@ -66,7 +66,7 @@ def test_decode_full_size_sampled(cfg):
     ws = torch.empty(P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, ps),
                      dtype=torch.uint8, device="cuda")
     out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
-    P.pa_decode_partitions(dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+    P.pa_decode_partitions(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
                            dw.context_lens, dw.max_context_len, w.scale, ps, ws)
     P.pa_decode_reduce(out, dw.context_lens, dw.max_context_len, w.Hkv, ps, ws)
     torch.cuda.synchronize()
