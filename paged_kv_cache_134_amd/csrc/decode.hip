@@ -28,8 +28,10 @@
 // K and V rows (coalesced 16-byte loads, prefetched one chunk ahead in
 // registers) into LDS.  QK: lane = token, each wave owns G/4 query heads
 // whose query vectors are read as scalar (SGPR) operands of v_dot2, and K
-// rows are read from a swizzled LDS layout (16 lanes hit 16 distinct bank
-// groups); no cross-lane reduction and one exp per (token, head).  PV: lane
+// rows sit in LDS with a padded row stride (consecutive rows start in
+// consecutive 16-byte bank groups, so a lane-per-row read is conflict-free
+// with a constant offset); no cross-lane reduction and one exp per (token,
+// head).  PV: lane
 // owns D/32 output columns of all G heads and each wave a quarter of the
 // chunk's tokens; probabilities are broadcast from LDS.
 #include <hip/hip_runtime.h>
@@ -314,12 +316,13 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
   constexpr int HPW = G / kDecodeWaves;            // query heads per wave in QK
   constexpr int DPL = D / 32;                      // output columns per lane in PV
   static_assert(PPT * kDecodeThreads == PIECES, "chunk must split evenly");
-  __shared__ uint4 sKV[2 * PIECES];                // K (swizzled) then V; reused at the end
+  constexpr int KSTR = RC + 1;                     // K row stride in pieces (padded)
+  __shared__ uint4 sKV[kChunk * KSTR + PIECES];    // K (padded rows) then V; reused at the end
   __shared__ float sP[kChunk][G];                  // probabilities of the chunk
   __shared__ float sAlpha[G];                      // per-head rescale of this chunk
   __shared__ float sM[G], sL[G];
   uint4* sK = sKV;
-  uint4* sV = sKV + PIECES;
+  uint4* sV = sKV + kChunk * KSTR;
 
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int s = blockIdx.x / p.num_kv_heads;
@@ -345,10 +348,12 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
   const const_u32_ptr qc = (const_u32_ptr)((const char*)p.query +
       (((int64_t)s * p.num_heads + (int64_t)kvh * G + wave * HPW) * D) * 2);
 
-  // Rows at or past the end are clamped to the last row (a valid, finite
-  // row the chunk loads anyway) and masked where they are used, so every load
-  // is unconditional and all block-table reads of a fetch go out before the
-  // K/V reads: nothing serialises the 2 * PPT row loads.
+  // Consecutive lanes load consecutive 16-byte chunks of a row, so every
+  // load instruction covers whole cache lines (the loads are non-temporal and
+  // a partly used line would be fetched again).  Rows at or past the end are
+  // clamped to the last row (a valid, finite row the chunk loads anyway) and
+  // masked where they are used, so every load is unconditional and all
+  // block-table reads of a fetch go out before the K/V reads.
   auto fetch = [&](int c0, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
     int32_t blk[PPT];
     int tc[PPT];
@@ -389,8 +394,7 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {
       const int piece = tid + kDecodeThreads * r;
-      const int row = piece / RC, col = piece % RC;
-      sK[row * RC + (col ^ (row % RC))] = kr[r];
+      sK[(piece / RC) * KSTR + piece % RC] = kr[r];
       sV[piece] = vr[r];
     }
     __syncthreads();
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
       for (int pc = 0; pc < RC; pc += 4) {
         uint4 kk[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kk[j] = sK[row * RC + ((pc + j) ^ (row % RC))];
+        for (int j = 0; j < 4; ++j) kk[j] = sK[row * KSTR + pc + j];  // padded rows: conflict-free
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
           const const_u32_ptr qh = qc + hh * (D / 2) + pc * 4;
@@ -455,11 +459,11 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
 #pragma unroll
           for (int e = 0; e < DPL; ++e) acc[h][e] *= al[h];
       }
-      const int rows = min(kChunk, t1 - c0);
-#pragma unroll 2
+      // rows past the end carry p = 0 and finite (clamped) V, so the trip
+      // count is fixed and the LDS reads of later rows can be issued early
+#pragma unroll
       for (int i = 0; i < kChunk / kDecodeWaves / 2; ++i) {
         const int row = wave * (kChunk / kDecodeWaves) + 2 * i + half;
-        if (wave * (kChunk / kDecodeWaves) + 2 * i >= rows) break;  // wave-uniform
         float vf[DPL];
         const char* vrow = reinterpret_cast<const char*>(sV + row * RC) + dl * DPL * 2;
         uint4 vw = make_uint4(0, 0, 0, 0);
