@@ -68,6 +68,7 @@ struct DecodeParams {
   int32_t max_partitions;
   float scale_log2e;
   pa_dtype out_dtype;
+  bool off32;  // every byte offset into either cache fits in 32 bits
 };
 
 // Maximum over the 64 lanes of a wave (every lane receives it).
@@ -300,12 +301,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
 }
 
 // ----------------------------------------------------------------- LDS kernel
-constexpr int kChunk = 64;  // tokens per LDS chunk (one per lane in QK)
+constexpr int kChunk = 64;   // tokens per LDS chunk (one per lane in QK)
+constexpr int kBtWin = 256;  // block-table entries staged in LDS at a time
 
-// 4 waves per SIMD (<= 128 VGPRs): with ~33 KB of LDS per workgroup that is
+// 4 waves per SIMD (<= 128 VGPRs): with ~34 KB of LDS per workgroup that is
 // 4 workgroups, i.e. 128 KB of prefetched K/V in flight, per CU.  (G = 16 at
-// head size 128 needs more accumulators and settles for 2.)
-template <pa_dtype DT, int D, int G>
+// head size 128 needs more accumulators and settles for 2.)  OFF32: both
+// caches span less than 4 GiB, so row addresses are 32-bit byte offsets from
+// the cache base.
+template <pa_dtype DT, int D, int G, bool OFF32>
 __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void decode_lds_kernel(
     const DecodeParams p) {
   static_assert(DT != PA_F32, "LDS kernel takes 16-bit elements");
@@ -313,6 +317,7 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
   constexpr int RC = D / 8;                        // 16-byte pieces per row
   constexpr int PIECES = kChunk * RC;              // pieces per chunk of K (or V)
   constexpr int PPT = PIECES / kDecodeThreads;     // pieces per thread per tensor
+  constexpr int RSTEP = kDecodeThreads / RC;       // rows between a thread's pieces
   constexpr int HPW = G / kDecodeWaves;            // query heads per wave in QK
   constexpr int DPL = D / 32;                      // output columns per lane in PV
   static_assert(PPT * kDecodeThreads == PIECES, "chunk must split evenly");
@@ -320,7 +325,9 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
   __shared__ uint4 sKV[kChunk * KSTR + PIECES];    // K (padded rows) then V; reused at the end
   __shared__ float sP[kChunk][G];                  // probabilities of the chunk
   __shared__ float sAlpha[G];                      // per-head rescale of this chunk
+  __shared__ int32_t sResc[kDecodeWaves];          // wave w moved a running max this chunk
   __shared__ float sM[G], sL[G];
+  __shared__ int32_t s_bt[kBtWin];                 // block-table window
   uint4* sK = sKV;
   uint4* sV = sKV + kChunk * KSTR;
 
@@ -342,7 +349,15 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
   const int lbs = p.log2_bs;
   const int bs_mask = (1 << lbs) - 1;
-  const int64_t head_off = (int64_t)kvh * p.head_stride;
+  const int e_last = (t1 - 1) >> lbs;  // last block-table entry this workgroup reads
+
+  // The window holds entries wb0 .. wb0 + kBtWin - 1 (clamped to e_last, so
+  // every staged id is one the sequence owns).
+  int wb0 = t0 >> lbs;
+  auto stage_bt = [&]() {
+    for (int i = tid; i < kBtWin; i += kDecodeThreads) s_bt[i] = bt[min(wb0 + i, e_last)];
+  };
+  stage_bt();
 
   // query vectors of this wave's heads as scalar operands (bf16/f16 pairs)
   const const_u32_ptr qc = (const_u32_ptr)((const char*)p.query +
@@ -352,23 +367,34 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
   // load instruction covers whole cache lines (the loads are non-temporal and
   // a partly used line would be fetched again).  Rows at or past the end are
   // clamped to the last row (a valid, finite row the chunk loads anyway) and
-  // masked where they are used, so every load is unconditional and all
-  // block-table reads of a fetch go out before the K/V reads.
+  // masked where they are used, so every load is unconditional.  Block ids
+  // come from the LDS window, so no load waits on another global load.
+  const int prow = tid / RC;
+  const int pcol = tid % RC;
+  const int64_t lane_off = (int64_t)kvh * p.head_stride + pcol * 8;  // elements
+  const uint32_t blk_b = (uint32_t)(p.blk_stride * 2);
+  const uint32_t tok_b = (uint32_t)(p.tok_stride * 2);
+  const uint32_t lane_b = (uint32_t)(lane_off * 2);
   auto fetch = [&](int c0, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
     int32_t blk[PPT];
     int tc[PPT];
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {
-      tc[r] = min(c0 + (tid + kDecodeThreads * r) / RC, t1 - 1);
-      blk[r] = bt[tc[r] >> lbs];
+      tc[r] = min(c0 + prow + RSTEP * r, t1 - 1);
+      blk[r] = s_bt[(tc[r] >> lbs) - wb0];
     }
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {
-      const int col = (tid + kDecodeThreads * r) % RC;
-      const int64_t off = (int64_t)blk[r] * p.blk_stride +
-                          (int64_t)(tc[r] & bs_mask) * p.tok_stride + head_off + col * 8;
-      kr[r] = load_nt(p.key_cache + off * 2);
-      vr[r] = load_nt(p.value_cache + off * 2);
+      if constexpr (OFF32) {
+        const uint32_t off = (uint32_t)blk[r] * blk_b + (uint32_t)(tc[r] & bs_mask) * tok_b + lane_b;
+        kr[r] = load_nt(p.key_cache + off);
+        vr[r] = load_nt(p.value_cache + off);
+      } else {
+        const int64_t off = (int64_t)blk[r] * p.blk_stride +
+                            (int64_t)(tc[r] & bs_mask) * p.tok_stride + lane_off;
+        kr[r] = load_nt(p.key_cache + off * 2);
+        vr[r] = load_nt(p.value_cache + off * 2);
+      }
     }
   };
 
@@ -387,18 +413,25 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
   const int half = lane / 32;  // PV: token parity within a pair
   const int dl = lane % 32;    // PV: output columns dl*DPL .. +DPL-1
 
+  __syncthreads();  // window staged
   uint4 kr[PPT], vr[PPT];
   fetch(t0, kr, vr);
   for (int c0 = t0; c0 < t1; c0 += kChunk) {
-    __syncthreads();  // previous chunk fully consumed
+    __syncthreads();  // previous chunk fully consumed (also every read of the window)
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {
       const int piece = tid + kDecodeThreads * r;
       sK[(piece / RC) * KSTR + piece % RC] = kr[r];
       sV[piece] = vr[r];
     }
+    const int cn = c0 + kChunk;
+    const bool more = cn < t1;
+    if (more && (min(cn + kChunk - 1, t1 - 1) >> lbs) - wb0 >= kBtWin) {  // uniform
+      wb0 = cn >> lbs;
+      stage_bt();
+    }
     __syncthreads();
-    if (c0 + kChunk < t1) fetch(c0 + kChunk, kr, vr);  // next chunk in flight
+    if (more) fetch(cn, kr, vr);  // next chunk in flight
 
     // ---- QK: lane = token row, this wave's HPW heads
     {
@@ -424,40 +457,50 @@ __global__ __launch_bounds__(kDecodeThreads, (G >= 16 && D >= 128) ? 2 : 4) void
           z[hh] = a;
         }
       }
-      // ---- online softmax of this wave's heads
+      // ---- online softmax of this wave's heads.  The running max moves only
+      // when some token of the chunk exceeds it by more than the headroom, so
+      // the wave-wide maximum is taken only then (a ballot decides).
+      bool resc = false;
+      float alpha[HPW];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
         const int h = wave * HPW + hh;
         const float zz = valid ? z[hh] * p.scale_log2e : -INFINITY;
-        const float mc = wave_max(zz);
-        float alpha = 1.f;
-        if (mc > m_ref[hh] + kLazyRescale) {
-          const float mn = fmaxf(m_ref[hh], mc);
-          alpha = exp2_diff(m_ref[hh], mn);
+        alpha[hh] = 1.f;
+        if (__any(zz > m_ref[hh] + kLazyRescale)) {
+          const float mn = fmaxf(m_ref[hh], wave_max(zz));
+          alpha[hh] = exp2_diff(m_ref[hh], mn);
           m_ref[hh] = mn;
-          l_lane[hh] *= alpha;
+          l_lane[hh] *= alpha[hh];
+          resc = true;
         }
         const float pw = valid ? __builtin_amdgcn_exp2f(zz - m_ref[hh]) : 0.f;
         l_lane[hh] += pw;
         sP[row][h] = pw;
-        if (lane == 0) sAlpha[h] = alpha;
+      }
+      if (lane == 0) {
+        sResc[wave] = resc;
+        if (resc) {
+#pragma unroll
+          for (int hh = 0; hh < HPW; ++hh) sAlpha[wave * HPW + hh] = alpha[hh];
+        }
       }
     }
     __syncthreads();
 
     // ---- PV: wave owns rows 16*wave .. +15, half-waves take alternate rows
     {
-      float al[G];
+      // heads of QK wave w are rescaled only when that wave moved a max
 #pragma unroll
-      for (int h = 0; h < G; ++h) al[h] = sAlpha[h];
-      bool resc = false;
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        if (__builtin_amdgcn_readfirstlane(sResc[w])) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) resc |= al[h] != 1.f;
-      if (resc) {
+          for (int hh = 0; hh < HPW; ++hh) {
+            const float a = sAlpha[w * HPW + hh];
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[h][e] *= al[h];
+            for (int e = 0; e < DPL; ++e) acc[w * HPW + hh][e] *= a;
+          }
+        }
       }
       // rows past the end carry p = 0 and finite (clamped) V, so the trip
       // count is fixed and the LDS reads of later rows can be issued early
@@ -577,15 +620,25 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
 }
 
 // ------------------------------------------------------------------- dispatch
+template <pa_dtype DT, int D, bool OFF32>
+hipError_t launch_lds(const DecodeParams& p, int G, dim3 grid, hipStream_t st) {
+  dim3 block(kDecodeThreads);
+  switch (G) {
+    case 4: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 4, OFF32>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 8, OFF32>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 16, OFF32>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <pa_dtype DT, int D>
 hipError_t launch_g(const DecodeParams& p, int G, dim3 grid, hipStream_t st) {
   dim3 block(kDecodeThreads);
   if constexpr (DT != PA_F32) {
-    switch (G) {
-      case 4: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 4>), grid, block, 0, st, p); return hipGetLastError();
-      case 8: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 8>), grid, block, 0, st, p); return hipGetLastError();
-      case 16: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 16>), grid, block, 0, st, p); return hipGetLastError();
-      default: break;
+    if (G == 4 || G == 8 || G == 16) {
+      if (p.off32) return launch_lds<DT, D, true>(p, G, grid, st);
+      return launch_lds<DT, D, false>(p, G, grid, st);
     }
   }
   switch (G) {
@@ -634,6 +687,8 @@ DecodeParams make_params(const DecodeArgs& a) {
   p.max_partitions = a.max_partitions;
   p.scale_log2e = a.scale * kLog2e;
   p.out_dtype = a.out_dtype;
+  const int64_t elem = a.kv_dtype == PA_F32 ? 4 : 2;
+  p.off32 = (int64_t)g.num_blocks * p.blk_stride * elem <= (int64_t)UINT32_MAX;
   return p;
 }
 

@@ -188,3 +188,41 @@ def test_prefill_small(name, cfg, over, layout):
     err, where = max_abs(got, ref)
     assert np.all(np.isfinite(got))
     assert err <= TOL[w.dtype], f"{name} err={err} at {where}"
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_decode_pool_beyond_4gib(G):
+    """A pool of more than 4 GiB per cache whose allocator hands out the
+    blocks above the 4 GiB mark first: rows are addressed with 64-bit offsets
+    (the narrow-offset path is taken only for smaller pools)."""
+    need_gpu()
+    Hkv, bs, D = 2, 32, 128
+    blk_bytes = bs * Hkv * D * 2
+    mark = (1 << 32) // blk_bytes
+    w = workloads.make(3, S=4, H=Hkv * G, Hkv=Hkv, len_median=300, len_cap=1200,
+                       pool_blocks=mark + 2048)
+    rng = np.random.default_rng(77)
+    w.free_order = np.concatenate([rng.permutation(np.arange(mark, w.NB)),
+                                   rng.permutation(np.arange(0, mark))]).astype(np.int32)
+    announce("pool > 4 GiB", "G", G, "NB", w.NB)
+    dw = M.setup(w, write_step=True)
+    st = build_state(w)
+    assert np.array_equal(dw.block_tables_host, st.block_tables)
+    used = np.concatenate([st.block_tables[s, :(int(w.context_lens[s]) + bs - 1) // bs]
+                           for s in range(w.S)])
+    assert used.min() >= mark  # every row sits beyond 4 GiB
+    qf = A.bits_to_f64(w.query, w.dtype)
+    for part in (0, -1):
+        got = _decode(dw, part)
+        worst = 0.0
+        for s in range(w.S):
+            K, V = w.kv(s)
+            for h in range(w.H):
+                g = h // w.G
+                ref, _ = A.attention_dense(qf[s, h], A.bits_to_f64(K[:, g], w.dtype),
+                                           A.bits_to_f64(V[:, g], w.dtype), w.scale)
+                worst = max(worst, float(np.max(np.abs(got[s, h] - ref))))
+        announce("partition", part, "max-abs", worst)
+        assert worst <= TOL[w.dtype]
+    del dw
+    torch.cuda.empty_cache()
