@@ -111,7 +111,8 @@ def main():
 
     if w.kind == "decode":
         ps = args.partition if args.partition >= 0 else P.pa_decode_auto_partition(
-            S, Hkv, dw.max_context_len)
+            S, H, Hkv, P.KV_DTYPE[w.dtype],
+            dw.max_context_len, int(lens.sum()))
         ws = None
         if ps > 0:
             ws = torch.empty(P.pa_decode_workspace_size(S, H, D, dw.max_context_len, ps),

@@ -135,9 +135,19 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
                                 int32_t head_size, int32_t max_context_len,
                                 int32_t partition_size);
 
-/* Partition size that partition_size = -1 resolves to for this shape. */
-int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
-                                 int32_t max_context_len);
+/*
+ * Partition size for this decode shape (0 = single pass): 512 for the
+ * per-head kernel (group size 1 or 2, or fp32), a larger power of two for
+ * the grouped kernel while about two workgroups per resident slot remain.
+ * total_context_len is the sum of context_lens when the caller knows it
+ * (<= 0: unknown, num_seqs * max_context_len is assumed); partition_size -1
+ * in the decode calls resolves with it unknown.  Never below 512, so a
+ * workspace sized for partition_size -1 fits every value it returns.
+ */
+int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, pa_dtype kv_dtype,
+                                 int32_t max_context_len,
+                                 int64_t total_context_len);
 
 pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
                     const void* key_cache, const void* value_cache,

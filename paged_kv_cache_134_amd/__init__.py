@@ -38,6 +38,7 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARGUMENT", 2: "PA_ERR_UNSUPPORTED
                 3: "PA_ERR_WORKSPACE_TOO_SMALL", 4: "PA_ERR_OUT_OF_BLOCKS", 5: "PA_ERR_HIP",
                 6: "PA_ERR_METADATA"}
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
+KV_DTYPE = {"f32": PA_F32, "bf16": PA_BF16, "f16": PA_F16}  # workload dtype names
 NHD, HND = 0, 1
 
 EXPORTED = [
@@ -60,7 +61,7 @@ _sig = {
                                     _i32, _i32, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
-    "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32]),
+    "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64]),
     "pa_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
@@ -183,8 +184,10 @@ def pa_decode_workspace_size(num_seqs: int, num_heads: int, head_size: int, max_
                                              partition_size))
 
 
-def pa_decode_auto_partition(num_seqs: int, num_kv_heads: int, max_context_len: int) -> int:
-    return int(_lib.pa_decode_auto_partition(num_seqs, num_kv_heads, max_context_len))
+def pa_decode_auto_partition(num_seqs: int, num_heads: int, num_kv_heads: int, kv_dtype: int,
+                             max_context_len: int, total_context_len: int = 0) -> int:
+    return int(_lib.pa_decode_auto_partition(num_seqs, num_heads, num_kv_heads, kv_dtype,
+                                             max_context_len, total_context_len))
 
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len: int,

@@ -15,6 +15,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 

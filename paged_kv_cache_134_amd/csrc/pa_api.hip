@@ -120,11 +120,45 @@ extern "C" pa_status pa_copy_blocks(void* key_cache, void* value_cache, const in
 }
 
 // ----------------------------------------------------------------- decode
-extern "C" int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
-                                            int32_t max_context_len) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  return max_context_len <= 512 ? 0 : 512;
+namespace {
+
+// Compute units of the current device (256 on MI355X), asked once.
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+}  // namespace
+
+// Per-head kernel: 512-token partitions as soon as a context is longer.
+// Grouped kernel (one workgroup reads a kv head for all G query heads, so a
+// workgroup has G times the work per token): the largest power-of-two
+// partition, at least 512 and shorter than the longest context, that still
+// leaves about two workgroups per resident slot (4 per compute unit) for
+// balance; a workgroup's fixed costs (block-table staging, the first load's
+// latency, the merge) are then spread over as many chunks as possible.
+extern "C" int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_heads,
+                                            int32_t num_kv_heads, pa_dtype kv_dtype,
+                                            int32_t max_context_len, int64_t total_context_len) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_heads <= 0 || max_context_len <= 512) return 0;
+  if (!pa::decode_uses_group_kernel(kv_dtype, num_heads / num_kv_heads)) return 512;
+  const int64_t total = total_context_len > 0 ? total_context_len
+                                              : (int64_t)num_seqs * max_context_len;
+  const int64_t want = 2 * 4 * (int64_t)device_cus();
+  for (int32_t ps = 8192; ps > 512; ps /= 2) {
+    if (ps >= max_context_len) continue;
+    const int64_t wgs = (int64_t)num_kv_heads * (total / ps + num_seqs / 2);
+    if (wgs >= want) return ps;
+  }
+  return 512;
 }
 
 extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
@@ -171,7 +205,8 @@ pa_status decode_prepare(const char* fn, void* out, pa_dtype out_dtype, const vo
   if (!(scale == scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale is NaN");
   if ((int64_t)num_seqs * num_kv_heads > 0x7FFFFFFF || (int64_t)num_seqs * num_heads > 0x7FFFFFFF)
     return fail(PA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
-  int32_t ps = partition_size < 0 ? pa_decode_auto_partition(num_seqs, num_kv_heads, max_context_len)
+  int32_t ps = partition_size < 0 ? pa_decode_auto_partition(num_seqs, num_heads, num_kv_heads,
+                                                              kv_dtype, max_context_len, 0)
                                   : partition_size;
   const int64_t parts = partitions_for(max_context_len, ps);
   if (ps > 0 && parts == 0) ps = 0;  // empty contexts: nothing to split

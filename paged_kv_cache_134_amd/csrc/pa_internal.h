@@ -54,6 +54,10 @@ struct DecodeArgs {
 };
 
 // Single pass (partition_size == 0) or the split-K partition kernel.
+// Whether decode takes the grouped (LDS-staged) kernel for this element type
+// and group size G = num_heads / num_kv_heads.
+bool decode_uses_group_kernel(pa_dtype kv_dtype, int G);
+
 hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream);
 // Split-K reduce over the partials in part_out / part_ml.
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);

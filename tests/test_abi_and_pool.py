@@ -96,6 +96,26 @@ def _pool_and_model(nb, bs, order):
     return P.BlockPool(nb, bs, order), BlockManagerModel(nb, bs, order)
 
 
+def test_auto_partition_policy():
+    """Host policy only (no device needed; without one 256 compute units are
+    assumed): the per-head kernel splits at 512, the grouped kernel takes the
+    largest partition that keeps about two workgroups per resident slot."""
+    ap = P.pa_decode_auto_partition
+    assert ap(64, 32, 32, P.PA_BF16, 512, 0) == 0          # short contexts: one pass
+    assert ap(64, 32, 32, P.PA_BF16, 2035, 75661) == 512   # MHA: per-head kernel
+    assert ap(4, 8, 8, P.PA_F32, 300, 448) == 0
+    assert ap(4, 64, 8, P.PA_F32, 4000, 0) == 512          # fp32 never takes the grouped kernel
+    assert ap(128, 64, 8, P.PA_BF16, 8192, 207090) == 1024  # lognormal GQA batch
+    assert ap(8, 64, 8, P.PA_BF16, 131072, 8 * 131072) == 4096
+    # unknown total: num_seqs * max_context_len is assumed
+    assert ap(8, 64, 8, P.PA_BF16, 131072, 0) == 4096
+    for args in [(1, 8, 1, P.PA_BF16, 600, 0), (3, 48, 3, P.PA_F16, 100000, 0)]:
+        ps = ap(*args)
+        assert ps >= 512 and ps % 16 == 0
+        assert P.pa_decode_workspace_size(args[0], args[1], 128, args[4], -1) >= \
+            P.pa_decode_workspace_size(args[0], args[1], 128, args[4], ps)
+
+
 def test_pool_matches_model_on_random_operations():
     rng = np.random.default_rng(17)
     nb, bs = 48, 8

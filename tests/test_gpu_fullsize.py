@@ -61,7 +61,8 @@ def test_decode_full_size_sampled(cfg):
     dw = M.setup(w, write_step=True)
     st = build_state(w)
     assert np.array_equal(dw.block_tables_host, st.block_tables)
-    ps = P.pa_decode_auto_partition(w.S, w.Hkv, dw.max_context_len)
+    ps = P.pa_decode_auto_partition(w.S, w.H, w.Hkv, P.KV_DTYPE[w.dtype], dw.max_context_len,
+                                   int(w.context_lens.sum()))
     assert ps > 0
     ws = torch.empty(P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, ps),
                      dtype=torch.uint8, device="cuda")

@@ -34,10 +34,9 @@ def _decode(dw, part, out_dtype=None):
     w = dw.w
     dt = torch.float32 if out_dtype is None else out_dtype
     out = torch.full(w.query_shape, float("nan"), dtype=dt, device="cuda")
-    ps = part if part >= 0 else P.pa_decode_auto_partition(w.S, w.Hkv, dw.max_context_len)
     ws = None
-    if ps != 0:
-        nbytes = P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, ps)
+    if part != 0:  # -1 sizes for the smallest automatic partition
+        nbytes = P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, part)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     P.pa_decode(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables, dw.context_lens,
                 dw.max_context_len, w.scale, layout=dw.layout, partition_size=part, workspace=ws)
@@ -86,16 +85,17 @@ def test_decode_bitwise_placement_invariance_and_determinism():
         assert np.array_equal(oa, _decode(da, part))
 
 
-def test_context_len_one_is_exactly_v():
+@pytest.mark.parametrize("G", [1, 8])
+def test_context_len_one_is_exactly_v(G):
     need_gpu()
-    w = workloads.make(2, S=5, H=4, Hkv=4, len_lo=1, len_hi=1, n_pad=0)
-    announce("ctx=1")
+    w = workloads.make(2, S=5, H=4 * G, Hkv=4, len_lo=1, len_hi=1, n_pad=0)
+    announce("ctx=1", "G", G)
     dw = M.setup(w, write_step=True)
     got = _decode(dw, 0)
     for s in range(w.S):
         _, v = w.kv(s, 0, 1)
-        expect = A.bits_to_f64(v[0], "bf16")
-        assert np.array_equal(got[s], expect)
+        expect = A.bits_to_f64(v[0], "bf16")  # [Hkv, D]
+        assert np.array_equal(got[s], np.repeat(expect, G, axis=0))
 
 
 def test_constant_v_gives_constant_output():
@@ -123,7 +123,8 @@ def test_gqa_equals_mha_with_repeated_kv():
                 dw.max_context_len, w.scale, partition_size=0)
     torch.cuda.synchronize()
     assert g[2] == 2
-    assert np.max(np.abs(out_m.cpu().numpy() - out_g)) <= 1e-6
+    # the grouped kernel rounds probabilities to f16, the per-head one keeps fp32
+    assert np.max(np.abs(out_m.cpu().numpy() - out_g)) <= TOL["bf16"]
 
 
 def test_bf16_output_within_one_ulp():
@@ -139,11 +140,12 @@ def test_bf16_output_within_one_ulp():
     assert np.all(np.abs(got - ref) <= ulp + 2e-3)
 
 
-def test_f16_decode():
+@pytest.mark.parametrize("G", [1, 8])
+def test_f16_decode(G):
     """f16 caches: the bf16 workload's values converted to f16 (exact in range)."""
     need_gpu()
-    w = workloads.make(2, S=3, H=4, Hkv=4, len_lo=30, len_hi=600, n_pad=1)
-    announce("f16 decode")
+    w = workloads.make(2, S=3, H=4 * G, Hkv=4, len_lo=30, len_hi=600, n_pad=1)
+    announce("f16 decode", "G", G)
     dw = M.setup(w, write_step=True)
     kc16 = dw.key_cache.to(torch.float16)
     vc16 = dw.value_cache.to(torch.float16)
@@ -226,3 +228,35 @@ def test_decode_pool_beyond_4gib(G):
         assert worst <= TOL[w.dtype]
     del dw
     torch.cuda.empty_cache()
+
+
+def test_decode_bf16_values_beyond_f16_range():
+    """Grouped decode computes PV with f16 operands; V rows holding bf16 values
+    of magnitude 2^17 must send their workgroup to the fp32 products (a later
+    chunk than the first, so the f16 pass is abandoned part-way)."""
+    need_gpu()
+    w = workloads.make(4, S=4, H=16, Hkv=2, lens=[1200, 700, 64, 1])
+    announce("wide bf16 V")
+    dw = M.setup(w, write_step=True)
+    st = build_state(w)
+    big = np.arange(300, 310)  # chunk 4 of sequence 0
+    slots = torch.from_numpy(st.seq_slots[0][big].astype(np.int64)).cuda()
+    blk, off = slots // w.bs, slots % w.bs
+    dw.value_cache[blk, off] *= 2.0 ** 17  # exact: exponent shift
+    qf = A.bits_to_f64(w.query, w.dtype)
+    for part in (0, -1):
+        got = _decode(dw, part)
+        for s in range(w.S):
+            K, V = w.kv(s)
+            Kf, Vf = A.bits_to_f64(K, w.dtype), A.bits_to_f64(V, w.dtype)
+            if s == 0:
+                Vf[big] *= 2.0 ** 17
+            for h in range(w.H):
+                g = h // w.G
+                ref, _ = A.attention_dense(qf[s, h], Kf[:, g], Vf[:, g], w.scale)
+                # the weights carry a relative rounding (f16), so the bound
+                # scales with the output; an f16 V would be off by ~100%
+                tol = TOL[w.dtype] * max(1.0, float(np.max(np.abs(ref))))
+                err = float(np.max(np.abs(got[s, h] - ref)))
+                assert err <= tol, (part, s, h, err, tol)
+        announce("partition", part, "ok")
