@@ -214,6 +214,9 @@ pa_status pa_decode_reduce(void* out, pa_dtype out_dtype,
  *   query_start_loc (device) int32 [num_seqs + 1], query_start_loc[0] = 0,
  *                   non-decreasing, query_start_loc[num_seqs] = num_tokens
  *   max_query_len   >= every n (host value)
+ * out, query and both caches must be 16-byte aligned (PA_ERR_INVALID_ARGUMENT
+ * otherwise).  Probabilities are rounded to f16 for the P.V product and the
+ * normaliser sums the rounded values; V must lie in f16 range.
  * Supported: kv_dtype PA_BF16 or PA_F16 (matrix cores), head_size 64 or 128,
  * num_heads / num_kv_heads in {1,2,4,8,16}, block_size a power of two.
  */

@@ -352,8 +352,8 @@ extern "C" pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query
   if (!out || !query || !key_cache || !value_cache || !block_tables || !query_start_loc ||
       !context_lens)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: null pointer");
-  if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: query and caches must be 16-byte aligned");
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: out, query and caches must be 16-byte aligned");
   pa::PrefillArgs a{};
   a.out = out;
   a.out_dtype = out_dtype;

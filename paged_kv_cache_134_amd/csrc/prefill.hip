@@ -10,9 +10,8 @@
 // 0 .. L - n + j.  Keys are read through the block table exactly as in decode.
 //
 // Kernel design (this file's own, for CDNA4 MFMA and wave64):
-//   * a workgroup of 4 waves owns BM = 64 * QB query rows of one (sequence,
-//     head); wave w owns 16 * QB rows, QB blocks of 16, so every K and V
-//     fragment read from LDS feeds QB matrix instructions;
+//   * a workgroup of 4 waves owns 128 query rows of one (sequence, head);
+//     wave w owns 32 rows, one 32-wide MFMA column block;
 //   * key tiles of 64 keys are gathered through the block table into
 //     registers one tile ahead of use, then into LDS: K row-major (bf16/f16
 //     as stored) and V transposed to [d][key] in f16; keys past the last
@@ -20,19 +19,24 @@
 //     masked, so no unwritten slot is ever read;
 //   * workgroup ids are remapped so the query tiles of one (sequence, head)
 //     run on one XCD and share its L2;
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16} (A = 16 keys x 32 d
-//     from LDS, B = 32 d x 16 queries held in registers), so each lane holds
-//     scores of ONE query (lane % 16) for 4 keys of every 16-key block;
-//   * the same lane-to-query map holds for O^T = V^T P^T (A = 16 d x 32 keys
-//     from the transposed V tile, B = 32 keys x 16 queries = this lane's own
-//     probabilities, converted to f16, with the key order permuted
-//     consistently in A and B), so the online-softmax statistics and the
-//     output rescaling stay in-lane; the 4 lanes that share a query combine
-//     their maxima with two cross-lane exchanges;
-//   * probabilities are rounded to f16 before the PV product (relative error
-//     at most 2^-11 per weight; V is converted exactly from bf16 and must lie
-//     in f16 range); the normaliser sums the unrounded fp32 values; QK^T uses
-//     the stored type with fp32 accumulation.
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16} (A = 32 keys x 16 d
+//     from LDS, B = 16 d x 32 queries held in registers), so each lane holds
+//     16 scores of ONE query (lane % 32) and the other half-wave the other 16
+//     keys of each 32-key block: one cross-lane exchange per row maximum;
+//   * O^T = V^T P^T with the same lane-to-query map (A = 32 d x 16 keys from
+//     the transposed V tile, B = 16 keys x 32 queries = this lane's own
+//     probabilities, with the key order permuted consistently in A and B),
+//     so the online-softmax statistics and the output rescaling stay
+//     in-lane;
+//   * scores stay unscaled until exp2(fma(z, scale*log2e, -m)); the running
+//     max moves only past a 2^8 headroom (a ballot decides); probabilities
+//     are rounded to f16 for PV (relative error at most 2^-10 per weight; V
+//     is converted exactly from bf16 and must lie in f16 range) and the
+//     normaliser sums the rounded values with v_dot2, so the weights that
+//     multiply V are exactly the ones that are divided out; QK^T uses the
+//     stored type with fp32 accumulation;
+//   * a wave whose rows are all padding, or that sees none of a tile's keys,
+//     skips that tile's products.
 #include <hip/hip_runtime.h>
 
 #include "kernel_common.h"
@@ -43,13 +47,15 @@ namespace {
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
-constexpr int kBN = 64;              // keys per tile
-constexpr float kLazyRescaleP = 8.f; // log2 headroom of the running max
+constexpr int kQW = 32;                         // query rows per wave
+constexpr int kBM = kPrefillWaves * kQW;        // query rows per workgroup
+constexpr int kBN = 64;                         // keys per tile
+constexpr float kLazyRescaleP = 8.f;            // log2 headroom of the running max
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 struct PrefillParams {
   void* out;
@@ -72,33 +78,36 @@ struct PrefillParams {
   int32_t num_work;  // q_tiles * num_heads * num_seqs
 };
 
+
+// 32x32x16 products: lane l holds A[m = l%32][k = 8(l/32) .. +7],
+// B[k = 8(l/32) .. +7][n = l%32] and D[m = 8(i/4) + 4(l/32) + i%4][n = l%32].
 template <pa_dtype DT>
-__device__ __forceinline__ f32x4_t mfma_qk(const uint4& a, const uint4& b, f32x4_t c) {
+__device__ __forceinline__ f32x16_t mfma_qk(const uint4& a, const uint4& b, f32x16_t c) {
   if constexpr (DT == PA_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4_t mfma_pv(const f16x8_t& a, const f16x8_t& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
-// D = head size, QB = 16-query blocks per wave.
-template <pa_dtype DT, int D, int QB>
-__global__ __launch_bounds__(kPrefillThreads, 3) void prefill_kernel(const PrefillParams p) {
-  constexpr int BM = kPrefillWaves * 16 * QB;   // query rows per workgroup
-  constexpr int KS = D / 32;                    // 32-wide k-steps over the head dim
-  constexpr int DB = D / 16;                    // 16-wide output blocks
+// D = head size.  OFF32: both caches span less than 4 GiB, so rows are
+// addressed by 32-bit byte offsets from the cache base.
+template <pa_dtype DT, int D, bool OFF32>
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillParams p) {
+  constexpr int KS = D / 16;                    // 16-wide k-steps over the head dim (QK)
+  constexpr int DB = D / 32;                    // 32-row blocks of O^T
   constexpr int KROW = D * 2 + 16;              // LDS bytes per K row (padded)
   constexpr int VROW = kBN * 2 + 8;             // LDS bytes per V^T row (padded)
   constexpr int KCH = D / 8;                    // 16-byte chunks per K/V row
   constexpr int KPT = kBN * KCH / kPrefillThreads;        // K chunks per thread per tile
   constexpr int VITEMS = (kBN / 4) * KCH;      // V items of 4 keys x 8 columns per tile
-  constexpr int VPT = (VITEMS + kPrefillThreads - 1) / kPrefillThreads;
   static_assert(KPT * kPrefillThreads == kBN * KCH, "K tile must split evenly");
+  static_assert(VITEMS <= kPrefillThreads, "one V item per thread");
   __shared__ __attribute__((aligned(16))) char sK[kBN * KROW];
   __shared__ __attribute__((aligned(16))) char sV[D * VROW];
 
@@ -117,50 +126,54 @@ __global__ __launch_bounds__(kPrefillThreads, 3) void prefill_kernel(const Prefi
 
   const int q_begin = p.query_start_loc[s];
   const int n = p.query_start_loc[s + 1] - q_begin;
-  const int q0 = qt * BM;
+  const int q0 = qt * kBM;
   if (q0 >= n) return;
   const int L = p.context_lens[s];
   const int kvh = h / (p.num_heads / p.num_kv_heads);
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  const int lq = lane % 16;     // query (column) owned by this lane within a block
-  const int lg = lane / 16;     // lane group: 4 keys / 8 k-elements slice
+  const int lq = lane % 32;     // query (column) owned by this lane
+  const int hf = lane / 32;     // half: k-slice 8 hf .. +7, rows 4 hf .. +3 of each 8
 
   // keys visible to the workgroup: 0 .. kend-1
-  const int last_row = min(n, q0 + BM) - 1;
+  const int last_row = min(n, q0 + kBM) - 1;
   const int kend = L - n + last_row + 1;
 
-  // Q^T fragments (B operand): query row q0 + wave*16*QB + qb*16 + lq,
-  // head-dim slice kstep*32 + lg*8 .. +7
-  uint4 qf[QB][KS];
-  int lim[QB];  // last visible key of this lane's query, per block
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int j = q0 + wave * 16 * QB + qb * 16 + lq;
-    lim[qb] = L - n + j;
+  // Q^T fragments (B operand): query row j, head-dim slice ks*16 + 8 hf .. +7
+  const int j = q0 + wave * kQW + lq;
+  const int lim = L - n + j;  // last visible key of this lane's query
+  uint4 qf[KS];
+  {
     const bool ok = j < n;
     const char* qp =
         p.query + (((int64_t)(q_begin + (ok ? j : 0)) * p.num_heads + h) * D) * Fmt<DT>::kBytes;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[qb][ks] = ok ? load16(qp + (ks * 4 + lg) * 16) : make_uint4(0, 0, 0, 0);
+      qf[ks] = ok ? load16(qp + (ks * 2 + hf) * 16) : make_uint4(0, 0, 0, 0);
   }
 
-  f32x4_t o[QB][DB];
-  float m[QB], l[QB];
+  f32x16_t o[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[qb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
 
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
   const int lbs = p.log2_bs;
   const int bs_mask = (1 << lbs) - 1;
   const int64_t head_off = (int64_t)kvh * p.head_stride;
+  const uint32_t blk_b = (uint32_t)(p.blk_stride * 2);
+  const uint32_t tok_b = (uint32_t)(p.tok_stride * 2);
+  // byte offset of row t (in block blk) at element column col
+  auto row_off = [&](int32_t blk, int t, int col) -> int64_t {
+    if constexpr (OFF32)
+      return (int64_t)((uint32_t)blk * blk_b + (uint32_t)(t & bs_mask) * tok_b +
+                       (uint32_t)((head_off + col) * 2));
+    else
+      return ((int64_t)blk * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride + head_off + col) * 2;
+  };
 
   // Global -> registers for one key tile.  Keys past kend are clamped to the
   // last visible key (finite data the tile reads anyway); the causal mask
@@ -182,147 +195,173 @@ __global__ __launch_bounds__(kPrefillThreads, 3) void prefill_kernel(const Prefi
     TileRegs r;
     {
       const int t = min(k0 + k_row, kend - 1);
-      const char* src = p.key_cache + ((int64_t)bt[t >> lbs] * p.blk_stride +
-                                       (int64_t)(t & bs_mask) * p.tok_stride + head_off + k_cg * 8) * 2;
+      const char* src = p.key_cache + row_off(bt[t >> lbs], t, k_cg * 8);
 #pragma unroll
       for (int i = 0; i < KPT; ++i) r.k[i] = load16(src + i * 16);
     }
     {
       const int tb = min(k0 + v_kq * 4, kend - 1);
-      const int64_t blk0 = (int64_t)bt[tb >> lbs] * p.blk_stride;
+      const int32_t blk0 = bt[tb >> lbs];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = min(k0 + v_kq * 4 + j, kend - 1);
-        const int64_t blk = bs_ge4 ? blk0 : (int64_t)bt[t >> lbs] * p.blk_stride;
-        r.v[j] = load16(p.value_cache +
-                        (blk + (int64_t)(t & bs_mask) * p.tok_stride + head_off + v_dq * 8) * 2);
+      for (int e = 0; e < 4; ++e) {
+        const int t = min(k0 + v_kq * 4 + e, kend - 1);
+        r.v[e] = load16(p.value_cache + row_off(bs_ge4 ? blk0 : bt[t >> lbs], t, v_dq * 8));
       }
     }
     return r;
   };
-  // smallest visible-key limit among this wave's query rows
-  const int lim_min = L - n + q0 + wave * 16 * QB;
+  // smallest and largest visible-key limits among this wave's query rows; a
+  // wave whose rows are all padding, or that sees none of a tile's keys,
+  // skips that tile's products (it still stages K/V and meets the barriers)
+  const int lim_min = L - n + q0 + wave * kQW;
+  const int lim_max = L - n + min(n - 1, q0 + wave * kQW + kQW - 1);
+  const bool wave_rows = q0 + wave * kQW < n;
+  const float c = p.scale_log2e;
+  const uint32_t ones = pk_f16(1.f, 1.f);
 
   TileRegs tr = fetch(0);
   for (int k0 = 0; k0 < kend; k0 += kBN) {
     // ---- registers -> LDS: K row-major, V transposed to [d][key] in f16
 #pragma unroll
     for (int i = 0; i < KPT; ++i) store16(sK + k_row * KROW + (k_cg + i) * 16, tr.k[i]);
-    if (VITEMS % kPrefillThreads == 0 || tid < VITEMS) {  // head size 64: half the threads stage no V
+    if (VITEMS == kPrefillThreads || tid < VITEMS) {  // head size 64: half the threads stage no V
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        f16x4_t col;
+      for (int e = 0; e < 8; e += 2) {
+        // columns e, e+1 of keys v_kq*4 .. +3
+        float f0[4], f1[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) col[j] = (_Float16)chunk_elem<DT>(tr.v[j], e);
-        *reinterpret_cast<f16x4_t*>(sV + (v_dq * 8 + e) * VROW + v_kq * 8) = col;
+        for (int k = 0; k < 4; ++k) {
+          f0[k] = chunk_elem<DT>(tr.v[k], e);
+          f1[k] = chunk_elem<DT>(tr.v[k], e + 1);
+        }
+        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e) * VROW + v_kq * 8) =
+            make_uint2(pk_f16(f0[0], f0[1]), pk_f16(f0[2], f0[3]));
+        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e + 1) * VROW + v_kq * 8) =
+            make_uint2(pk_f16(f1[0], f1[1]), pk_f16(f1[2], f1[3]));
       }
     }
     __syncthreads();
     tr = fetch(k0 + kBN);  // next tile in flight (clamped past the end: never a wait on a branch)
+    if (wave_rows && k0 <= lim_max) {  // wave-uniform
 
-    // ---- S^T = K Q^T for 4 key blocks of 16
-    float sc[QB][4][4];  // [query block][key block][key within lane group]
+    // ---- S^T = K Q^T: two blocks of 32 keys; lane holds query lq, keys
+    // k0 + 32 kb + 8 (i/4) + 4 hf + i%4
+    f32x16_t sc[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      f32x4_t acc[QB];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = load16(sK + (kb * 16 + lq) * KROW + ks * 64 + lg * 16);
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma_qk<DT>(a, qf[qb][ks], acc[qb]);
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 a = load16(sK + (kb * 32 + lq) * KROW + ks * 32 + hf * 16);
+        sc[kb] = mfma_qk<DT>(a, qf[ks], sc[kb]);
       }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[qb][kb][i] = acc[qb][i];
     }
 
-    // ---- online softmax, in-lane per query; 4 lanes share a query.  Only
-    // tiles that reach past some row's last visible key need the mask.
+    // ---- online softmax in the scaled log2 domain; the two halves of the
+    // wave hold the two key sets of each query.  Only tiles that reach past
+    // some row's last visible key need the mask.
     const bool need_mask = k0 + kBN - 1 > lim_min;  // wave-uniform
+    float mt = -INFINITY;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mt = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + kb * 16 + lg * 4 + i;
-          float zz = sc[qb][kb][i] * p.scale_log2e;
-          if (need_mask && key > lim[qb]) zz = -INFINITY;
-          sc[qb][kb][i] = zz;
-          mt = fmaxf(mt, zz);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (__any(mt > m[qb] + kLazyRescaleP)) {
-        const float mn = fmaxf(m[qb], mt);
-        const float a = exp2_diff(m[qb], mn);
-        m[qb] = mn;
-        l[qb] *= a;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[qb][db] *= a;
+      for (int i = 0; i < 16; ++i) {
+        float z = sc[kb][i];
+        if (need_mask && k0 + kb * 32 + 8 * (i / 4) + 4 * hf + (i % 4) > lim) z = -INFINITY;
+        sc[kb][i] = z;
+        mt = fmaxf(mt, z);
       }
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;  // c > 0: the max commutes with the scale
+    if (__any(mt > m + kLazyRescaleP)) {
+      const float mn = fmaxf(m, mt);
+      const float a = exp2_diff(m, mn);
+      m = mn;
+      l *= a;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= a;
     }
-
-    // ---- O^T += V^T P^T, 2 k-steps of 32 keys (key blocks 2ks, 2ks+1)
+    // p = 2^(c z - m), rounded to f16 (key 0 is visible to every query, so m
+    // is finite here and masked scores give exp2(-inf) = 0); the normaliser
+    // sums the rounded values
+    const float nm = -m;
+    uint32_t pp[2][8];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f16x8_t pb[QB];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // every query sees key 0, so m is finite here and exp2(-inf) = 0
-          const float e0 = __builtin_amdgcn_exp2f(sc[qb][2 * ks][i] - m[qb]);
-          const float e1 = __builtin_amdgcn_exp2f(sc[qb][2 * ks + 1][i] - m[qb]);
-          pb[qb][i] = (_Float16)e0;
-          pb[qb][4 + i] = (_Float16)e1;
-          l[qb] += e0 + e1;
-        }
+      for (int i = 0; i < 16; i += 2) {
+        const uint32_t w2 = pk_f16(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], c, nm)),
+                                   __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, nm)));
+        pp[kb][i / 2] = w2;
+        l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w2), __builtin_bit_cast(f16x2_t, ones),
+                                   l, false);
       }
+
+    // ---- O^T += V^T P^T over 4 slices of 16 keys.  Slice t = (kb, jp) uses
+    // this lane's registers 8 jp .. 8 jp + 7 of key block kb, i.e. keys
+    // 32 kb + 16 jp + 8 (e/4) + 4 hf + e%4 for e = 0..7; the V^T fragment
+    // takes its contraction slots in the same order.
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t / 2, jp = t % 2;
+      const f16x8_t pb = __builtin_bit_cast(
+          f16x8_t, make_uint4(pp[kb][4 * jp], pp[kb][4 * jp + 1], pp[kb][4 * jp + 2], pp[kb][4 * jp + 3]));
+      const int col = (kb * 32 + jp * 16 + hf * 4) * 2;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char* vrow = sV + (db * 16 + lq) * VROW;
-        const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vrow + (ks * 32 + lg * 4) * 2);
-        const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vrow + (ks * 32 + 16 + lg * 4) * 2);
-        const f16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma_pv(a, pb[qb], o[qb][db]);
+        const char* vrow = sV + (db * 32 + lq) * VROW + col;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb, o[db], 0, 0, 0);
       }
     }
+    }  // wave has visible keys in this tile
     __syncthreads();
   }
 
-  // ---- normalise and store: lane holds O[query lq][d = db*16 + lg*4 + i]
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float lt = l[qb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    const int j = q0 + wave * 16 * QB + qb * 16 + lq;
-    if (j >= n) continue;
+  // ---- normalise and store: lane holds O[query lq][d = 32 db + 8 g + 4 hf + i]
+  const float lt = l + __shfl_xor(l, 32);
+  if (j < n) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int64_t row = ((int64_t)(q_begin + j) * p.num_heads + h) * D;
+    // four consecutive columns per group g
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store_out(p.out, row + db * 16 + lg * 4 + i, o[qb][db][i] * inv, p.out_dtype);
+      for (int g = 0; g < 4; ++g) {
+        const int64_t idx = row + db * 32 + 8 * g + 4 * hf;
+        const float v0 = o[db][4 * g] * inv, v1 = o[db][4 * g + 1] * inv;
+        const float v2 = o[db][4 * g + 2] * inv, v3 = o[db][4 * g + 3] * inv;
+        if (p.out_dtype == PA_F32) {
+          store16(reinterpret_cast<float*>(p.out) + idx,
+                  make_uint4(__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)));
+        } else if (p.out_dtype == PA_BF16) {
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + idx) =
+              make_uint2(f32_to_bf16(v0) | (uint32_t)f32_to_bf16(v1) << 16,
+                         f32_to_bf16(v2) | (uint32_t)f32_to_bf16(v3) << 16);
+        } else {
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + idx) =
+              make_uint2(f32_to_f16(v0) | (uint32_t)f32_to_f16(v1) << 16,
+                         f32_to_f16(v2) | (uint32_t)f32_to_f16(v3) << 16);
+        }
+      }
   }
 }
 
 template <pa_dtype DT, int D>
-hipError_t launch_pd(PrefillParams p, int num_seqs, int max_q, hipStream_t st) {
-  constexpr int QB = 1;
-  constexpr int BM = kPrefillWaves * 16 * QB;
-  p.q_tiles = (max_q + BM - 1) / BM;
+hipError_t launch_pd(PrefillParams p, int num_seqs, int max_q, bool off32, hipStream_t st) {
+  p.q_tiles = (max_q + kBM - 1) / kBM;
   const int64_t nwork = (int64_t)p.q_tiles * p.num_heads * num_seqs;
   if (nwork > 0x7FFFFFFF - 8) return hipErrorInvalidValue;
   p.num_work = (int)nwork;
   dim3 grid((unsigned)(((nwork + 7) / 8) * 8)), block(kPrefillThreads);
-  hipLaunchKernelGGL((prefill_kernel<DT, D, QB>), grid, block, 0, st, p);
+  if (off32)
+    hipLaunchKernelGGL((prefill_kernel<DT, D, true>), grid, block, 0, st, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<DT, D, false>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
@@ -354,12 +393,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.log2_bs = __builtin_ctz((unsigned)g.block_size);
   p.scale_log2e = a.scale * kLog2e;
   p.out_dtype = a.out_dtype;
+  const bool off32 = (int64_t)g.num_blocks * p.blk_stride * 2 <= (int64_t)UINT32_MAX;
   if (a.kv_dtype == PA_BF16) {
-    if (g.head_size == 64) return launch_pd<PA_BF16, 64>(p, a.num_seqs, a.max_query_len, stream);
-    if (g.head_size == 128) return launch_pd<PA_BF16, 128>(p, a.num_seqs, a.max_query_len, stream);
+    if (g.head_size == 64) return launch_pd<PA_BF16, 64>(p, a.num_seqs, a.max_query_len, off32, stream);
+    if (g.head_size == 128) return launch_pd<PA_BF16, 128>(p, a.num_seqs, a.max_query_len, off32, stream);
   } else if (a.kv_dtype == PA_F16) {
-    if (g.head_size == 64) return launch_pd<PA_F16, 64>(p, a.num_seqs, a.max_query_len, stream);
-    if (g.head_size == 128) return launch_pd<PA_F16, 128>(p, a.num_seqs, a.max_query_len, stream);
+    if (g.head_size == 64) return launch_pd<PA_F16, 64>(p, a.num_seqs, a.max_query_len, off32, stream);
+    if (g.head_size == 128) return launch_pd<PA_F16, 128>(p, a.num_seqs, a.max_query_len, off32, stream);
   }
   return hipErrorInvalidValue;
 }
