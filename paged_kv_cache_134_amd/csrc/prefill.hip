@@ -51,6 +51,7 @@ constexpr int kQW = 32;                         // query rows per wave
 constexpr int kBM = kPrefillWaves * kQW;        // query rows per workgroup
 constexpr int kBN = 64;                         // keys per tile
 constexpr float kLazyRescaleP = 8.f;            // log2 headroom of the running max
+constexpr int kBtWinP = 256;                    // block-table entries staged in LDS at a time
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -75,7 +76,7 @@ struct PrefillParams {
   float scale_log2e;
   pa_dtype out_dtype;
   int32_t q_tiles;   // query tiles per sequence (of the longest)
-  int32_t num_work;  // q_tiles * num_heads * num_seqs
+  int32_t num_work;  // (sequence, head) pairs: num_heads * num_seqs
 };
 
 
@@ -110,19 +111,24 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   static_assert(VITEMS <= kPrefillThreads, "one V item per thread");
   __shared__ __attribute__((aligned(16))) char sK[kBN * KROW];
   __shared__ __attribute__((aligned(16))) char sV[D * VROW];
+  __shared__ int32_t s_bt[kBtWinP];  // block-table window
 
-  // XCD-aware order: consecutive workgroup ids are spread over the 8 XCDs
-  // (each with its own L2), so the ids are remapped to give every XCD a
-  // contiguous run of work items, i.e. the query tiles of one (sequence,
-  // head), which read the same K/V tiles, share an L2.
-  const int nwork = p.num_work;
-  const int per_xcd = (nwork + 7) / 8;
+  // XCD-aware order: consecutive workgroup ids go round-robin to the 8 XCDs
+  // (each with its own L2).  Pairs are numbered head-major (pair = head *
+  // num_seqs + sequence) and XCD x takes pairs x, x + 8, x + 16, ...: all
+  // query tiles of a pair, which read the same K/V tiles, run back to back
+  // on one XCD; each XCD works through the heads in order, so a head's
+  // shared prefix blocks stay in its L2 while the sequences that share them
+  // pass; and interleaving the pairs keeps the XCDs' shares even when
+  // sequence lengths vary.
   const int b = blockIdx.x;
-  const int work = (b % 8) * per_xcd + b / 8;
-  if (work >= nwork) return;
-  const int qt = work % p.q_tiles;
-  const int h = (work / p.q_tiles) % p.num_heads;
-  const int s = work / (p.q_tiles * p.num_heads);
+  const int local = b / 8;
+  const int pair = (local / p.q_tiles) * 8 + b % 8;
+  if (pair >= p.num_work) return;  // num_work counts (sequence, head) pairs
+  const int qt = local % p.q_tiles;
+  const int num_seqs = p.num_work / p.num_heads;
+  const int h = pair / num_seqs;
+  const int s = pair % num_seqs;
 
   const int q_begin = p.query_start_loc[s];
   const int n = p.query_start_loc[s + 1] - q_begin;
@@ -175,6 +181,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       return ((int64_t)blk * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride + head_off + col) * 2;
   };
 
+  // Block ids come from an LDS window of the table (entries wb0 ..
+  // wb0 + kBtWinP - 1, clamped to the last entry the workgroup reads), so no
+  // tile load waits on another global load.
+  const int e_last = (kend - 1) >> lbs;
+  int wb0 = 0;
+  auto stage_bt = [&]() {
+    for (int i = tid; i < kBtWinP; i += kPrefillThreads) s_bt[i] = bt[min(wb0 + i, e_last)];
+  };
+  stage_bt();
+  __syncthreads();
+
   // Global -> registers for one key tile.  Keys past kend are clamped to the
   // last visible key (finite data the tile reads anyway); the causal mask
   // gives them probability 0, so every load is unconditional.  A thread
@@ -195,17 +212,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     TileRegs r;
     {
       const int t = min(k0 + k_row, kend - 1);
-      const char* src = p.key_cache + row_off(bt[t >> lbs], t, k_cg * 8);
+      const char* src = p.key_cache + row_off(s_bt[(t >> lbs) - wb0], t, k_cg * 8);
 #pragma unroll
       for (int i = 0; i < KPT; ++i) r.k[i] = load16(src + i * 16);
     }
     {
       const int tb = min(k0 + v_kq * 4, kend - 1);
-      const int32_t blk0 = bt[tb >> lbs];
+      const int32_t blk0 = s_bt[(tb >> lbs) - wb0];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = min(k0 + v_kq * 4 + e, kend - 1);
-        r.v[e] = load16(p.value_cache + row_off(bs_ge4 ? blk0 : bt[t >> lbs], t, v_dq * 8));
+        r.v[e] = load16(p.value_cache + row_off(bs_ge4 ? blk0 : s_bt[(t >> lbs) - wb0], t, v_dq * 8));
       }
     }
     return r;
@@ -240,6 +257,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
             make_uint2(pk_f16(f1[0], f1[1]), pk_f16(f1[2], f1[3]));
       }
     }
+    {
+      // the next tile's entries must be in the window; every read of it
+      // ended with the previous fetch, which the loop's last barrier orders
+      // (the window spans >= 256 keys, so no refill happens before the
+      // first tile's fetch has passed a barrier)
+      const int kn = k0 + kBN;
+      if (kn < kend && (min(kn + kBN - 1, kend - 1) >> lbs) - wb0 >= kBtWinP) {  // uniform
+        wb0 = kn >> lbs;
+        stage_bt();
+      }
+    }
     __syncthreads();
     tr = fetch(k0 + kBN);  // next tile in flight (clamped past the end: never a wait on a branch)
     if (wave_rows && k0 <= lim_max) {  // wave-uniform
@@ -251,14 +279,16 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
+    // all K fragments of the tile are requested before the first product
+    uint4 ka[KS][2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint4 a = load16(sK + (kb * 32 + lq) * KROW + ks * 32 + hf * 16);
-        sc[kb] = mfma_qk<DT>(a, qf[ks], sc[kb]);
-      }
-    }
+      for (int kb = 0; kb < 2; ++kb) ka[ks][kb] = load16(sK + (kb * 32 + lq) * KROW + ks * 32 + hf * 16);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma_qk<DT>(ka[ks][kb], qf[ks], sc[kb]);
 
     // ---- online softmax in the scaled log2 domain; the two halves of the
     // wave hold the two key sets of each query.  Only tiles that reach past
@@ -354,10 +384,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 template <pa_dtype DT, int D>
 hipError_t launch_pd(PrefillParams p, int num_seqs, int max_q, bool off32, hipStream_t st) {
   p.q_tiles = (max_q + kBM - 1) / kBM;
-  const int64_t nwork = (int64_t)p.q_tiles * p.num_heads * num_seqs;
-  if (nwork > 0x7FFFFFFF - 8) return hipErrorInvalidValue;
-  p.num_work = (int)nwork;
-  dim3 grid((unsigned)(((nwork + 7) / 8) * 8)), block(kPrefillThreads);
+  const int64_t pairs = (int64_t)p.num_heads * num_seqs;
+  const int64_t blocks = (pairs + 7) / 8 * 8 * p.q_tiles;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  p.num_work = (int)pairs;
+  dim3 grid((unsigned)blocks), block(kPrefillThreads);
   if (off32)
     hipLaunchKernelGGL((prefill_kernel<DT, D, true>), grid, block, 0, st, p);
   else
