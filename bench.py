@@ -35,7 +35,16 @@ if ROOT not in sys.path:
 METRIC = "paged decode KV GB/s (fraction of HBM peak); prefill MFMA util; tokens/s"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16/fp16 MFMA, AMD published
-KERNEL_SOURCES = {"decode": "decode.hip", "prefill": "prefill.hip", "write": "cache_ops.hip"}
+# source file of each timed kernel (its hash ties a committed counter profile
+# to the kernel it was taken on)
+KERNEL_SOURCES = {"decode_head": "decode_head.hip", "decode_group": "decode_group.hip",
+                  "prefill": "prefill.hip", "write": "cache_ops.hip"}
+
+
+def decode_kernel_kind(w) -> str:
+    """Which decode kernel the library dispatches for this workload (grouped
+    kernel for group sizes 4, 8, 16 with 16-bit caches, else per-head)."""
+    return "decode_group" if w.dtype != "f32" and w.G in (4, 8, 16) else "decode_head"
 
 
 def log(*a):
@@ -208,7 +217,7 @@ def main():
         unit = "GB/s"
         dom_ms = kern_ms[dominant]
         achieved = kv_bytes / (dom_ms * 1e-3) / 1e9
-        kind_src = "decode"
+        kind_src = decode_kernel_kind(w)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
         alg = {"kv_bytes_per_step": kv_bytes}

@@ -23,7 +23,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["pa_api.hip", "cache_ops.hip", "decode.hip", "prefill.hip"]
+HIP_SOURCES = ["pa_api.hip", "cache_ops.hip", "decode.hip", "decode_head.hip", "decode_group.hip",
+               "prefill.hip"]
 CXX_SOURCES = ["pool.cpp"]
 
 

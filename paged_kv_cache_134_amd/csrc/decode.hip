@@ -1,5 +1,5 @@
 // Paged decode attention for gfx950: single pass ("V1") or split-K partitions
-// plus a reduce ("V2").
+// plus a reduce ("V2") -- dispatch, launch parameters and the reduce kernel.
 //
 // What is computed follows "PagedAttention 在 vLLM 中的实现分析" §3.1 (block
 // table lookup: block block_table[t / block_size], offset t % block_size),
@@ -8,637 +8,23 @@
 // attention" post (k4i.top, attention over non-contiguous blocks).
 //
 // Two kernels share one contract; the dispatcher picks by GQA group size G
-// and element type.  Both use one workgroup of 4 waves per (sequence, kv
-// head, partition), read each kv head's K/V rows once for all G query heads
-// of its group, never load a token at or past the context length (so NaN in
-// unused slots cannot reach the arithmetic), and order every floating-point
-// operation by logical position only, so results are bitwise independent of
-// which physical blocks hold the context.  Running maxima are moved lazily:
-// only when a batch exceeds the reference by more than 2^8, since the final
-// quotient does not depend on where the reference sits.
-//
-// Register kernel (G <= 2, and every fp32 case): a token row of one kv head
-// is spread over LPT lanes that each own one 16-byte chunk, so a wave reads
-// TPW = 64 / LPT whole rows per 16-byte load; QK partial dots are summed
-// across the LPT lanes with DPP.  The partition's block-table entries are
-// staged in LDS, and the next batch of rows is loaded while the current one
-// is consumed.
-//
-// LDS kernel (G >= 4, bf16/f16): per chunk of 64 tokens the workgroup copies
-// K and V rows (coalesced 16-byte loads, prefetched one chunk ahead in
-// registers) into LDS.  QK: lane = token, each wave owns G/4 query heads
-// whose query vectors are read as scalar (SGPR) operands of v_dot2, and K
-// rows sit in LDS with a padded row stride (consecutive rows start in
-// consecutive 16-byte bank groups, so a lane-per-row read is conflict-free
-// with a constant offset); no cross-lane reduction and one exp per (token,
-// head).  PV: lane
-// owns D/32 output columns of all G heads and each wave a quarter of the
-// chunk's tokens; probabilities are broadcast from LDS.
+// and element type: the per-head kernel (decode_head.hip) for G <= 2 and
+// every fp32 cache, the grouped kernel (decode_group.hip) otherwise.  Both
+// use one workgroup of 4 waves per (sequence, kv head, partition), read each
+// kv head's K/V rows once for all G query heads of its group, never load a
+// token at or past the context length (so NaN in unused slots cannot reach
+// the arithmetic), and order every floating-point operation by logical
+// position only, so results are bitwise independent of which physical
+// blocks hold the context.  Running maxima are moved lazily: only when a
+// batch exceeds the reference by more than 2^8, since the final quotient
+// does not depend on where the reference sits.
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-
-#include "kernel_common.h"
-#include "pa_internal.h"
+#include "decode_common.h"
 
 namespace pa {
+namespace dec {
 namespace {
-
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeThreads = kDecodeWaves * kWave;
-constexpr float kLazyRescale = 8.f;  // log2 headroom before a running max moves
-
-typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
-
-struct DecodeParams {
-  void* out;
-  const void* query;
-  const char* key_cache;
-  const char* value_cache;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  float* part_out;
-  float* part_ml;
-  int64_t blk_stride;   // elements between blocks
-  int64_t tok_stride;   // elements between tokens of a block
-  int64_t head_stride;  // elements between kv heads
-  int32_t max_blocks_per_seq;
-  int32_t num_heads;
-  int32_t num_kv_heads;
-  int32_t log2_bs;
-  int32_t partition_size;  // 0 = single pass
-  int32_t max_partitions;
-  float scale_log2e;
-  pa_dtype out_dtype;
-  bool off32;  // every byte offset into either cache fits in 32 bits
-};
-
-// Maximum over the 64 lanes of a wave (every lane receives it).
-__device__ __forceinline__ float wave_max(float x) {
-  x = group_max<16>(x);
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-  x = group_sum<16>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
-// Writes one (max, sum, unnormalised output) partial, or the final output
-// when the whole context is one partition (the reduce skips those heads).
-__device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int part, int d, int D,
-                                     float M, float lsum, float o, bool single) {
-  if (p.partition_size > 0 && !single) {
-    const int64_t pi = head * p.max_partitions + part;
-    p.part_out[pi * D + d] = o;
-    if (d == 0) {
-      p.part_ml[2 * pi] = M;
-      p.part_ml[2 * pi + 1] = lsum;
-    }
-  } else {
-    store_out(p.out, head * D + d, lsum > 0.f ? o / lsum : 0.f, p.out_dtype);
-  }
-}
-
-// ------------------------------------------------------------ register kernel
-constexpr int kUnroll = 4;    // token rows per lane group per batch
-constexpr int kWindow = 512;  // tokens per block-table staging window
-
-template <pa_dtype DT, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const DecodeParams p) {
-  using F = Fmt<DT>;
-  constexpr int VEC = F::kVec;             // elements per lane chunk
-  constexpr int LPT = D / VEC;             // lanes per token row
-  constexpr int TPW = kWave / LPT;         // token rows per wave per step
-  constexpr int TPS = TPW * kDecodeWaves;  // token rows per workgroup per step
-  static_assert(LPT >= 1 && LPT <= kWave && (kWave % LPT) == 0, "bad head size");
-  __shared__ int32_t s_bt[kWindow + 1];
-
-  const int kvh = blockIdx.x % p.num_kv_heads;
-  const int s = blockIdx.x / p.num_kv_heads;
-  const int part = blockIdx.y;
-  const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  const int tg = lane / LPT;  // lane group (token row) within the wave
-  const int ch = lane % LPT;  // 16-byte chunk of the row owned by this lane
-
-  const int L = p.context_lens[s];
-  int t0 = 0, t1 = L;
-  if (p.partition_size > 0) {
-    t0 = part * p.partition_size;
-    if (t0 >= L) return;  // partition past the end: the reduce ignores it
-    t1 = min(L, t0 + p.partition_size);
-  }
-
-  uint4 q[G];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(p.query) +
-                      ((int64_t)s * p.num_heads + (int64_t)kvh * G) * (D / VEC) + ch;
-#pragma unroll
-    for (int g = 0; g < G; ++g) q[g] = qp[g * (D / VEC)];
-  }
-
-  float m[G], l[G], acc[G][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[g][e] = 0.f;
-  }
-
-  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-  const int lbs = p.log2_bs;
-  const int bs_mask = (1 << lbs) - 1;
-  const int64_t lane_off = (int64_t)kvh * p.head_stride + ch * VEC;
-
-  for (int w0 = t0; w0 < t1; w0 += kWindow) {
-    const int w1 = min(t1, w0 + kWindow);
-    const int e0 = w0 >> lbs;
-    const int ne = ((w1 - 1) >> lbs) - e0 + 1;
-    __syncthreads();  // the previous window's readers are done
-    for (int i = threadIdx.x; i < ne; i += kDecodeThreads) s_bt[i] = bt[e0 + i];
-    __syncthreads();
-
-    // Rows past the window are clamped to its last row (finite data loaded
-    // anyway) and masked by `valid`, so the loads are unconditional and none
-    // waits for another.
-    auto load = [&](int wbase, uint4 (&kr)[kUnroll], uint4 (&vr)[kUnroll], bool (&valid)[kUnroll]) {
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int t = wbase + u * TPS + tg;
-        valid[u] = t < w1;
-        const int tc = min(t, w1 - 1);
-        const int64_t blk = s_bt[(tc >> lbs) - e0];
-        const int64_t off = blk * p.blk_stride + (int64_t)(tc & bs_mask) * p.tok_stride + lane_off;
-        kr[u] = load_nt(p.key_cache + off * F::kBytes);
-        vr[u] = load_nt(p.value_cache + off * F::kBytes);
-      }
-    };
-
-    // consume one batch: scores, lazy rescale, probabilities, V accumulation
-    auto consume = [&](int wbase, const uint4 (&kr)[kUnroll], const uint4 (&vr)[kUnroll]) {
-      bool valid[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) valid[u] = wbase + u * TPS + tg < w1;
-      float z[kUnroll][G];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float d = group_sum<LPT>(dot_chunk<DT>(q[g], kr[u], 0.f));
-          z[u][g] = valid[u] ? d * p.scale_log2e : -INFINITY;
-        }
-      }
-      bool need = false;
-      float mb[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        mb[g] = z[0][g];
-#pragma unroll
-        for (int u = 1; u < kUnroll; ++u) mb[g] = fmaxf(mb[g], z[u][g]);
-        need |= mb[g] > m[g] + kLazyRescale;
-      }
-      if (__any(need)) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float mn = fmaxf(m[g], mb[g]);
-          const float a = exp2_diff(m[g], mn);
-          m[g] = mn;
-          l[g] *= a;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[g][e] *= a;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        float vf[VEC];
-        chunk_to_f32<DT>(vr[u], vf);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float pw = valid[u] ? __builtin_amdgcn_exp2f(z[u][g] - m[g]) : 0.f;
-          l[g] += pw;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[g][e] = __builtin_fmaf(pw, vf[e], acc[g][e]);
-        }
-      }
-    };
-
-    // ping-pong buffers: the next batch is always in flight (its rows past
-    // the window are clamped, so the load is unconditional and no wait merges
-    // across a branch)
-    constexpr int kStep = kUnroll * TPS;
-    uint4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
-    bool dummy[kUnroll];
-    int wbase = w0 + wave * TPW;  // wave-uniform: groups past the end carry invalid rows
-    load(wbase, ka, va, dummy);
-    while (wbase < w1) {
-      load(wbase + kStep, kb, vb, dummy);
-      consume(wbase, ka, va);
-      wbase += kStep;
-      if (wbase >= w1) break;
-      load(wbase + kStep, ka, va, dummy);
-      consume(wbase, kb, vb);
-      wbase += kStep;
-    }
-  }
-
-  // merge the lane groups of the wave (log-sum-exp rule)
-#pragma unroll
-  for (int x = LPT; x < kWave; x <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], x);
-      const float lo = __shfl_xor(l[g], x);
-      const float mn = fmaxf(m[g], mo);
-      const float a = exp2_diff(m[g], mn);
-      const float b = exp2_diff(mo, mn);
-      l[g] = a * l[g] + b * lo;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float ao = __shfl_xor(acc[g][e], x);
-        acc[g][e] = a * acc[g][e] + b * ao;
-      }
-      m[g] = mn;
-    }
-  }
-
-  // merge the waves through LDS
-  __shared__ float sm_m[kDecodeWaves][G];
-  __shared__ float sm_l[kDecodeWaves][G];
-  __shared__ float sm_acc[kDecodeWaves][G][D];
-  if (tg == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sm_acc[wave][g][ch * VEC + e] = acc[g][e];
-      if (ch == 0) {
-        sm_m[wave][g] = m[g];
-        sm_l[wave][g] = l[g];
-      }
-    }
-  }
-  __syncthreads();
-
-  const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
-  for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) {
-    const int g = i / D;
-    const int d = i % D;
-    float M = sm_m[0][g];
-#pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w][g]);
-    float lsum = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float a = exp2_diff(sm_m[w][g], M);
-      lsum += a * sm_l[w][g];
-      o += a * sm_acc[w][g][d];
-    }
-    emit(p, head0 + g, part, d, D, M, lsum, o, L <= p.partition_size);
-  }
-}
-
-// ----------------------------------------------------------------- LDS kernel
-constexpr int kChunk = 64;   // tokens per LDS chunk (one per lane in QK)
-constexpr int kBtWin = 256;  // block-table entries staged in LDS at a time
-
-// 4 waves per SIMD (<= 128 VGPRs): with ~34 KB of LDS per workgroup that is
-// 4 workgroups, i.e. 128 KB of prefetched K/V in flight, per CU.  (G = 16 at
-// head size 128 needs more accumulators and settles for 2.)  OFF32: both
-// caches span less than 4 GiB, so row addresses are 32-bit byte offsets from
-// the cache base.
-//
-// PV runs on v_dot2 with f16 operands: the probabilities are rounded to f16
-// once (the normaliser sums the rounded values), and bf16 V converts to f16
-// exactly while |v| < 65536 (the significand fits; a subnormal f16 loses
-// less than 2^-24).  If a chunk of a bf16 cache holds a larger, infinite or
-// NaN value, the workgroup starts its range again with fp32 products; the
-// two passes are separate loops, so neither carries the other's state.
-template <int G, int D>
-constexpr int kLdsMinWaves = (G >= 16 && D >= 128) ? 2 : 4;
-
-template <pa_dtype DT, int D, int G, bool OFF32>
-__global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_lds_kernel(
-    const DecodeParams p) {
-  static_assert(DT != PA_F32, "LDS kernel takes 16-bit elements");
-  static_assert(G % kDecodeWaves == 0, "G must be a multiple of 4");
-  constexpr int RC = D / 8;                        // 16-byte pieces per row
-  constexpr int PIECES = kChunk * RC;              // pieces per chunk of K (or V)
-  constexpr int PPT = PIECES / kDecodeThreads;     // pieces per thread per tensor
-  constexpr int RSTEP = kDecodeThreads / RC;       // rows between a thread's pieces
-  constexpr int HPW = G / kDecodeWaves;            // query heads per wave in QK
-  constexpr int DPL = D / 32;                      // output columns per lane in PV
-  constexpr int NPI = kChunk / kDecodeWaves / 4;   // PV token-pair iterations per wave
-  static_assert(PPT * kDecodeThreads == PIECES, "chunk must split evenly");
-  constexpr int KSTR = RC + 1;                     // K row stride in pieces (padded)
-  __shared__ uint4 sKV[kChunk * KSTR + PIECES];    // K (padded rows) then V; reused at the end
-  __shared__ __align__(16) _Float16 sPh[kChunk / 2][G][2];  // probabilities, token pairs interleaved
-  __shared__ float sAlpha[G];                      // per-head rescale of this chunk
-  __shared__ int32_t sResc[kDecodeWaves];          // wave w moved a running max this chunk
-  __shared__ int32_t sVwide[2];                    // chunk parity: a V value is beyond f16 range
-  __shared__ float sM[G], sL[G];
-  __shared__ int32_t s_bt[kBtWin];                 // block-table window
-  uint4* sK = sKV;
-  uint4* sV = sKV + kChunk * KSTR;
-
-  const int kvh = blockIdx.x % p.num_kv_heads;
-  const int s = blockIdx.x / p.num_kv_heads;
-  const int part = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-
-  const int L = p.context_lens[s];
-  int t0 = 0, t1 = L;
-  if (p.partition_size > 0) {
-    t0 = part * p.partition_size;
-    if (t0 >= L) return;
-    t1 = min(L, t0 + p.partition_size);
-  }
-
-  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-  const int lbs = p.log2_bs;
-  const int bs_mask = (1 << lbs) - 1;
-  const int e_last = (t1 - 1) >> lbs;  // last block-table entry this workgroup reads
-
-  // query vectors of this wave's heads as scalar operands (bf16/f16 pairs)
-  const const_u32_ptr qc = (const_u32_ptr)((const char*)p.query +
-      (((int64_t)s * p.num_heads + (int64_t)kvh * G + wave * HPW) * D) * 2);
-
-  // Consecutive lanes load consecutive 16-byte chunks of a row, so every
-  // load instruction covers whole cache lines (the loads are non-temporal and
-  // a partly used line would be fetched again).  Rows at or past the end are
-  // clamped to the last row (a valid, finite row the chunk loads anyway) and
-  // masked where they are used, so every load is unconditional.  Block ids
-  // come from the LDS window, so no load waits on another global load.
-  const int prow = tid / RC;
-  const int pcol = tid % RC;
-  const int64_t lane_off = (int64_t)kvh * p.head_stride + pcol * 8;  // elements
-  const uint32_t blk_b = (uint32_t)(p.blk_stride * 2);
-  const uint32_t tok_b = (uint32_t)(p.tok_stride * 2);
-  const uint32_t lane_b = (uint32_t)(lane_off * 2);
-
-  const int half = lane / 32;  // PV: token parity within a pair
-  const int dl = lane % 32;    // PV: output columns dl*DPL .. +DPL-1
-  // PV bases: V row 2 (wave * 8 + half) at the lane's columns, and the weight
-  // pairs of token pair wave * 8 + half
-  const char* pv_base = reinterpret_cast<const char*>(sV) +
-                        (2 * (wave * (kChunk / kDecodeWaves / 2) + half) * RC) * 16 + dl * DPL * 2;
-  const char* pp_base = reinterpret_cast<const char*>(&sPh[wave * (kChunk / kDecodeWaves / 2) + half][0][0]);
-
-  // One pass over [t0, t1).  F16: PV on f16 v_dot2; returns false, having
-  // written nothing, as soon as a chunk holds a V value beyond f16 range.
-  auto run = [&](auto f16_tag) -> bool {
-    constexpr bool F16 = decltype(f16_tag)::value;
-    int wb0 = t0 >> lbs;  // the window holds entries wb0 .. wb0 + kBtWin - 1 (clamped to e_last)
-    auto stage_bt = [&]() {
-      for (int i = tid; i < kBtWin; i += kDecodeThreads) s_bt[i] = bt[min(wb0 + i, e_last)];
-    };
-    auto fetch = [&](int c0, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
-      int32_t blk[PPT];
-      int tc[PPT];
-#pragma unroll
-      for (int r = 0; r < PPT; ++r) {
-        tc[r] = min(c0 + prow + RSTEP * r, t1 - 1);
-        blk[r] = s_bt[(tc[r] >> lbs) - wb0];
-      }
-#pragma unroll
-      for (int r = 0; r < PPT; ++r) {
-        if constexpr (OFF32) {
-          const uint32_t off = (uint32_t)blk[r] * blk_b + (uint32_t)(tc[r] & bs_mask) * tok_b + lane_b;
-          kr[r] = load_nt(p.key_cache + off);
-          vr[r] = load_nt(p.value_cache + off);
-        } else {
-          const int64_t off = (int64_t)blk[r] * p.blk_stride +
-                              (int64_t)(tc[r] & bs_mask) * p.tok_stride + lane_off;
-          kr[r] = load_nt(p.key_cache + off * 2);
-          vr[r] = load_nt(p.value_cache + off * 2);
-        }
-      }
-    };
-
-    float m_ref[HPW], l_lane[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      m_ref[hh] = -INFINITY;
-      l_lane[hh] = 0.f;
-    }
-    float acc[G][DPL];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-
-    __syncthreads();  // LDS of an abandoned pass is no longer read
-    stage_bt();
-    if (F16 && tid == 0) sVwide[0] = sVwide[1] = 0;
-    __syncthreads();  // window staged
-    // One chunk in flight in registers while the previous one is consumed
-    // from LDS.  ci counts chunks (its parity selects the V-range flag).
-    auto step = [&](int c0, int ci, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) -> bool {
-      __syncthreads();  // previous chunk fully consumed (also every read of the window)
-#pragma unroll
-      for (int r = 0; r < PPT; ++r) {  // piece tid + 256 r: row prow + RSTEP r, column pcol
-        sK[(prow + RSTEP * r) * KSTR + pcol] = kr[r];
-        sV[tid + kDecodeThreads * r] = vr[r];
-      }
-      if constexpr (F16 && DT == PA_BF16) {
-        // largest |v| bit pattern of this thread's V pieces (sign cleared)
-        u16x2_t mx = {0, 0};
-#pragma unroll
-        for (int r = 0; r < PPT; ++r) {
-          const uint32_t w4[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, w4[j] & 0x7FFF7FFFu));
-        }
-        if (max(mx.x, mx.y) >= 0x4780) sVwide[ci & 1] = 1;  // |v| >= 65536, inf or NaN
-      }
-      const int cn = c0 + kChunk;
-      const bool more = cn < t1;
-      if (more && (min(cn + kChunk - 1, t1 - 1) >> lbs) - wb0 >= kBtWin) {  // uniform
-        wb0 = cn >> lbs;
-        stage_bt();
-      }
-      __syncthreads();
-      if constexpr (F16 && DT == PA_BF16) {
-        if (tid == 0) sVwide[(ci + 1) & 1] = 0;  // its last reader was the previous chunk
-        if (__builtin_amdgcn_readfirstlane(sVwide[ci & 1]) != 0) return false;  // uniform
-      }
-      if (more) fetch(cn, kr, vr);  // next chunk in flight
-
-      // ---- QK: lane = token row, this wave's HPW heads
-      const int row = lane;
-      const bool valid = c0 + row < t1;
-      float z[HPW];
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) z[hh] = 0.f;
-#pragma unroll 1
-      for (int pc = 0; pc < RC; pc += 4) {
-        uint4 kk[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kk[j] = sK[row * KSTR + pc + j];  // padded rows: conflict-free
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-          const const_u32_ptr qh = qc + hh * (D / 2) + pc * 4;
-          float a = z[hh];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint4 qq = make_uint4(qh[4 * j], qh[4 * j + 1], qh[4 * j + 2], qh[4 * j + 3]);
-            a = dot_chunk<DT>(qq, kk[j], a);
-          }
-          z[hh] = a;
-        }
-      }
-      // ---- online softmax of this wave's heads.  The running max moves only
-      // when some token of the chunk exceeds it by more than the headroom, so
-      // the wave-wide maximum is taken only then (a ballot decides).
-      bool resc = false;
-      float alpha[HPW];
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        const int h = wave * HPW + hh;
-        const float zz = valid ? z[hh] * p.scale_log2e : -INFINITY;
-        alpha[hh] = 1.f;
-        if (__any(zz > m_ref[hh] + kLazyRescale)) {
-          const float mn = fmaxf(m_ref[hh], wave_max(zz));
-          alpha[hh] = exp2_diff(m_ref[hh], mn);
-          m_ref[hh] = mn;
-          l_lane[hh] *= alpha[hh];
-          resc = true;
-        }
-        // rounded to f16 once: the PV weights and the normaliser use the
-        // same value
-        const _Float16 ph = (_Float16)(valid ? __builtin_amdgcn_exp2f(zz - m_ref[hh]) : 0.f);
-        l_lane[hh] += (float)ph;
-        sPh[row >> 1][h][row & 1] = ph;
-      }
-      if (lane == 0) {
-        sResc[wave] = resc;
-        if (resc) {
-#pragma unroll
-          for (int hh = 0; hh < HPW; ++hh) sAlpha[wave * HPW + hh] = alpha[hh];
-        }
-      }
-      __syncthreads();
-
-      // ---- PV: wave owns rows 16 wave .. +15 as 8 token pairs; a half-wave
-      // takes pairs (2j, 2j+1) and a lane D/32 columns of all G heads.  Rows
-      // past the end carry p = 0 and finite (clamped) V.
-      // Heads of QK wave w are rescaled only when that wave moved a max.
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        if (__builtin_amdgcn_readfirstlane(sResc[w])) {
-#pragma unroll
-          for (int hh = 0; hh < HPW; ++hh) {
-            const float a = sAlpha[w * HPW + hh];
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[w * HPW + hh][e] *= a;
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < NPI; ++i) {
-        const char* va = pv_base + i * (4 * RC * 16);  // pair wave * 8 + 2 i + half
-        const char* vb = va + RC * 16;
-        uint32_t wa[DPL / 2], wb[DPL / 2];
-        if constexpr (DPL == 4) {
-          const uint2 a2 = *reinterpret_cast<const uint2*>(va);
-          const uint2 b2 = *reinterpret_cast<const uint2*>(vb);
-          wa[0] = a2.x; wa[1] = a2.y; wb[0] = b2.x; wb[1] = b2.y;
-        } else {
-          wa[0] = *reinterpret_cast<const uint32_t*>(va);
-          wb[0] = *reinterpret_cast<const uint32_t*>(vb);
-        }
-        const uint4* pq = reinterpret_cast<const uint4*>(pp_base + i * (2 * G * 4));
-        uint32_t pw[G];
-#pragma unroll
-        for (int h4 = 0; h4 < G / 4; ++h4) {
-          const uint4 pw4 = pq[h4];
-          pw[4 * h4] = pw4.x; pw[4 * h4 + 1] = pw4.y; pw[4 * h4 + 2] = pw4.z; pw[4 * h4 + 3] = pw4.w;
-        }
-        if constexpr (F16) {
-          uint32_t vv[DPL];  // (row 2j, row 2j+1) f16 pairs per column
-#pragma unroll
-          for (int c = 0; c < DPL; ++c) {
-            const uint32_t xa = wa[c / 2], xb = wb[c / 2];
-            if constexpr (DT == PA_BF16) {
-              const float fa = __uint_as_float((c & 1) ? (xa & 0xFFFF0000u) : (xa << 16));
-              const float fb = __uint_as_float((c & 1) ? (xb & 0xFFFF0000u) : (xb << 16));
-              vv[c] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa, fb));
-            } else {
-              vv[c] = __builtin_amdgcn_perm(xb, xa, (c & 1) ? 0x07060302u : 0x05040100u);
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int c = 0; c < DPL; ++c)
-              acc[h][c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[h]),
-                                                 __builtin_bit_cast(f16x2_t, vv[c]), acc[h][c], false);
-        } else {
-          // fp32 products, row 2j then 2j+1
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float pa = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[h] & 0xFFFFu));
-            const float pb = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[h] >> 16));
-#pragma unroll
-            for (int c = 0; c < DPL; ++c) {
-              const float fa = chunk_elem<DT>(make_uint4(wa[c / 2], 0, 0, 0), c & 1);
-              const float fb = chunk_elem<DT>(make_uint4(wb[c / 2], 0, 0, 0), c & 1);
-              acc[h][c] = __builtin_fmaf(pb, fb, __builtin_fmaf(pa, fa, acc[h][c]));
-            }
-          }
-        }
-      }
-      return true;
-    };
-    uint4 kr[PPT], vr[PPT];
-    fetch(t0, kr, vr);
-    for (int c0 = t0, ci = 0; c0 < t1; c0 += kChunk, ++ci)
-      if (!step(c0, ci, kr, vr)) return false;
-
-    // ---- merge: halves, then waves; statistics from the QK waves
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const float lt = wave_sum(l_lane[hh]);
-      if (lane == 0) {
-        sM[wave * HPW + hh] = m_ref[hh];
-        sL[wave * HPW + hh] = lt;
-      }
-    }
-    __syncthreads();  // last PV done: LDS tiles free for the merge
-    float* sAcc = reinterpret_cast<float*>(sKV);  // [waves][G][D]
-    if (half == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) sAcc[(wave * G + h) * D + dl * DPL + e] = acc[h][e];
-    }
-    __syncthreads();
-    const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
-    for (int i = tid; i < G * D; i += kDecodeThreads) {
-      const int h = i / D, d = i % D;
-      float o = 0.f;
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) o += sAcc[(w * G + h) * D + d];
-      emit(p, head0 + h, part, d, D, sM[h], sL[h], o, L <= p.partition_size);
-    }
-    return true;
-  };
-
-  if (!run(std::true_type{})) {
-    if constexpr (DT == PA_BF16) run(std::false_type{});
-  }
-}
 
 // --------------------------------------------------------------------- reduce
 // Split-K reduce ("V2" reduce): for one (sequence, head), M = max_p m_p and
@@ -698,46 +84,6 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   for (int c = 0; c < CPL; ++c) store_out(p.out, sh * D + lane * CPL + c, o[c] * inv, p.out_dtype);
 }
 
-// ------------------------------------------------------------------- dispatch
-template <pa_dtype DT, int D, bool OFF32>
-hipError_t launch_lds(const DecodeParams& p, int G, dim3 grid, hipStream_t st) {
-  dim3 block(kDecodeThreads);
-  switch (G) {
-    case 4: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 4, OFF32>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 8, OFF32>), grid, block, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 16, OFF32>), grid, block, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <pa_dtype DT, int D>
-hipError_t launch_g(const DecodeParams& p, int G, dim3 grid, hipStream_t st) {
-  dim3 block(kDecodeThreads);
-  if constexpr (DT != PA_F32) {
-    if (decode_uses_group_kernel(DT, G)) {
-      if (p.off32) return launch_lds<DT, D, true>(p, G, grid, st);
-      return launch_lds<DT, D, false>(p, G, grid, st);
-    }
-  }
-  switch (G) {
-    case 1: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 2>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 4>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 8>), grid, block, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((decode_reg_kernel<DT, D, 16>), grid, block, 0, st, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <pa_dtype DT>
-hipError_t launch_d(const DecodeParams& p, int D, int G, dim3 grid, hipStream_t st) {
-  if (D == 64) return launch_g<DT, 64>(p, G, grid, st);
-  if (D == 128) return launch_g<DT, 128>(p, G, grid, st);
-  return hipErrorInvalidValue;
-}
-
 DecodeParams make_params(const DecodeArgs& a) {
   const PoolGeom& g = a.geom;
   DecodeParams p{};
@@ -772,6 +118,7 @@ DecodeParams make_params(const DecodeArgs& a) {
 }
 
 }  // namespace
+}  // namespace dec
 
 bool decode_uses_group_kernel(pa_dtype kv_dtype, int G) {
   return kv_dtype != PA_F32 && (G == 4 || G == 8 || G == 16);
@@ -779,28 +126,25 @@ bool decode_uses_group_kernel(pa_dtype kv_dtype, int G) {
 
 hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
-  const DecodeParams p = make_params(a);
+  const dec::DecodeParams p = dec::make_params(a);
   const PoolGeom& g = a.geom;
   const int G = a.num_heads / g.num_kv_heads;
   dim3 grid((unsigned)(a.num_seqs * g.num_kv_heads), a.partition_size > 0 ? a.max_partitions : 1);
-  switch (a.kv_dtype) {
-    case PA_F32: return launch_d<PA_F32>(p, g.head_size, G, grid, stream);
-    case PA_BF16: return launch_d<PA_BF16>(p, g.head_size, G, grid, stream);
-    case PA_F16: return launch_d<PA_F16>(p, g.head_size, G, grid, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (decode_uses_group_kernel(a.kv_dtype, G))
+    return dec::launch_group(p, a.kv_dtype, g.head_size, G, grid, stream);
+  return dec::launch_head(p, a.kv_dtype, g.head_size, G, grid, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0 || a.partition_size <= 0) return hipSuccess;
-  const DecodeParams p = make_params(a);
+  const dec::DecodeParams p = dec::make_params(a);
   const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
-  constexpr int per_block = kReduceThreads / kWave;
+  constexpr int per_block = dec::kReduceThreads / kWave;
   dim3 rgrid((unsigned)((pairs + per_block - 1) / per_block));
   if (a.geom.head_size == 64)
-    hipLaunchKernelGGL(decode_reduce_kernel<64>, rgrid, dim3(kReduceThreads), 0, stream, p, pairs);
+    hipLaunchKernelGGL(dec::decode_reduce_kernel<64>, rgrid, dim3(dec::kReduceThreads), 0, stream, p, pairs);
   else if (a.geom.head_size == 128)
-    hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(kReduceThreads), 0, stream, p, pairs);
+    hipLaunchKernelGGL(dec::decode_reduce_kernel<128>, rgrid, dim3(dec::kReduceThreads), 0, stream, p, pairs);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -1,0 +1,86 @@
+// Shared definitions of the paged decode kernels (per-head and grouped
+// kernels, split-K reduce): launch parameters, wave reductions and the
+// partial/final output rule.  What is computed follows "PagedAttention 在
+// vLLM 中的实现分析" §3.1 (block block_table[t / block_size], offset
+// t % block_size) and §7.2-7.3 (per-block QK, softmax, V accumulation;
+// partitions merged by max/sum rescaling).
+#ifndef PA_DECODE_COMMON_H_
+#define PA_DECODE_COMMON_H_
+
+#include <hip/hip_runtime.h>
+
+#include "kernel_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace dec {
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = kDecodeWaves * kWave;
+constexpr float kLazyRescale = 8.f;  // log2 headroom before a running max moves
+
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+
+struct DecodeParams {
+  void* out;
+  const void* query;
+  const char* key_cache;
+  const char* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* part_out;
+  float* part_ml;
+  int64_t blk_stride;   // elements between blocks
+  int64_t tok_stride;   // elements between tokens of a block
+  int64_t head_stride;  // elements between kv heads
+  int32_t max_blocks_per_seq;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t log2_bs;
+  int32_t partition_size;  // 0 = single pass
+  int32_t max_partitions;
+  float scale_log2e;
+  pa_dtype out_dtype;
+  bool off32;  // every byte offset into either cache fits in 32 bits
+};
+
+// Maximum over the 64 lanes of a wave (every lane receives it).
+__device__ __forceinline__ float wave_max(float x) {
+  x = group_max<16>(x);
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Writes one (max, sum, unnormalised output) partial, or the final output
+// when the whole context is one partition (the reduce skips those heads).
+__device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int part, int d, int D,
+                                     float M, float lsum, float o, bool single) {
+  if (p.partition_size > 0 && !single) {
+    const int64_t pi = head * p.max_partitions + part;
+    p.part_out[pi * D + d] = o;
+    if (d == 0) {
+      p.part_ml[2 * pi] = M;
+      p.part_ml[2 * pi + 1] = lsum;
+    }
+  } else {
+    store_out(p.out, head * D + d, lsum > 0.f ? o / lsum : 0.f, p.out_dtype);
+  }
+}
+
+// Kernel launches of one decode pass; grid = (num_seqs * num_kv_heads,
+// partitions or 1).
+hipError_t launch_head(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st);
+hipError_t launch_group(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st);
+
+}  // namespace dec
+}  // namespace pa
+
+#endif  // PA_DECODE_COMMON_H_
