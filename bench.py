@@ -278,7 +278,10 @@ def cpu_baseline(w, budget_s: float, unit: str):
         t0 = time.perf_counter()
         kc, vc = A.write_ref(kc, vc, K, V, st.step_slots, w.bs)
         t_write = time.perf_counter() - t0
-        for s in range(w.S):
+        # whole sequences in order, passing over the batch again while the
+        # budget lasts (a short workload is timed over several passes)
+        order = [s for _ in range(1000) for s in range(w.S)]
+        for s in order:
             t0 = time.perf_counter()
             if w.kind == "decode":
                 A.decode_ref(w.query[s:s + 1], kc, vc, st.block_tables[s:s + 1], lens[s:s + 1],
@@ -296,11 +299,13 @@ def cpu_baseline(w, budget_s: float, unit: str):
                 break
     secs += t_write * len(done) / w.S
     value = work / secs / (1e9 if unit == "GB/s" else 1e12)
+    passes = len(done) / w.S
+    what = (f"{len(done)} of {w.S} sequences" if len(done) < w.S
+            else f"{passes:.2f} passes over the {w.S} sequences")
     return {"value": round(value, 6), "unit": unit, "cores": 1, "kind": "oracle",
             "seconds": round(secs, 2),
-            "sample": f"{len(done)} of {w.S} sequences of {w.name} (all heads): oracle {w.kind} "
-                      f"of those sequences + their share of the oracle write of the step rows; "
-                      f"pool built untimed"}
+            "sample": f"{what} of {w.name} (all heads): oracle {w.kind} of those sequences + "
+                      f"their share of the oracle write of the step rows; pool built untimed"}
 
 
 if __name__ == "__main__":
