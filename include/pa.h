@@ -199,6 +199,46 @@ pa_status pa_decode_reduce(void* out, pa_dtype out_dtype,
                            const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_cascade -- pa_decode for a batch whose sequences share their
+ * first common_prefix_len tokens in the same physical blocks ([vllm] §6.4
+ * cascade attention: the shared prefix is attended once, without a causal
+ * mask, each sequence's own tokens separately, and the parts are merged with
+ * the online-softmax rule of §7.3).
+ *
+ * Same result as pa_decode (same arguments and output).  Additionally:
+ *   common_prefix_len  tokens, a positive multiple of block_size, at most
+ *                      every context_lens[s]; block_tables[s][0 ..
+ *                      common_prefix_len / block_size - 1] must be the same
+ *                      blocks for every s (row 0's are read; not checked on
+ *                      the device)
+ *   partition_size     split of each sequence's own tokens [common_prefix_len,
+ *                      L): > 0 (a multiple of 16), 0 = one partition for the
+ *                      longest, -1 = chosen by the library
+ *   workspace          (device, 16-byte aligned) >=
+ *                      pa_decode_cascade_workspace_size(...) bytes; out must
+ *                      be 16-byte aligned
+ * The prefix pass runs on matrix cores: kv_dtype must be PA_BF16 or PA_F16
+ * (PA_ERR_UNSUPPORTED otherwise).  Three launches on `stream`: the prefix
+ * pass (all sequences' queries against the common blocks, in key
+ * partitions), the partitions of each sequence's own tokens, and the reduce.
+ */
+size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                        int32_t head_size, int32_t max_context_len,
+                                        int32_t common_prefix_len,
+                                        int32_t partition_size);
+
+pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void* query,
+                            const void* key_cache, const void* value_cache,
+                            pa_dtype kv_dtype, pa_layout layout,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len,
+                            int32_t common_prefix_len, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            int32_t block_size, int32_t num_blocks, float scale,
+                            int32_t partition_size, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill -- causal attention of packed query rows over the paged cache
  * ([vllm] §6.2 flash_attn_varlen_func with cu_seqlens_q = query_start_loc,
  * seqlen_k = seq_lens, block_table, causal = True; [packed] §2.3).

@@ -44,7 +44,7 @@ NHD, HND = 0, 1
 EXPORTED = [
     "pa_status_string", "pa_last_error", "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode", "pa_decode_partitions",
-    "pa_decode_reduce", "pa_prefill",
+    "pa_decode_reduce", "pa_decode_cascade_workspace_size", "pa_decode_cascade", "pa_prefill",
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
     "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
     "pa_pool_num_free", "pa_pool_refcount",
@@ -67,6 +67,9 @@ _sig = {
     "pa_decode_partitions": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_cascade_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_cascade": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "pa_check_metadata": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -212,6 +215,37 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, ma
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, H, hkv, d, bs,
         nb, float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_decode_cascade_workspace_size(num_seqs: int, num_heads: int, head_size: int,
+                                     max_context_len: int, common_prefix_len: int,
+                                     partition_size: int = -1) -> int:
+    return int(_lib.pa_decode_cascade_workspace_size(num_seqs, num_heads, head_size,
+                                                     max_context_len, common_prefix_len,
+                                                     partition_size))
+
+
+def pa_decode_cascade(out, query, key_cache, value_cache, block_tables, context_lens,
+                      max_context_len: int, common_prefix_len: int, scale: float, workspace,
+                      layout: int = NHD, partition_size: int = -1, stream=None) -> None:
+    """Decode with a shared prefix attended once (same result as pa_decode)."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    S, H, D = query.shape
+    if D != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_seqs, num_heads, head_size]")
+    if query.dtype != key_cache.dtype:
+        raise TypeError("query dtype must equal the cache dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables [S, max_blocks] and context_lens [S] required")
+    _check("pa_decode_cascade", _lib.pa_decode_cascade(
+        _dev(out, "out"), _dtype_code(out), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dtype_code(key_cache), layout,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len),
+        int(common_prefix_len), S, H, hkv, d, bs, nb, float(scale), int(partition_size),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
 
 
 def pa_decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens,

@@ -43,8 +43,8 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   const int lane = threadIdx.x % kWave;
   const int s = (int)(sh / p.num_heads);
   const int L = p.context_lens[s];
-  if (L <= p.partition_size) return;
-  const int np = (L + p.partition_size - 1) / p.partition_size;
+  if (single_partition(p, L)) return;
+  const int np = p.part_base + (L > p.key_begin ? (L - p.key_begin + p.partition_size - 1) / p.partition_size : 0);
   const float* ml = p.part_ml + sh * p.max_partitions * 2;
   const float* po = p.part_out + sh * p.max_partitions * D + lane * CPL;
 
@@ -110,6 +110,9 @@ DecodeParams make_params(const DecodeArgs& a) {
   p.log2_bs = g.block_size > 0 ? __builtin_ctz((unsigned)g.block_size) : 0;
   p.partition_size = a.partition_size;
   p.max_partitions = a.max_partitions;
+  p.key_begin = a.key_begin;
+  p.part_base = a.part_base;
+  p.all_partial = a.all_partial;
   p.scale_log2e = a.scale * kLog2e;
   p.out_dtype = a.out_dtype;
   const int64_t elem = a.kv_dtype == PA_F32 ? 4 : 2;
@@ -129,7 +132,9 @@ hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
   const dec::DecodeParams p = dec::make_params(a);
   const PoolGeom& g = a.geom;
   const int G = a.num_heads / g.num_kv_heads;
-  dim3 grid((unsigned)(a.num_seqs * g.num_kv_heads), a.partition_size > 0 ? a.max_partitions : 1);
+  dim3 grid((unsigned)(a.num_seqs * g.num_kv_heads),
+            a.partition_size > 0 ? a.max_partitions - a.part_base : 1);
+  if (grid.y == 0) return hipSuccess;
   if (decode_uses_group_kernel(a.kv_dtype, G))
     return dec::launch_group(p, a.kv_dtype, g.head_size, G, grid, stream);
   return dec::launch_head(p, a.kv_dtype, g.head_size, G, grid, stream);

@@ -38,7 +38,10 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t log2_bs;
   int32_t partition_size;  // 0 = single pass
-  int32_t max_partitions;
+  int32_t max_partitions;  // workspace partitions per (sequence, head)
+  int32_t key_begin;       // partitions cover keys [key_begin, L) (0 outside cascades)
+  int32_t part_base;       // workspace index of partition 0 (earlier slots hold prefix partials)
+  bool all_partial;        // never finish a head here: other partials exist
   float scale_log2e;
   pa_dtype out_dtype;
   bool off32;  // every byte offset into either cache fits in 32 bits
@@ -59,12 +62,18 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Whether a sequence of context L is finished by its single partition (the
+// reduce then skips it).
+__device__ __forceinline__ bool single_partition(const DecodeParams& p, int L) {
+  return !p.all_partial && L <= p.partition_size;
+}
+
 // Writes one (max, sum, unnormalised output) partial, or the final output
 // when the whole context is one partition (the reduce skips those heads).
 __device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int part, int d, int D,
                                      float M, float lsum, float o, bool single) {
   if (p.partition_size > 0 && !single) {
-    const int64_t pi = head * p.max_partitions + part;
+    const int64_t pi = head * p.max_partitions + p.part_base + part;
     p.part_out[pi * D + d] = o;
     if (d == 0) {
       p.part_ml[2 * pi] = M;

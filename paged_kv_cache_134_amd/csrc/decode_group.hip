@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
   const int L = p.context_lens[s];
   int t0 = 0, t1 = L;
   if (p.partition_size > 0) {
-    t0 = part * p.partition_size;
+    t0 = p.key_begin + part * p.partition_size;
     if (t0 >= L) return;
     t1 = min(L, t0 + p.partition_size);
   }
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
       float o = 0.f;
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) o += sAcc[(w * G + h) * D + d];
-      emit(p, head0 + h, part, d, D, sM[h], sL[h], o, L <= p.partition_size);
+      emit(p, head0 + h, part, d, D, sM[h], sL[h], o, single_partition(p, L));
     }
     return true;
   };

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
   const int L = p.context_lens[s];
   int t0 = 0, t1 = L;
   if (p.partition_size > 0) {
-    t0 = part * p.partition_size;
+    t0 = p.key_begin + part * p.partition_size;
     if (t0 >= L) return;  // partition past the end: the reduce ignores it
     t1 = min(L, t0 + p.partition_size);
   }
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
       lsum += a * sm_l[w][g];
       o += a * sm_acc[w][g][d];
     }
-    emit(p, head0 + g, part, d, D, M, lsum, o, L <= p.partition_size);
+    emit(p, head0 + g, part, d, D, M, lsum, o, single_partition(p, L));
   }
 }
 

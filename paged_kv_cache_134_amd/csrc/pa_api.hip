@@ -2,6 +2,7 @@
 // Everything here runs on the host; device work is only enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -314,6 +315,126 @@ extern "C" pa_status pa_decode_reduce(void* out, pa_dtype out_dtype, const int32
   if (st != PA_OK || num_seqs == 0 || a.partition_size == 0) return st;
   hipError_t e = pa::launch_decode_reduce(a, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode_reduce");
+}
+
+// ---------------------------------------------------------------- cascade
+namespace {
+
+// Shared-prefix pass: key partitions sized so that (heads x query tiles x
+// partitions) is about 512 workgroups, in multiples of 64 keys.
+int32_t cascade_key_part(int32_t num_seqs, int32_t num_heads, int32_t prefix) {
+  const int64_t qt = (num_seqs + 127) / 128;
+  const int64_t per = (int64_t)num_heads * qt;
+  const int64_t parts = std::max<int64_t>(1, (512 + per - 1) / per);
+  const int64_t kp = (prefix + parts - 1) / parts;
+  return (int32_t)std::max<int64_t>(64, (kp + 63) / 64 * 64);
+}
+
+int64_t cascade_suffix_parts(int32_t max_context_len, int32_t prefix, int32_t ps) {
+  return max_context_len > prefix ? (max_context_len - prefix + (int64_t)ps - 1) / ps : 0;
+}
+
+}  // namespace
+
+extern "C" size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                                   int32_t head_size, int32_t max_context_len,
+                                                   int32_t common_prefix_len,
+                                                   int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || common_prefix_len <= 0 ||
+      max_context_len < common_prefix_len || partition_size < -1)
+    return 0;
+  const int32_t kp = cascade_key_part(num_seqs, num_heads, common_prefix_len);
+  const int64_t npp = (common_prefix_len + kp - 1) / kp;
+  const int32_t suffix = max_context_len - common_prefix_len;
+  const int32_t ps = partition_size > 0 ? partition_size
+                     : partition_size < 0 ? kAutoSmallestPartition
+                                          : std::max(16, (suffix + 15) / 16 * 16);
+  return workspace_bytes(num_seqs, num_heads, head_size,
+                         npp + cascade_suffix_parts(max_context_len, common_prefix_len, ps));
+}
+
+extern "C" pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void* query,
+                                       const void* key_cache, const void* value_cache,
+                                       pa_dtype kv_dtype, pa_layout layout,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t common_prefix_len, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t num_blocks, float scale,
+                                       int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes_, void* stream) {
+  const char* fn = "pa_decode_cascade";
+  pa::DecodeArgs a;
+  pa_status st = decode_prepare(fn, out, out_dtype, query, key_cache, value_cache, kv_dtype, layout,
+                                block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                                num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                                num_blocks, scale, 0, nullptr, 0, true, true, &a);
+  if (st != PA_OK) return st;
+  if (kv_dtype != PA_BF16 && kv_dtype != PA_F16)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: the shared-prefix pass needs bf16 or f16 caches");
+  if (common_prefix_len <= 0 || common_prefix_len % block_size != 0 ||
+      common_prefix_len > max_context_len)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT,
+                   "pa_decode_cascade: common_prefix_len must be a positive multiple of block_size "
+                   "and at most max_context_len");
+  if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT,
+                   "pa_decode_cascade: partition_size must be -1, 0 or a positive multiple of 16");
+  if (num_seqs == 0) return PA_OK;
+  const int32_t suffix = max_context_len - common_prefix_len;
+  int32_t ps = partition_size > 0 ? partition_size
+               : partition_size < 0 ? pa_decode_auto_partition(num_seqs, num_heads, num_kv_heads,
+                                                              kv_dtype, suffix, 0)
+                                    : 0;
+  if (ps <= 0) ps = std::max(16, (suffix + 15) / 16 * 16);  // one partition per suffix
+  const int32_t kp = cascade_key_part(num_seqs, num_heads, common_prefix_len);
+  const int64_t npp = (common_prefix_len + kp - 1) / kp;
+  const int64_t parts = npp + cascade_suffix_parts(max_context_len, common_prefix_len, ps);
+  if (parts > 65535) return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: more than 65535 partitions");
+  const size_t need = workspace_bytes(num_seqs, num_heads, head_size, parts);
+  if (!workspace || workspace_bytes_ < need) {
+    char msg[200];
+    std::snprintf(msg, sizeof msg, "%s: needs %zu workspace bytes, got %zu", fn, need,
+                  workspace ? workspace_bytes_ : (size_t)0);
+    return pa_fail(PA_ERR_WORKSPACE_TOO_SMALL, msg);
+  }
+  if (!aligned16(workspace) || !aligned16(out))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_cascade: workspace and out must be 16-byte aligned");
+  const size_t out_b = (size_t)num_seqs * num_heads * parts * head_size * sizeof(float);
+  a.partition_size = ps;
+  a.max_partitions = (int32_t)parts;
+  a.part_out = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((out_b + 255) / 256) * 256);
+  a.key_begin = common_prefix_len;
+  a.part_base = (int32_t)npp;
+  a.all_partial = true;
+
+  // 1. shared prefix: every sequence's query against the common blocks
+  //    (block_tables row 0), once, on matrix cores
+  pa::PrefillArgs pr{};
+  pr.query = query;
+  pr.key_cache = key_cache;
+  pr.value_cache = value_cache;
+  pr.kv_dtype = kv_dtype;
+  pr.out_dtype = PA_F32;
+  pr.block_tables = block_tables;
+  pr.max_blocks_per_seq = max_blocks_per_seq;
+  pr.num_seqs = 1;
+  pr.num_tokens = num_seqs;
+  pr.max_query_len = 1;
+  pr.num_heads = num_heads;
+  pr.geom = a.geom;
+  pr.scale = scale;
+  pr.prefix_keys = common_prefix_len;
+  pr.key_part = kp;
+  pr.part_out = a.part_out;
+  pr.part_ml = a.part_ml;
+  pr.max_partitions = (int32_t)parts;
+  hipError_t e = pa::launch_prefill(pr, (hipStream_t)stream);
+  // 2. each sequence's own keys [common_prefix_len, L), 3. merge of all partials
+  if (e == hipSuccess) e = pa::launch_decode_main(a, (hipStream_t)stream);
+  if (e == hipSuccess) e = pa::launch_decode_reduce(a, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, fn);
 }
 
 // ---------------------------------------------------------------- prefill

@@ -51,6 +51,9 @@ struct DecodeArgs {
   int32_t max_partitions;  // ceil(max_context_len / partition_size) when split
   float* part_out;         // [num_seqs, num_heads, max_partitions, head_size]
   float* part_ml;          // [num_seqs, num_heads, max_partitions, 2] (max, sum)
+  int32_t key_begin = 0;   // cascade: partitions cover [key_begin, L) ...
+  int32_t part_base = 0;   // ... and start at this workspace partition
+  bool all_partial = false;  // cascade: prefix partials exist, never finish a head early
 };
 
 // Single pass (partition_size == 0) or the split-K partition kernel.
@@ -79,6 +82,16 @@ struct PrefillArgs {
   int32_t num_heads;
   PoolGeom geom;
   float scale;
+  // Shared-prefix mode (prefix_keys > 0): the num_tokens query rows attend,
+  // without a causal mask, to keys [0, prefix_keys) through block_tables
+  // row 0, in key partitions of key_part tokens; each (row, head, partition)
+  // writes a (max, sum, unnormalised output) partial at workspace partition
+  // index = key partition.
+  int32_t prefix_keys = 0;
+  int32_t key_part = 0;
+  float* part_out = nullptr;
+  float* part_ml = nullptr;
+  int32_t max_partitions = 0;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -76,7 +76,16 @@ struct PrefillParams {
   float scale_log2e;
   pa_dtype out_dtype;
   int32_t q_tiles;   // query tiles per sequence (of the longest)
-  int32_t num_work;  // (sequence, head) pairs: num_heads * num_seqs
+  int32_t num_work;  // (sequence, head) pairs: num_heads * num_seqs (prefix mode: (head, key part))
+  // shared-prefix mode: rows 0 .. num_rows-1 attend to keys [0, prefix_keys)
+  // of block_tables row 0 in key_parts partitions of key_part keys
+  int32_t num_rows;
+  int32_t prefix_keys;
+  int32_t key_part;
+  int32_t key_parts;
+  float* part_out;
+  float* part_ml;
+  int32_t max_partitions;
 };
 
 
@@ -97,8 +106,11 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
 }
 
 // D = head size.  OFF32: both caches span less than 4 GiB, so rows are
-// addressed by 32-bit byte offsets from the cache base.
-template <pa_dtype DT, int D, bool OFF32>
+// addressed by 32-bit byte offsets from the cache base.  PREFIX: the
+// shared-prefix pass of a cascade -- every query row sees every key of its
+// key partition (no causal mask) and writes a (max, sum, unnormalised
+// output) partial instead of a normalised row.
+template <pa_dtype DT, int D, bool OFF32, bool PREFIX>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillParams p) {
   constexpr int KS = D / 16;                    // 16-wide k-steps over the head dim (QK)
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
@@ -126,15 +138,27 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   const int pair = (local / p.q_tiles) * 8 + b % 8;
   if (pair >= p.num_work) return;  // num_work counts (sequence, head) pairs
   const int qt = local % p.q_tiles;
-  const int num_seqs = p.num_work / p.num_heads;
-  const int h = pair / num_seqs;
-  const int s = pair % num_seqs;
-
-  const int q_begin = p.query_start_loc[s];
-  const int n = p.query_start_loc[s + 1] - q_begin;
+  int h, s, q_begin, n, L, k_lo;
+  if constexpr (PREFIX) {
+    // pairs (head, key part); all rows form one batch, keys [k_lo, k_lo + key_part)
+    h = pair / p.key_parts;
+    const int kp = pair % p.key_parts;
+    s = kp;  // block-table row 0 is used; s names the key partition below
+    q_begin = 0;
+    n = p.num_rows;
+    k_lo = kp * p.key_part;
+    L = min(p.prefix_keys, k_lo + p.key_part);
+  } else {
+    const int num_seqs = p.num_work / p.num_heads;
+    h = pair / num_seqs;
+    s = pair % num_seqs;
+    q_begin = p.query_start_loc[s];
+    n = p.query_start_loc[s + 1] - q_begin;
+    L = p.context_lens[s];
+    k_lo = 0;
+  }
   const int q0 = qt * kBM;
   if (q0 >= n) return;
-  const int L = p.context_lens[s];
   const int kvh = h / (p.num_heads / p.num_kv_heads);
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -142,13 +166,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   const int lq = lane % 32;     // query (column) owned by this lane
   const int hf = lane / 32;     // half: k-slice 8 hf .. +7, rows 4 hf .. +3 of each 8
 
-  // keys visible to the workgroup: 0 .. kend-1
+  // keys visible to the workgroup: k_lo .. kend-1 (prefix mode: all of the
+  // partition for every row)
   const int last_row = min(n, q0 + kBM) - 1;
-  const int kend = L - n + last_row + 1;
+  const int kend = PREFIX ? L : L - n + last_row + 1;
 
   // Q^T fragments (B operand): query row j, head-dim slice ks*16 + 8 hf .. +7
   const int j = q0 + wave * kQW + lq;
-  const int lim = L - n + j;  // last visible key of this lane's query
+  const int lim = PREFIX ? L - 1 : L - n + j;  // last visible key of this lane's query
   uint4 qf[KS];
   {
     const bool ok = j < n;
@@ -166,7 +191,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+  const int32_t* bt = p.block_tables + (PREFIX ? 0 : (int64_t)s * p.max_blocks_per_seq);
   const int lbs = p.log2_bs;
   const int bs_mask = (1 << lbs) - 1;
   const int64_t head_off = (int64_t)kvh * p.head_stride;
@@ -185,7 +210,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   // wb0 + kBtWinP - 1, clamped to the last entry the workgroup reads), so no
   // tile load waits on another global load.
   const int e_last = (kend - 1) >> lbs;
-  int wb0 = 0;
+  int wb0 = k_lo >> lbs;
   auto stage_bt = [&]() {
     for (int i = tid; i < kBtWinP; i += kPrefillThreads) s_bt[i] = bt[min(wb0 + i, e_last)];
   };
@@ -230,14 +255,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   // smallest and largest visible-key limits among this wave's query rows; a
   // wave whose rows are all padding, or that sees none of a tile's keys,
   // skips that tile's products (it still stages K/V and meets the barriers)
-  const int lim_min = L - n + q0 + wave * kQW;
-  const int lim_max = L - n + min(n - 1, q0 + wave * kQW + kQW - 1);
+  const int lim_min = PREFIX ? L - 1 : L - n + q0 + wave * kQW;
+  const int lim_max = PREFIX ? L - 1 : L - n + min(n - 1, q0 + wave * kQW + kQW - 1);
   const bool wave_rows = q0 + wave * kQW < n;
   const float c = p.scale_log2e;
   const uint32_t ones = pk_f16(1.f, 1.f);
 
-  TileRegs tr = fetch(0);
-  for (int k0 = 0; k0 < kend; k0 += kBN) {
+  TileRegs tr = fetch(k_lo);
+  for (int k0 = k_lo; k0 < kend; k0 += kBN) {
     // ---- registers -> LDS: K row-major, V transposed to [d][key] in f16
 #pragma unroll
     for (int i = 0; i < KPT; ++i) store16(sK + k_row * KROW + (k_cg + i) * 16, tr.k[i]);
@@ -313,9 +338,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= a;
     }
-    // p = 2^(c z - m), rounded to f16 (key 0 is visible to every query, so m
-    // is finite here and masked scores give exp2(-inf) = 0); the normaliser
-    // sums the rounded values
+    // p = 2^(c z - m), rounded to f16 (the first key of the range is visible
+    // to every query, so m is finite here and masked scores give exp2(-inf)
+    // = 0); the normaliser sums the rounded values
     const float nm = -m;
     uint32_t pp[2][8];
 #pragma unroll
@@ -354,6 +379,25 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 
   // ---- normalise and store: lane holds O[query lq][d = 32 db + 8 g + 4 hf + i]
   const float lt = l + __shfl_xor(l, 32);
+  if constexpr (PREFIX) {
+    // partial of (row j, head h, key partition s)
+    if (j < n) {
+      const int64_t pi = ((int64_t)j * p.num_heads + h) * p.max_partitions + s;
+      float* po = p.part_out + pi * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store16(po + db * 32 + 8 * g + 4 * hf,
+                  make_uint4(__float_as_uint(o[db][4 * g]), __float_as_uint(o[db][4 * g + 1]),
+                             __float_as_uint(o[db][4 * g + 2]), __float_as_uint(o[db][4 * g + 3])));
+      if (hf == 0) {
+        p.part_ml[2 * pi] = m;
+        p.part_ml[2 * pi + 1] = lt;
+      }
+    }
+    return;
+  }
   if (j < n) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int64_t row = ((int64_t)(q_begin + j) * p.num_heads + h) * D;
@@ -383,16 +427,24 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 
 template <pa_dtype DT, int D>
 hipError_t launch_pd(PrefillParams p, int num_seqs, int max_q, bool off32, hipStream_t st) {
-  p.q_tiles = (max_q + kBM - 1) / kBM;
-  const int64_t pairs = (int64_t)p.num_heads * num_seqs;
+  const bool prefix = p.prefix_keys > 0;
+  p.q_tiles = ((prefix ? p.num_rows : max_q) + kBM - 1) / kBM;
+  const int64_t pairs = (int64_t)p.num_heads * (prefix ? p.key_parts : num_seqs);
   const int64_t blocks = (pairs + 7) / 8 * 8 * p.q_tiles;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   p.num_work = (int)pairs;
   dim3 grid((unsigned)blocks), block(kPrefillThreads);
-  if (off32)
-    hipLaunchKernelGGL((prefill_kernel<DT, D, true>), grid, block, 0, st, p);
-  else
-    hipLaunchKernelGGL((prefill_kernel<DT, D, false>), grid, block, 0, st, p);
+  if (prefix) {
+    if (off32)
+      hipLaunchKernelGGL((prefill_kernel<DT, D, true, true>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<DT, D, false, true>), grid, block, 0, st, p);
+  } else {
+    if (off32)
+      hipLaunchKernelGGL((prefill_kernel<DT, D, true, false>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<DT, D, false, false>), grid, block, 0, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -424,6 +476,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.log2_bs = __builtin_ctz((unsigned)g.block_size);
   p.scale_log2e = a.scale * kLog2e;
   p.out_dtype = a.out_dtype;
+  p.num_rows = a.num_tokens;
+  p.prefix_keys = a.prefix_keys;
+  p.key_part = a.key_part;
+  p.key_parts = a.prefix_keys > 0 ? (a.prefix_keys + a.key_part - 1) / a.key_part : 0;
+  p.part_out = a.part_out;
+  p.part_ml = a.part_ml;
+  p.max_partitions = a.max_partitions;
   const bool off32 = (int64_t)g.num_blocks * p.blk_stride * 2 <= (int64_t)UINT32_MAX;
   if (a.kv_dtype == PA_BF16) {
     if (g.head_size == 64) return launch_pd<PA_BF16, 64>(p, a.num_seqs, a.max_query_len, off32, stream);

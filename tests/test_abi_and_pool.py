@@ -84,6 +84,30 @@ def test_argument_errors_enqueue_nothing():
                                     ctypes.c_void_p(256), 3, 8, 128, 16, 4, 1, 0, None) == 1
 
 
+def test_cascade_argument_errors_and_workspace():
+    """pa_decode_cascade's host checks (no device needed)."""
+    lib = P._lib
+    v = ctypes.c_void_p(256)
+    args = lambda dt, prefix, ws, wsb, ps=-1: (v, 0, v, v, v, dt, 0, v, 200, v, 3000, prefix, 100,  # noqa
+                                                32, 32, 128, 256, 300, 1.0, ps, ws, wsb, None)
+    # every call below fails its host checks before anything is launched
+    need = P.pa_decode_cascade_workspace_size(100, 32, 128, 3000, 1792, -1)
+    n256 = P.pa_decode_cascade_workspace_size(100, 32, 128, 3000, 1792, 256)
+    assert need > 0 and n256 > 0
+    assert lib.pa_decode_cascade(*args(0, 1792, v, need)) == 2      # fp32: no matrix-core pass
+    assert lib.pa_decode_cascade(*args(1, 1800, v, need)) == 1      # prefix not block-aligned
+    assert lib.pa_decode_cascade(*args(1, 3072, v, need)) == 1      # prefix beyond the contexts
+    assert lib.pa_decode_cascade(*args(1, 1792, v, n256 - 16, 256)) == 3  # workspace too small
+    assert lib.pa_decode_cascade(*args(1, 1792, None, 0)) == 3
+    assert lib.pa_decode_cascade(*args(1, 1792, v, need, 24)) == 1   # partition not a multiple of 16
+    # the workspace for -1 covers every explicit partition size the library may pick
+    for ps in (0, 256, 512, 1024):
+        assert P.pa_decode_cascade_workspace_size(100, 32, 128, 3000, 1792, ps) <= need
+    # prefix partials + suffix partials, (D + 2) floats each
+    assert need >= 100 * 32 * (128 + 2) * 4 * 2
+    assert P.pa_decode_cascade_workspace_size(100, 32, 128, 1000, 1792, -1) == 0
+
+
 def test_workspace_size():
     ws = P.pa_decode_workspace_size(8, 64, 128, 131072, 512)
     parts = 256

@@ -120,3 +120,35 @@ def test_prefill_full_size_sampled(cfg):
                 worst = max(worst, float(np.max(np.abs(got[r, h] - ref))))
     announce("max-abs", worst)
     assert worst <= TOL[w.dtype]
+
+
+def test_cascade_decode_full_size_sampled():
+    """The shared-prefix workload through the cascade path (common prefix =
+    its fully shared blocks), sampled against the plain definition."""
+    need_gpu()
+    w = workloads.make("5a")
+    announce("full-size cascade decode", w.name)
+    dw = M.setup(w, write_step=True)
+    st = build_state(w)
+    common = (w.prefix_len // w.bs) * w.bs
+    nbc = common // w.bs
+    assert np.all(st.block_tables[:, :nbc] == st.block_tables[0, :nbc])
+    ws = torch.empty(P.pa_decode_cascade_workspace_size(w.S, w.H, w.D, dw.max_context_len, common, -1),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+    P.pa_decode_cascade(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                        dw.context_lens, dw.max_context_len, common, w.scale, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    qf = A.bits_to_f64(w.query, w.dtype)
+    worst = 0.0
+    for s in sorted({0, w.S // 2, w.S - 1}):
+        K, V = w.kv(s)
+        for h in sorted({0, w.H // 2, w.H - 1}):
+            g = h // w.G
+            ref, _ = A.attention_dense(qf[s, h], A.bits_to_f64(K[:, g], w.dtype),
+                                       A.bits_to_f64(V[:, g], w.dtype), w.scale)
+            worst = max(worst, float(np.max(np.abs(got[s, h] - ref))))
+    announce("max-abs", worst)
+    assert worst <= TOL[w.dtype]

@@ -260,3 +260,44 @@ def test_decode_bf16_values_beyond_f16_range():
                 err = float(np.max(np.abs(got[s, h] - ref)))
                 assert err <= tol, (part, s, h, err, tol)
         announce("partition", part, "ok")
+
+
+def _cascade(dw, common, part):
+    w = dw.w
+    out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+    nbytes = P.pa_decode_cascade_workspace_size(w.S, w.H, w.D, dw.max_context_len, common, part)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    P.pa_decode_cascade(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                        dw.context_lens, dw.max_context_len, common, w.scale, ws,
+                        layout=dw.layout, partition_size=part)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("layout", [P.NHD, P.HND])
+@pytest.mark.parametrize("name,over", [
+    ("mha", dict(S=5, H=4, Hkv=4, prefix=600, suffix_lo=20, suffix_hi=90)),
+    ("gqa", dict(S=6, H=16, Hkv=2, prefix=700, suffix_lo=1, suffix_hi=300)),
+    ("bs16", dict(S=4, H=8, Hkv=8, bs=16, prefix=100, suffix_lo=5, suffix_hi=40)),
+])
+def test_cascade_decode_small(name, over, layout):
+    """Shared-prefix (cascade) decode: the common full blocks attended once for
+    every sequence, each sequence's own tokens separately, merged; equal to the
+    plain definition over the whole context."""
+    need_gpu()
+    w = workloads.make("5a", **over)
+    announce("cascade decode", name, "layout", layout)
+    dw = M.setup(w, layout=layout, write_step=True)
+    st = build_state(w)
+    common = (w.prefix_len // w.bs) * w.bs
+    nbc = common // w.bs
+    assert common > 0 and np.all(st.block_tables[:, :nbc] == st.block_tables[0, :nbc])
+    kc, vc = build_pool(w, st, layout=layout, include_step=True)
+    ref = A.decode_ref(w.query, kc, vc, st.block_tables, w.context_lens, w.scale, w.bs, w.dtype,
+                       layout)
+    for part in (-1, 0, 64):
+        got = _cascade(dw, common, part)
+        assert np.all(np.isfinite(got))
+        err, where = max_abs(got, ref)
+        announce("partition", part, "max-abs", err)
+        assert err <= TOL[w.dtype], (name, part, err, where)
