@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="2", help="workload: 1, 2, 3, 4, 5a, 5b, 5c")
     ap.add_argument("--layout", choices=["nhd", "hnd"], default="nhd")
+    ap.add_argument("--cascade", action="store_true",
+                    help="shared-prefix decode workloads: attend the common blocks once "
+                         "(pa_decode_cascade)")
     ap.add_argument("--partition", type=int, default=-1,
                     help="decode partition size (-1 auto, 0 single pass)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -118,7 +121,32 @@ def main():
     out = torch.empty(w.query_shape, dtype=torch.float32, device="cuda")
     kinds = []
 
-    if w.kind == "decode":
+    cascade = None
+    if args.cascade:
+        if w.kind != "decode" or w.prefix_len < w.bs:
+            raise SystemExit("--cascade needs a decode workload with a shared prefix (5a)")
+        common = (w.prefix_len // w.bs) * w.bs  # the fully shared blocks
+        # unique bytes the method must read: the common blocks once, then each
+        # sequence's own tokens
+        unique = (common + int((lens - common).sum())) * Hkv * D * 2 * eb
+        cascade = {"common_prefix_len": common, "unique_kv_bytes_per_step": unique}
+        ps = args.partition if args.partition >= 0 else -1
+        ws = torch.empty(P.pa_decode_cascade_workspace_size(S, H, D, dw.max_context_len, common, ps),
+                         dtype=torch.uint8, device="cuda")
+
+        def step(ev):
+            ev[0].record(stream)
+            M.write_step_rows(dw)
+            ev[1].record(stream)
+            P.pa_decode_cascade(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                dw.context_lens, dw.max_context_len, common, w.scale, ws,
+                                layout=layout, partition_size=ps)
+            ev[2].record(stream)
+            ev[3].record(stream)
+        kinds = ["reshape_and_cache", "decode_cascade", None]
+        dominant = 1
+        work_units = S
+    elif w.kind == "decode":
         ps = args.partition if args.partition >= 0 else P.pa_decode_auto_partition(
             S, H, Hkv, P.KV_DTYPE[w.dtype],
             dw.max_context_len, int(lens.sum()))
@@ -216,7 +244,9 @@ def main():
         value = kv_bytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
         dom_ms = kern_ms[dominant]
-        achieved = kv_bytes / (dom_ms * 1e-3) / 1e9
+        # the cascade's roofline counts the bytes it must read (common blocks
+        # once); the value keeps the logical KV bytes of the plain method
+        achieved = (cascade["unique_kv_bytes_per_step"] if cascade else kv_bytes) / (dom_ms * 1e-3) / 1e9
         kind_src = decode_kernel_kind(w)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
@@ -244,7 +274,8 @@ def main():
         "config": {"workload": w.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
                    "head_size": D, "block_size": w.bs, "layout": args.layout.upper(),
                    "context_tokens": int(lens.sum()), "write_rows": w.T,
-                   "partition_size": ps, "seed": w.seed},
+                   "partition_size": ps, "seed": w.seed,
+                   **({"path": "cascade", **cascade} if cascade else {})},
         "tokens_per_s": round(work_units / (ms_per_step * 1e-3), 1),
         "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4) if unit == "GB/s" else None,
         "kernels_us": kernels_us,
