@@ -55,7 +55,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed warm-up steps; -1 (default): as many as fill 0.3 s (at least 5), "
+                         "so clocks have settled before the timed steps")
     ap.add_argument("--config", default="2", help="workload: 1, 2, 3, 4, 5a, 5b, 5c")
     ap.add_argument("--layout", choices=["nhd", "hnd"], default="nhd")
     ap.add_argument("--cascade", action="store_true",
@@ -200,9 +202,17 @@ def main():
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
-    for _ in range(args.warmup):
-        step(events())
-    torch.cuda.synchronize()
+    if args.warmup >= 0:
+        for _ in range(args.warmup):
+            step(events())
+        torch.cuda.synchronize()
+    else:
+        args.warmup, t_w = 0, time.perf_counter()
+        while args.warmup < 5 or time.perf_counter() - t_w < 0.3:
+            for _ in range(5):
+                step(events())
+            torch.cuda.synchronize()
+            args.warmup += 5
     evs = [events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
