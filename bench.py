@@ -275,6 +275,7 @@ def main():
     roof["kernel_source_sha"] = source_sha(kind_src)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds, unit)
+    pcache = prefix_cache_probe(w, P) if w.prefix_len >= w.bs else None
 
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
@@ -291,10 +292,30 @@ def main():
         "kernels_us": kernels_us,
         **alg,
         "parity": parity,
+        **({"prefix_cache": pcache} if pcache else {}),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def prefix_cache_probe(w, P):
+    """Host prefix cache on the workload's prompts: every sequence's prompt
+    (shared prefix tokens, then its own) through pa_pool_add_seq_cached on a
+    fresh pool.  Token ids are seeded draws; timed: the adds only."""
+    import numpy as np
+    rng = np.random.default_rng([w.seed, 99])
+    prefix = rng.integers(0, 32000, w.prefix_len).astype(np.int32)
+    prompts = [np.concatenate([prefix, rng.integers(0, 32000, int(L) - w.prefix_len).astype(np.int32)])
+               for L in w.context_lens]
+    nb = 2 * sum(-(-int(L) // w.bs) for L in w.context_lens)
+    pool = P.BlockPool(nb, w.bs)
+    t0 = time.perf_counter()
+    hits = [pool.add_seq_cached(t)[1] for t in prompts]
+    us = (time.perf_counter() - t0) * 1e6 / len(prompts)
+    return {"sequences": len(prompts), "prompt_tokens": int(sum(len(t) for t in prompts)),
+            "cached_tokens": int(sum(hits)), "cached_blocks": pool.num_cached(),
+            "host_us_per_sequence": round(us, 2)}
 
 
 def cpu_baseline(w, budget_s: float, unit: str):

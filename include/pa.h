@@ -310,6 +310,31 @@ pa_status pa_pool_add_seq(pa_pool* pool, int32_t* seq_id);
 pa_status pa_pool_fork(pa_pool* pool, int32_t parent, int32_t* child);
 
 /*
+ * Prefix cache ([k4i] #prefix-caching; [vllm] §4.2 allocation steps 1-5 and
+ * §4.3 chained block hash).  New sequence holding a prompt of num_tokens
+ * token ids (host int32): its full blocks are hashed in a chain
+ * hash(parent hash, block's token ids, extra_key) and looked up from the
+ * left; every cached block up to the first miss is reused (count + 1; a
+ * block whose count was 0 leaves the free queue), the remaining blocks are
+ * taken from the front of the free queue and the fresh full blocks are
+ * registered (their K/V is the caller's to write, e.g. by prefill of the
+ * uncached tokens).  *cached_tokens = reused blocks x block_size: the
+ * caller skips attention/K-V computation for those positions.  extra_key
+ * separates caches of different configurations (adapter, salt).  A block
+ * freed to count 0 stays cached at the back of the queue; its entry is
+ * dropped when the queue hands it out for new content (least recently
+ * freed first).  Partial last blocks and blocks filled later by
+ * pa_pool_append are not cached.  Hash matches are confirmed against the
+ * stored token ids, so a collision is a miss.  All-or-nothing:
+ * PA_ERR_OUT_OF_BLOCKS with no change when the queue is too short.
+ */
+pa_status pa_pool_add_seq_cached(pa_pool* pool, const int32_t* token_ids,
+                                 int32_t num_tokens, uint64_t extra_key,
+                                 int32_t* seq_id, int32_t* cached_tokens);
+/* Number of blocks currently registered in the prefix cache. */
+int32_t pa_pool_num_cached(const pa_pool* pool);
+
+/*
  * Append n tokens to a sequence.  slots_out (host, int64 [n], may be NULL)
  * receives block * block_size + offset of each new position.  When the first
  * new token lands in a partly filled block shared with other sequences, the

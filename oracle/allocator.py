@@ -20,6 +20,18 @@ Semantics, from the pages:
   count of one the write goes in place ([k4i] #cow steps 1-5; [atb]
   copy-on-write section).
 
+* prefix cache ([k4i] #prefix-caching; [vllm] §4.2-4.3): a full block is
+  known by the chain (parent block's key, its token ids, an extra key); a
+  new prompt reuses the cached blocks of its full blocks from the left up to
+  the first miss (count + 1), takes fresh blocks for the rest and registers
+  the keys of the fresh full blocks.  Reading taken where the pages differ:
+  a block whose count drops to zero keeps its key and goes to the back of
+  the queue (so the queue's remove-from-the-middle serves hits on it and its
+  front-first hand-out is the least-recently-freed eviction of §4.1); the
+  key is dropped when the queue hands the block out for new content.  The
+  chain here is the exact nested tuple, so this model has no hash
+  collisions.
+
 Allocation is all-or-nothing: when the queue holds fewer blocks than an
 append needs, ``OutOfBlocks`` is raised and no state changes.
 """
@@ -44,6 +56,8 @@ class BlockManagerModel:
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
         self._next = 0
+        self.cache: Dict[tuple, int] = {}       # chain key -> block
+        self.block_key: Dict[int, tuple] = {}   # cached block -> its chain key
 
     # ---------------------------------------------------------------- seqs
     def add_seq(self) -> int:
@@ -57,7 +71,46 @@ class BlockManagerModel:
         b = self.free.popleft()
         assert self.ref[b] == 0
         self.ref[b] = 1
+        key = self.block_key.pop(b, None)  # new content: the cached key goes
+        if key is not None and self.cache.get(key) == b:
+            del self.cache[key]
         return b
+
+    def add_seq_cached(self, tokens, extra: int = 0) -> Tuple[int, int]:
+        """New sequence holding the prompt ``tokens`` with the prefix cache.
+
+        Returns (sequence id, tokens covered by reused blocks)."""
+        bs = self.block_size
+        tokens = [int(t) for t in tokens]
+        nfull, nblocks = len(tokens) // bs, -(-len(tokens) // bs)
+        keys, hits, parent = [], [], None
+        for i in range(nfull):
+            key = (parent, tuple(tokens[i * bs:(i + 1) * bs]), int(extra))
+            keys.append(key)
+            if len(hits) == i and key in self.cache:
+                hits.append(self.cache[key])
+            parent = key
+        revived = sum(1 for b in hits if self.ref[b] == 0)
+        if nblocks - len(hits) + revived > len(self.free):
+            raise OutOfBlocks(f"prompt of {len(tokens)}: free {len(self.free)}")
+        sid = self.add_seq()
+        tab = self.tables[sid]
+        for b in hits:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+            tab.append(b)
+        for i in range(len(hits), nblocks):
+            b = self._take()
+            tab.append(b)
+            if i < nfull:
+                old = self.cache.get(keys[i])
+                if old is not None and old != b:
+                    self.block_key.pop(old, None)
+                self.cache[keys[i]] = b
+                self.block_key[b] = keys[i]
+        self.lens[sid] = len(tokens)
+        return sid, len(hits) * bs
 
     def blocks_needed(self, sid: int, n: int) -> int:
         """Free blocks an append of n tokens consumes (new blocks + copy-on-write)."""
@@ -116,3 +169,6 @@ class BlockManagerModel:
 
     def num_free(self) -> int:
         return len(self.free)
+
+    def num_cached(self) -> int:
+        return len(self.cache)

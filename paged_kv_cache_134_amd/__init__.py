@@ -47,7 +47,7 @@ EXPORTED = [
     "pa_decode_reduce", "pa_decode_cascade_workspace_size", "pa_decode_cascade", "pa_prefill",
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
     "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
-    "pa_pool_num_free", "pa_pool_refcount",
+    "pa_pool_num_free", "pa_pool_refcount", "pa_pool_add_seq_cached", "pa_pool_num_cached",
 ]
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -77,6 +77,8 @@ _sig = {
     "pa_pool_destroy": (None, [_vp]),
     "pa_pool_add_seq": (_i32, [_vp, _pi32]),
     "pa_pool_fork": (_i32, [_vp, _i32, _pi32]),
+    "pa_pool_add_seq_cached": (_i32, [_vp, _pi32, _i32, ctypes.c_uint64, _pi32, _pi32]),
+    "pa_pool_num_cached": (_i32, [_vp]),
     "pa_pool_append": (_i32, [_vp, _i32, _i32, _pi64, _pi32, _i32, _pi32]),
     "pa_pool_free_seq": (_i32, [_vp, _i32]),
     "pa_pool_block_table": (_i32, [_vp, _i32, _pi32, _i32, _pi32]),
@@ -335,7 +337,7 @@ class BlockPool:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        if h and _lib is not None:  # the module may be torn down first at exit
             _lib.pa_pool_destroy(h)
             self._h = None
 
@@ -343,6 +345,20 @@ class BlockPool:
         sid = ctypes.c_int32()
         _check("pa_pool_add_seq", _lib.pa_pool_add_seq(self._h, ctypes.byref(sid)))
         return sid.value
+
+    def add_seq_cached(self, tokens, extra: int = 0) -> Tuple[int, int]:
+        """New sequence for a prompt, reusing cached full blocks from the
+        left; returns (sequence id, tokens covered by reused blocks)."""
+        arr = np.ascontiguousarray(tokens, dtype=np.int32)
+        sid, hit = ctypes.c_int32(), ctypes.c_int32()
+        st = _lib.pa_pool_add_seq_cached(self._h, arr.ctypes.data_as(_pi32), arr.size,
+                                         ctypes.c_uint64(int(extra)), ctypes.byref(sid),
+                                         ctypes.byref(hit))
+        _check("pa_pool_add_seq_cached", st)
+        return sid.value, hit.value
+
+    def num_cached(self) -> int:
+        return int(_lib.pa_pool_num_cached(self._h))
 
     def fork(self, parent: int) -> int:
         c = ctypes.c_int32()

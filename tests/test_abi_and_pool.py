@@ -140,6 +140,64 @@ def test_auto_partition_policy():
             P.pa_decode_workspace_size(args[0], args[1], 128, args[4], ps)
 
 
+def test_prefix_cache_matches_model_on_random_operations():
+    """pa_pool_add_seq_cached against the oracle model: prompts drawn from a
+    few shared prefixes (so hits, partial hits, revivals of freed blocks and
+    evictions all occur), mixed with appends, forks and frees."""
+    rng = np.random.default_rng(23)
+    nb, bs = 40, 4
+    order = list(rng.permutation(nb))
+    pool, model = _pool_and_model(nb, bs, order)
+    stems = [list(rng.integers(0, 3, 24)) for _ in range(3)]
+    live, hits = [], 0
+    for _ in range(3000):
+        op = int(rng.integers(0, 5))
+        if op <= 1 or not live:
+            stem = stems[int(rng.integers(len(stems)))]
+            cut = int(rng.integers(0, len(stem) + 1))
+            tail = list(rng.integers(0, 3, int(rng.integers(0, 9))))
+            prompt = stem[:cut] + tail
+            extra = int(rng.integers(0, 2))
+            try:
+                mb, mh = model.add_seq_cached(prompt, extra)
+            except ModelOOM:
+                with pytest.raises(P.OutOfBlocks):
+                    pool.add_seq_cached(prompt, extra)
+            else:
+                pb, ph = pool.add_seq_cached(prompt, extra)
+                assert (pb, ph) == (mb, mh)
+                hits += ph
+                live.append(pb)
+        elif op == 2:
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(1, 7))
+            try:
+                ms, mc = model.append(s, n)
+            except ModelOOM:
+                with pytest.raises(P.OutOfBlocks):
+                    pool.append(s, n)
+            else:
+                ps, pc = pool.append(s, n)
+                assert list(ps) == ms and pc == mc
+        elif op == 3:
+            s = live[int(rng.integers(len(live)))]
+            c = pool.fork(s)
+            assert c == model.fork(s)
+            live.append(c)
+        else:
+            s = live.pop(int(rng.integers(len(live))))
+            pool.free_seq(s)
+            model.free_seq(s)
+        assert pool.num_free() == model.num_free()
+        assert pool.num_cached() == model.num_cached()
+        for s in live:
+            assert list(pool.block_table(s)) == model.block_table(s)
+            assert pool.seq_len(s) == model.lens[s]
+        for b in range(nb):
+            assert pool.refcount(b) == model.ref[b]
+    assert hits > 0
+
+
 def test_pool_matches_model_on_random_operations():
     rng = np.random.default_rng(17)
     nb, bs = 48, 8

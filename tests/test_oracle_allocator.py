@@ -154,3 +154,78 @@ def test_shared_prefix_workload_refcounts():
     for s in range(w.S):
         assert np.array_equal(st.block_tables[s, :7], full)
     assert len({int(st.block_tables[s, 7]) for s in range(w.S)}) == 100
+
+
+# ------------------------------------------------------------ prefix cache
+def _cache_model(nb=64, bs=4):
+    return BlockManagerModel(nb, bs, list(range(nb)))
+
+
+def test_prefix_cache_reuses_a_shared_system_prompt():
+    """[k4i] #prefix-caching: a 4096-token system prompt at block_size 16 is
+    256 blocks, all reusable by a second request with the same prompt
+    (golden/pages_needed.json); each shared block's count is then 2."""
+    case = [c for c in golden("pages_needed.json")["cases"] if c["tokens"] == 4096][0]
+    m = BlockManagerModel(600, case["block_size"], list(range(600)))
+    prompt = list(range(1000, 1000 + case["tokens"]))
+    a, hit_a = m.add_seq_cached(prompt)
+    b, hit_b = m.add_seq_cached(prompt)
+    assert hit_a == 0 and hit_b == case["tokens"]
+    assert m.block_table(a) == m.block_table(b) and len(m.block_table(b)) == case["blocks"]
+    assert all(m.ref[x] == 2 for x in m.block_table(a))
+    assert m.num_cached() == case["blocks"] and m.num_free() == 600 - case["blocks"]
+
+
+def test_prefix_cache_stops_at_the_first_miss_and_skips_partial_blocks():
+    m = _cache_model()
+    p = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10]          # 2 full blocks + 2 tokens
+    a, _ = m.add_seq_cached(p)
+    assert m.num_cached() == 2                    # the partial block is not cached
+    q = [1, 2, 3, 4, 0, 6, 7, 8, 9, 10]          # second block differs
+    b, hit = m.add_seq_cached(q)
+    assert hit == 4                               # only the first block is reused
+    assert m.block_table(b)[0] == m.block_table(a)[0]
+    assert m.block_table(b)[1] != m.block_table(a)[1]
+    # a later block with equal tokens but a different parent chain is new too
+    r = [9, 9, 9, 9, 5, 6, 7, 8]
+    _, hit = m.add_seq_cached(r)
+    assert hit == 0
+
+
+def test_prefix_cache_extra_key_separates_caches():
+    m = _cache_model()
+    p = [1, 2, 3, 4, 5, 6, 7, 8]
+    m.add_seq_cached(p, extra=1)
+    _, hit = m.add_seq_cached(p, extra=2)
+    assert hit == 0
+    _, hit = m.add_seq_cached(p, extra=1)
+    assert hit == 8
+
+
+def test_freed_cached_blocks_are_revived_then_evicted_least_recently_freed_first():
+    m = BlockManagerModel(6, 2, list(range(6)))
+    a, _ = m.add_seq_cached([1, 1, 2, 2])        # blocks 0, 1
+    b, _ = m.add_seq_cached([3, 3, 4, 4])        # blocks 2, 3
+    m.free_seq(a)                                 # 0, 1 back (still cached)
+    m.free_seq(b)                                 # then 2, 3
+    assert list(m.free) == [4, 5, 0, 1, 2, 3] and m.num_cached() == 4
+    c, hit = m.add_seq_cached([1, 1, 2, 2])      # revived from the middle of the queue
+    assert hit == 4 and m.block_table(c) == [0, 1] and list(m.free) == [4, 5, 2, 3]
+    d, _ = m.add_seq_cached([7, 7, 8, 8, 9, 9])  # takes 4, 5, then 2: 2's entry goes
+    assert m.block_table(d) == [4, 5, 2]
+    assert m.num_cached() == 4 - 1 + 3  # 2 lost its entry; 4, 5, 2 hold the new full blocks
+    e, hit = m.add_seq_cached([3, 3])            # its block was evicted: a miss, which
+    assert hit == 0 and m.block_table(e) == [3]   # takes 3 (the last free) and drops (3,3)->(4,4)
+    assert m.num_free() == 0
+
+
+def test_prefix_cache_out_of_blocks_is_atomic():
+    m = BlockManagerModel(4, 2, list(range(4)))
+    m.add_seq_cached([1, 1, 2, 2])
+    before = (list(m.free), dict(m.cache), list(m.ref))
+    try:
+        m.add_seq_cached([5, 5, 6, 6, 7])         # needs 3 blocks, 2 free
+        raise AssertionError("expected OutOfBlocks")
+    except OutOfBlocks:
+        pass
+    assert (list(m.free), dict(m.cache), list(m.ref)) == before
