@@ -28,6 +28,9 @@ Modules
 ``attention``  cache write, per-token gather, decode and causal packed
                prefill as plain definitions, plus the block-wise online-softmax
                and split-K merge written out as cross-checks.
+``fp8``        FP8 (OCP E4M3) KV cache: code table, quantising write
+               (x / scale in fp32, nearest with ties to even, saturated) and
+               read-back (code value times scale).
 ``allocator``  step-by-step block-manager model (free queue, reference counts,
                fork, append with copy-on-write, free).
 ``state``      derives block tables, slot mappings and the host pool of a
@@ -38,6 +41,6 @@ examples printed on the pages, closed forms, invariants or brute force.
 """
 from .attention import (  # noqa: F401
     attention_dense, bits_to_f64, decode_ref, gather_seq, merge_partitions,
-    online_softmax_blocks, partition_stats, prefill_ref, write_ref, NHD, HND,
+    online_softmax_blocks, partition_stats, prefill_ref, write_ref, write_ref_fp8, NHD, HND,
 )
 from .allocator import BlockManagerModel, OutOfBlocks  # noqa: F401

@@ -15,6 +15,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .fp8 import E4M3, quantize
+
 NHD, HND = 0, 1
 
 
@@ -33,7 +35,18 @@ def bits_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
             .view(np.float32).astype(np.float64)
     if dtype == "f16":
         return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "e4m3":  # FP8 codes (uint8), unscaled values
+        return E4M3[np.asarray(a, dtype=np.uint8)]
     raise ValueError(dtype)
+
+
+def _cache_f64(rows, dtype, kv_dtype, scale):
+    """Gathered cache rows as float64: the stored values, times the scale for
+    an FP8 cache (oracle.fp8: a code reads back as its value times scale)."""
+    if kv_dtype is None or kv_dtype == dtype:
+        return bits_to_f64(rows, dtype)
+    assert kv_dtype == "e4m3", kv_dtype
+    return bits_to_f64(rows, "e4m3") * float(np.float32(scale))
 
 
 def _raw(a: np.ndarray) -> np.ndarray:
@@ -78,6 +91,18 @@ def write_ref(key_cache, value_cache, key, value, slot_mapping, block_size, layo
     return kc, vc
 
 
+def write_ref_fp8(key_cache, value_cache, key, value, slot_mapping, block_size, src_dtype,
+                  k_scale, v_scale, layout=NHD):
+    """Cache write into an FP8 (E4M3) pool ([vllm] §6.3, §7.4 flash variant):
+    every new row is quantised (``oracle.fp8.quantize``: x / scale in fp32,
+    nearest E4M3 with ties to even, saturated to +-448) and scattered exactly
+    as ``write_ref`` scatters; padding rows are skipped.  Caches are uint8
+    codes; returns the new (key, value) code arrays."""
+    kq = quantize(key, src_dtype, k_scale)
+    vq = quantize(value, src_dtype, v_scale)
+    return write_ref(key_cache, value_cache, kq, vq, slot_mapping, block_size, layout)
+
+
 # -------------------------------------------------------------------- gather
 def gather_seq(cache, block_table_row, L, block_size, layout=NHD):
     """Logical rows 0..L-1 of one sequence, read through its block table.
@@ -116,7 +141,8 @@ def attention_dense(q, K, V, scale):
 
 
 def decode_ref(query, key_cache, value_cache, block_tables, context_lens, scale,
-               block_size, dtype, layout=NHD, return_probs=False):
+               block_size, dtype, layout=NHD, return_probs=False, kv_dtype=None,
+               k_scale=1.0, v_scale=1.0):
     """Decode attention over the paged cache, float64.
 
     For sequence s and query head h: kv head ``h // (H / Hkv)`` (contiguous
@@ -124,7 +150,9 @@ def decode_ref(query, key_cache, value_cache, block_tables, context_lens, scale,
     gathered through ``block_tables[s]`` ([vllm] §3.1, §6.2 with
     ``seqlen_k = seq_lens``), and the output is ``attention_dense``.
     ``query`` is [S, H, D] raw; returns out [S, H, D] (and the probability
-    vectors per (s, h) if asked).
+    vectors per (s, h) if asked).  ``kv_dtype`` "e4m3": the caches hold FP8
+    codes that read back as value * k_scale (keys) and value * v_scale
+    (values), the query keeps ``dtype``.
     """
     qf = bits_to_f64(np.asarray(query), dtype)
     S, H, D = qf.shape
@@ -134,8 +162,10 @@ def decode_ref(query, key_cache, value_cache, block_tables, context_lens, scale,
     probs = {}
     for s in range(S):
         L = int(context_lens[s])
-        K = bits_to_f64(gather_seq(key_cache, block_tables[s], L, block_size, layout), dtype)
-        V = bits_to_f64(gather_seq(value_cache, block_tables[s], L, block_size, layout), dtype)
+        K = _cache_f64(gather_seq(key_cache, block_tables[s], L, block_size, layout), dtype,
+                       kv_dtype, k_scale)
+        V = _cache_f64(gather_seq(value_cache, block_tables[s], L, block_size, layout), dtype,
+                       kv_dtype, v_scale)
         for h in range(H):
             o, p = attention_dense(qf[s, h], K[:, h // G], V[:, h // G], scale)
             out[s, h] = o
@@ -145,7 +175,7 @@ def decode_ref(query, key_cache, value_cache, block_tables, context_lens, scale,
 
 
 def prefill_ref(query, key_cache, value_cache, block_tables, query_start_loc, context_lens,
-                scale, block_size, dtype, layout=NHD):
+                scale, block_size, dtype, layout=NHD, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Causal packed-sequence prefill over the paged cache, float64.
 
     Queries of all sequences are packed without padding; sequence s owns rows
@@ -154,7 +184,8 @@ def prefill_ref(query, key_cache, value_cache, block_tables, query_start_loc, co
     ``context_lens[s]`` (all L tokens already cached), row j is the token at
     absolute position ``L - n + j`` and attends to keys 0 .. L - n + j (causal,
     aligned to the end of the context: [vllm] §6.2 ``causal=True`` with
-    ``seqlen_k = seq_lens``).  Returns out [num_tokens, H, D].
+    ``seqlen_k = seq_lens``).  Returns out [num_tokens, H, D].  ``kv_dtype``
+    and the scales as in ``decode_ref``.
     """
     qf = bits_to_f64(np.asarray(query), dtype)
     T, H, D = qf.shape
@@ -166,8 +197,10 @@ def prefill_ref(query, key_cache, value_cache, block_tables, query_start_loc, co
         n = int(qsl[s + 1] - qsl[s])
         L = int(context_lens[s])
         assert n <= L
-        K = bits_to_f64(gather_seq(key_cache, block_tables[s], L, block_size, layout), dtype)
-        V = bits_to_f64(gather_seq(value_cache, block_tables[s], L, block_size, layout), dtype)
+        K = _cache_f64(gather_seq(key_cache, block_tables[s], L, block_size, layout), dtype,
+                       kv_dtype, k_scale)
+        V = _cache_f64(gather_seq(value_cache, block_tables[s], L, block_size, layout), dtype,
+                       kv_dtype, v_scale)
         for j in range(n):
             a = L - n + j  # absolute position of query row j
             for h in range(H):

@@ -24,7 +24,7 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 from .allocator import BlockManagerModel
-from .attention import NHD, write_ref
+from .attention import NHD, write_ref, write_ref_fp8
 
 
 @dataclass
@@ -87,23 +87,32 @@ def build_state(w, max_blocks: Optional[int] = None) -> OracleState:
     return OracleState(bt, seq_slots, copies, step, setup_positions, prefix_slots, poison, model)
 
 
-def empty_pool(w, layout=NHD) -> np.ndarray:
-    """All-NaN pool of NB + 1 blocks (the extra one is the poison block)."""
-    raw = np.uint32 if w.dtype == "f32" else np.uint16
+def empty_pool(w, layout=NHD, kv_dtype=None) -> np.ndarray:
+    """All-NaN pool of NB + 1 blocks (the extra one is the poison block);
+    all-ones bits are NaN in every element type, E4M3 codes included."""
+    raw = np.uint8 if kv_dtype == "e4m3" else np.uint32 if w.dtype == "f32" else np.uint16
     shape = (w.NB + 1, w.bs, w.Hkv, w.D) if layout == NHD else (w.NB + 1, w.Hkv, w.bs, w.D)
     return np.full(shape, np.iinfo(raw).max, dtype=raw)
 
 
-def build_pool(w, st: OracleState, layout=NHD, include_step: bool = False, seqs=None):
+def build_pool(w, st: OracleState, layout=NHD, include_step: bool = False, seqs=None,
+               kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Host K and V pools after set-up (and after the step's write if asked).
 
     ``seqs`` restricts the per-sequence writes (and the step rows) to those
     sequences; the shared prefix and the copies are always applied.
+    ``kv_dtype`` "e4m3": every write quantises (``write_ref_fp8``) into pools
+    of E4M3 codes.
     """
-    kc, vc = empty_pool(w, layout), empty_pool(w, layout)
+    def write(kc, vc, k, v, slots, bs, lay):
+        if kv_dtype == "e4m3":
+            return write_ref_fp8(kc, vc, k, v, slots, bs, w.dtype, k_scale, v_scale, lay)
+        return write_ref(kc, vc, k, v, slots, bs, lay)
+
+    kc, vc = empty_pool(w, layout, kv_dtype), empty_pool(w, layout, kv_dtype)
     if st.prefix_slots is not None:
         k, v = w.kv(0, 0, w.prefix_len)
-        kc, vc = write_ref(kc, vc, k, v, st.prefix_slots, w.bs, layout)
+        kc, vc = write(kc, vc, k, v, st.prefix_slots, w.bs, layout)
     for src, dst in st.copies:
         kc[dst] = kc[src]
         vc[dst] = vc[src]
@@ -118,12 +127,12 @@ def build_pool(w, st: OracleState, layout=NHD, include_step: bool = False, seqs=
         vs.append(v[pos - lo])
         ss.append(st.seq_slots[s][pos])
     if ss:
-        kc, vc = write_ref(kc, vc, np.concatenate(ks), np.concatenate(vs), np.concatenate(ss),
-                           w.bs, layout)
+        kc, vc = write(kc, vc, np.concatenate(ks), np.concatenate(vs), np.concatenate(ss),
+                       w.bs, layout)
     if include_step:
         K, V = w.new_rows()
         slots = st.step_slots.copy()
         if seqs is not None:
             slots[~np.isin(w.row_seq, list(seqs))] = -1
-        kc, vc = write_ref(kc, vc, K, V, slots, w.bs, layout)
+        kc, vc = write(kc, vc, K, V, slots, w.bs, layout)
     return kc, vc
