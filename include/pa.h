@@ -27,7 +27,8 @@
  *     out-of-range values are undefined behaviour; pa_check_metadata checks
  *     them synchronously for tests and debugging.
  *   - Element types: PA_F32, PA_BF16, PA_F16.  K/V caches, keys, values and
- *     queries of one call share one type.
+ *     queries of one call share one type, except in the *_fp8 calls, whose
+ *     caches are PA_FP8_E4M3.
  *   - Sizes are in elements unless the name says bytes.
  */
 #ifndef PA_H_
@@ -50,7 +51,14 @@ typedef enum {
   PA_ERR_METADATA = 6          /* pa_check_metadata found a violated precondition*/
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
+/* PA_FP8_E4M3: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; no infinities, largest finite 448, S.1111.111 = NaN), one
+ * byte per element.  A cache element type only ([vllm] §6.3 kv_cache_dtype
+ * with k_scale / v_scale, §8 FP8 KV-cache quantisation): it is written by
+ * pa_reshape_and_cache_fp8 (or bit-copied by pa_reshape_and_cache /
+ * pa_copy_blocks) and read by pa_decode_fp8; queries and outputs stay
+ * 16-bit or fp32. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Cache layouts ([vllm] §3.3).  A block is contiguous in both. */
 typedef enum {
@@ -88,6 +96,32 @@ pa_status pa_reshape_and_cache(const void* key, const void* value,
                                int32_t num_kv_heads, int32_t head_size,
                                int32_t block_size, int32_t num_blocks,
                                pa_dtype dtype, pa_layout layout, void* stream);
+
+/*
+ * pa_reshape_and_cache_fp8 -- the cache write into FP8 pools ([vllm] §6.3
+ * reshape_and_cache_flash with kv_cache_dtype, k_scale and v_scale; §7.4 the
+ * flash variant of the write kernel).
+ *
+ * As pa_reshape_and_cache, but every element x of a key (value) row is
+ * stored as the E4M3 code of x / k_scale (x / v_scale): the quotient is
+ * taken in fp32 (correctly rounded), clamped to [-448, 448] (infinities
+ * too), then rounded to the nearest E4M3 value with ties to the even code;
+ * NaN stays NaN (code 0x7F or 0xFF).  A code c later reads back as
+ * value(c) * scale.
+ *   key, value             (device) rows of src_dtype (PA_F32, PA_BF16, PA_F16)
+ *   key_cache, value_cache (device) uint8 pools of num_blocks blocks
+ *   k_scale, v_scale       positive, finite
+ * head_size must be a multiple of 16; pointers and source row strides
+ * 16-byte aligned.  Slot preconditions as in pa_reshape_and_cache.
+ */
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, pa_dtype src_dtype,
+                                   int64_t key_row_stride, int64_t value_row_stride,
+                                   void* key_cache, void* value_cache,
+                                   const int64_t* slot_mapping, int32_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_size,
+                                   int32_t block_size, int32_t num_blocks,
+                                   pa_layout layout, float k_scale, float v_scale,
+                                   void* stream);
 
 /*
  * pa_copy_blocks -- whole-block copies of both pools (copy-on-write, [k4i]
@@ -158,6 +192,26 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
                     int32_t head_size, int32_t block_size, int32_t num_blocks,
                     float scale, int32_t partition_size, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_fp8 -- pa_decode over FP8 (E4M3) pools written by
+ * pa_reshape_and_cache_fp8: the cached key t reads back as K_t = value(code)
+ * * k_scale and the value as V_t = value(code) * v_scale ([vllm] §6.3), so
+ *   out[s,h,:] = softmax_t(scale * k_scale * q . value(K codes)) value(V codes) * v_scale.
+ * The query is q_dtype (PA_BF16 or PA_F16); out_dtype is PA_F32 or q_dtype.
+ * Every other argument, the workspace (pa_decode_workspace_size) and the
+ * partition policy (pa_decode_auto_partition with kv_dtype PA_FP8_E4M3) are
+ * as in pa_decode; head_size 64 or 128.
+ */
+pa_status pa_decode_fp8(void* out, pa_dtype out_dtype, const void* query, pa_dtype q_dtype,
+                        const void* key_cache, const void* value_cache,
+                        float k_scale, float v_scale, pa_layout layout,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t max_context_len,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_size, int32_t block_size, int32_t num_blocks,
+                        float scale, int32_t partition_size, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /*
  * The two halves of split-K decode, for callers that schedule or time them

@@ -37,13 +37,14 @@ PA_OK = 0
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARGUMENT", 2: "PA_ERR_UNSUPPORTED",
                 3: "PA_ERR_WORKSPACE_TOO_SMALL", 4: "PA_ERR_OUT_OF_BLOCKS", 5: "PA_ERR_HIP",
                 6: "PA_ERR_METADATA"}
-PA_F32, PA_BF16, PA_F16 = 0, 1, 2
-KV_DTYPE = {"f32": PA_F32, "bf16": PA_BF16, "f16": PA_F16}  # workload dtype names
+PA_F32, PA_BF16, PA_F16, PA_FP8_E4M3 = 0, 1, 2, 3
+KV_DTYPE = {"f32": PA_F32, "bf16": PA_BF16, "f16": PA_F16, "e4m3": PA_FP8_E4M3}  # dtype names
 NHD, HND = 0, 1
 
 EXPORTED = [
-    "pa_status_string", "pa_last_error", "pa_reshape_and_cache", "pa_copy_blocks",
-    "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode", "pa_decode_partitions",
+    "pa_status_string", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_fp8",
+    "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode",
+    "pa_decode_fp8", "pa_decode_partitions",
     "pa_decode_reduce", "pa_decode_cascade_workspace_size", "pa_decode_cascade", "pa_prefill",
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
     "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
@@ -59,11 +60,15 @@ _sig = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _vp]),
+    "pa_reshape_and_cache_fp8": (_i32, [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64]),
     "pa_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_fp8": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _f32, _f32, _i32, _vp, _i32, _vp,
+                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
@@ -117,7 +122,8 @@ def _torch():
 
 def _dtype_code(t) -> int:
     torch = _torch()
-    m = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.float16: PA_F16}
+    m = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.float16: PA_F16,
+         torch.uint8: PA_FP8_E4M3, torch.float8_e4m3fn: PA_FP8_E4M3}  # 1-byte caches hold E4M3 codes
     if t.dtype not in m:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
@@ -172,6 +178,30 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, layou
         T, hkv, d, bs, nb, _dtype_code(key_cache), layout, _stream(stream)))
 
 
+def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale: float,
+                             v_scale: float, layout: int = NHD, stream=None) -> None:
+    """Quantising cache write: rows key/value [T, Hkv, D] (f32/bf16/f16) stored as
+    E4M3 codes of x / k_scale and x / v_scale into uint8 pools at slot_mapping [T]."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    if key.dim() != 3 or key.shape[1:] != (hkv, d) or value.shape != key.shape:
+        raise ValueError("key/value must be [T, num_kv_heads, head_size] matching the cache")
+    if key.stride(2) != 1 or key.stride(1) != d or value.stride(2) != 1 or value.stride(1) != d:
+        raise ValueError("key/value rows must be contiguous")
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if _dtype_code(key_cache) != PA_FP8_E4M3 or key.dtype != value.dtype:
+        raise TypeError("FP8 pools are uint8 (or float8_e4m3fn); key and value share a dtype")
+    T = key.shape[0]
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    _check("pa_reshape_and_cache_fp8", _lib.pa_reshape_and_cache_fp8(
+        _dev(key, "key", contiguous=False), _dev(value, "value", contiguous=False),
+        _dtype_code(key), key.stride(0), value.stride(0), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
+        T, hkv, d, bs, nb, layout, float(k_scale), float(v_scale), _stream(stream)))
+
+
 def pa_copy_blocks(key_cache, value_cache, block_pairs, layout: int = NHD, stream=None) -> None:
     """Copy whole blocks: block_pairs int32 [n, 2] = (source, destination)."""
     torch = _torch()
@@ -217,6 +247,32 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, ma
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, H, hkv, d, bs,
         nb, float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens,
+                  max_context_len: int, scale: float, k_scale: float, v_scale: float,
+                  layout: int = NHD, partition_size: int = -1, workspace=None,
+                  stream=None) -> None:
+    """Decode attention over E4M3 pools (uint8); query bf16/f16, out float32 or the query type."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    S, H, D = query.shape
+    if D != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_seqs, num_heads, head_size]")
+    if _dtype_code(key_cache) != PA_FP8_E4M3 or value_cache.dtype != key_cache.dtype:
+        raise TypeError("FP8 pools are uint8 (or float8_e4m3fn)")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables [S, max_blocks] and context_lens [S] required")
+    ws_ptr, ws_bytes = (None, 0)
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    _check("pa_decode_fp8", _lib.pa_decode_fp8(
+        _dev(out, "out"), _dtype_code(out), _dev(query, "query"), _dtype_code(query),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), float(k_scale),
+        float(v_scale), layout, _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context_len), S, H, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr,
+        ws_bytes, _stream(stream)))
 
 
 def pa_decode_cascade_workspace_size(num_seqs: int, num_heads: int, head_size: int,

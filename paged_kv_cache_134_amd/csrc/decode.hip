@@ -113,9 +113,10 @@ DecodeParams make_params(const DecodeArgs& a) {
   p.key_begin = a.key_begin;
   p.part_base = a.part_base;
   p.all_partial = a.all_partial;
-  p.scale_log2e = a.scale * kLog2e;
+  p.scale_log2e = a.scale * a.k_scale * kLog2e;
+  p.v_scale = a.v_scale;
   p.out_dtype = a.out_dtype;
-  const int64_t elem = a.kv_dtype == PA_F32 ? 4 : 2;
+  const int64_t elem = a.kv_dtype == PA_F32 ? 4 : a.kv_dtype == PA_FP8_E4M3 ? 1 : 2;
   p.off32 = (int64_t)g.num_blocks * p.blk_stride * elem <= (int64_t)UINT32_MAX;
   return p;
 }
@@ -135,8 +136,11 @@ hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.num_seqs * g.num_kv_heads),
             a.partition_size > 0 ? a.max_partitions - a.part_base : 1);
   if (grid.y == 0) return hipSuccess;
-  if (decode_uses_group_kernel(a.kv_dtype, G))
-    return dec::launch_group(p, a.kv_dtype, g.head_size, G, grid, stream);
+  const bool group = decode_uses_group_kernel(a.kv_dtype, G);
+  if (a.kv_dtype == PA_FP8_E4M3)
+    return group ? dec::launch_group_fp8(p, a.q_dtype, g.head_size, G, grid, stream)
+                 : dec::launch_head_fp8(p, a.q_dtype, g.head_size, G, grid, stream);
+  if (group) return dec::launch_group(p, a.kv_dtype, g.head_size, G, grid, stream);
   return dec::launch_head(p, a.kv_dtype, g.head_size, G, grid, stream);
 }
 

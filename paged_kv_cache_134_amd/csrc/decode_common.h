@@ -42,7 +42,8 @@ struct DecodeParams {
   int32_t key_begin;       // partitions cover keys [key_begin, L) (0 outside cascades)
   int32_t part_base;       // workspace index of partition 0 (earlier slots hold prefix partials)
   bool all_partial;        // never finish a head here: other partials exist
-  float scale_log2e;
+  float scale_log2e;        // softmax scale * log2(e), times k_scale for FP8 caches
+  float v_scale;            // FP8 caches: V scale, applied to the merged output (else 1)
   pa_dtype out_dtype;
   bool off32;  // every byte offset into either cache fits in 32 bits
 };
@@ -72,6 +73,7 @@ __device__ __forceinline__ bool single_partition(const DecodeParams& p, int L) {
 // when the whole context is one partition (the reduce skips those heads).
 __device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int part, int d, int D,
                                      float M, float lsum, float o, bool single) {
+  o *= p.v_scale;
   if (p.partition_size > 0 && !single) {
     const int64_t pi = head * p.max_partitions + p.part_base + part;
     p.part_out[pi * D + d] = o;
@@ -88,6 +90,9 @@ __device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int pa
 // partitions or 1).
 hipError_t launch_head(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st);
 hipError_t launch_group(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st);
+// FP8 (E4M3) caches; qt = query type (bf16 or f16).
+hipError_t launch_head_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st);
+hipError_t launch_group_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st);
 
 }  // namespace dec
 }  // namespace pa

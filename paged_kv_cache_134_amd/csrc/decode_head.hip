@@ -1,4 +1,5 @@
-// Paged decode, per-head kernel (group size 1 or 2, and every fp32 cache).
+// Paged decode, per-head kernel (group size 1 or 2, and every fp32 cache;
+// FP8 caches with group size 1 or 2).
 //
 // One workgroup of 4 waves per (sequence, kv head, partition) reads the kv
 // head's K/V rows once for its G query heads.  A token row is spread over
@@ -23,10 +24,15 @@ namespace {
 constexpr int kUnroll = 4;    // token rows per lane group per batch
 constexpr int kWindow = 512;  // tokens per block-table staging window
 
-template <pa_dtype DT, int D, int G>
+// FP8: the cache holds E4M3 codes (one byte) and DT is the query's type; a
+// lane's 16-byte chunk is then 16 elements, K converts exactly to DT pairs
+// for the same dot products and V to fp32.
+template <pa_dtype DT, int D, int G, bool FP8 = false>
 __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const DecodeParams p) {
   using F = Fmt<DT>;
-  constexpr int VEC = F::kVec;             // elements per lane chunk
+  constexpr int CB = FP8 ? 1 : F::kBytes;  // cache bytes per element
+  constexpr int VEC = 16 / CB;             // elements per lane chunk
+  constexpr int QC = FP8 ? 2 : 1;          // 16-byte query chunks per lane chunk
   constexpr int LPT = D / VEC;             // lanes per token row
   constexpr int TPW = kWave / LPT;         // token rows per wave per step
   constexpr int TPS = TPW * kDecodeWaves;  // token rows per workgroup per step
@@ -49,12 +55,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
     t1 = min(L, t0 + p.partition_size);
   }
 
-  uint4 q[G];
+  uint4 q[G][QC];
   {
     const uint4* qp = reinterpret_cast<const uint4*>(p.query) +
-                      ((int64_t)s * p.num_heads + (int64_t)kvh * G) * (D / VEC) + ch;
+                      ((int64_t)s * p.num_heads + (int64_t)kvh * G) * (D / F::kVec) + ch * QC;
 #pragma unroll
-    for (int g = 0; g < G; ++g) q[g] = qp[g * (D / VEC)];
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int c = 0; c < QC; ++c) q[g][c] = qp[g * (D / F::kVec) + c];
   }
 
   float m[G], l[G], acc[G][VEC];
@@ -90,8 +98,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
         const int tc = min(t, w1 - 1);
         const int64_t blk = s_bt[(tc >> lbs) - e0];
         const int64_t off = blk * p.blk_stride + (int64_t)(tc & bs_mask) * p.tok_stride + lane_off;
-        kr[u] = load_nt(p.key_cache + off * F::kBytes);
-        vr[u] = load_nt(p.value_cache + off * F::kBytes);
+        kr[u] = load_nt(p.key_cache + off * CB);
+        vr[u] = load_nt(p.value_cache + off * CB);
       }
     };
 
@@ -103,9 +111,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
       float z[kUnroll][G];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
+        uint4 kc[QC];
+        if constexpr (FP8)
+          fp8x16_to_pairs<DT>(kr[u], kc[0], kc[1]);
+        else
+          kc[0] = kr[u];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float d = group_sum<LPT>(dot_chunk<DT>(q[g], kr[u], 0.f));
+          float d = 0.f;
+#pragma unroll
+          for (int c = 0; c < QC; ++c) d = dot_chunk<DT>(q[g][c], kc[c], d);
+          d = group_sum<LPT>(d);
           z[u][g] = valid[u] ? d * p.scale_log2e : -INFINITY;
         }
       }
@@ -132,7 +148,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         float vf[VEC];
-        chunk_to_f32<DT>(vr[u], vf);
+        if constexpr (FP8)
+          fp8x16_to_f32(vr[u], vf);
+        else
+          chunk_to_f32<DT>(vr[u], vf);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float pw = valid[u] ? __builtin_amdgcn_exp2f(z[u][g] - m[g]) : 0.f;
@@ -238,6 +257,25 @@ hipError_t launch_d(const DecodeParams& p, int D, int G, dim3 grid, hipStream_t 
   return hipErrorInvalidValue;
 }
 
+// FP8 caches take this kernel for group sizes 1 and 2.
+template <pa_dtype QT, int D>
+hipError_t launch_fp8_g(const DecodeParams& p, int G, dim3 grid, hipStream_t st) {
+  dim3 block(kDecodeThreads);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_reg_kernel<QT, D, 1, true>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_reg_kernel<QT, D, 2, true>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <pa_dtype QT>
+hipError_t launch_fp8_d(const DecodeParams& p, int D, int G, dim3 grid, hipStream_t st) {
+  if (D == 64) return launch_fp8_g<QT, 64>(p, G, grid, st);
+  if (D == 128) return launch_fp8_g<QT, 128>(p, G, grid, st);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_head(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st) {
@@ -245,6 +283,14 @@ hipError_t launch_head(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 gr
     case PA_F32: return launch_d<PA_F32>(p, D, G, grid, st);
     case PA_BF16: return launch_d<PA_BF16>(p, D, G, grid, st);
     case PA_F16: return launch_d<PA_F16>(p, D, G, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_head_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st) {
+  switch (qt) {
+    case PA_BF16: return launch_fp8_d<PA_BF16>(p, D, G, grid, st);
+    case PA_F16: return launch_fp8_d<PA_F16>(p, D, G, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -96,6 +96,59 @@ __device__ __forceinline__ void chunk_to_f32(const uint4& v, float* out) {
   for (int e = 0; e < Fmt<DT>::kVec; ++e) out[e] = chunk_elem<DT>(v, e);
 }
 
+// ---- FP8 (OCP E4M3) cache elements.  gfx950's conversion instructions read
+// and write the OCP E4M3 format; reading is exact (every E4M3 value is a
+// bf16, f16 and fp32 value), writing rounds to nearest even but does not
+// saturate (magnitudes past 464 become NaN), so writers clamp first.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Codes in bytes 0-1 (HI = false) or 2-3 (HI = true) of w as a packed pair of
+// DT (bf16 or f16), element order kept; the scale operand 1.0 leaves the
+// values unscaled.
+template <pa_dtype DT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_pair(uint32_t w) {
+  if constexpr (DT == PA_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// 16 codes (one 16-byte chunk) as 16 elements of DT in two 16-byte chunks.
+template <pa_dtype DT>
+__device__ __forceinline__ void fp8x16_to_pairs(const uint4& v, uint4& lo, uint4& hi) {
+  lo = make_uint4(fp8x2_to_pair<DT, false>(v.x), fp8x2_to_pair<DT, true>(v.x),
+                  fp8x2_to_pair<DT, false>(v.y), fp8x2_to_pair<DT, true>(v.y));
+  hi = make_uint4(fp8x2_to_pair<DT, false>(v.z), fp8x2_to_pair<DT, true>(v.z),
+                  fp8x2_to_pair<DT, false>(v.w), fp8x2_to_pair<DT, true>(v.w));
+}
+
+// 16 codes as floats.
+__device__ __forceinline__ void fp8x16_to_f32(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);
+    out[4 * j] = a.x;
+    out[4 * j + 1] = a.y;
+    out[4 * j + 2] = b.x;
+    out[4 * j + 3] = b.y;
+  }
+}
+
+// Clamp to the largest finite E4M3 magnitude (NaN passes through).
+__device__ __forceinline__ float e4m3_saturate(float y) {
+  return y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
+}
+
+// Four floats (already in range) as four E4M3 codes, byte i = code of the
+// i-th argument.
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(

@@ -21,9 +21,15 @@ bool pow2_in(int32_t v, int32_t lo, int32_t hi) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : t == PA_FP8_E4M3 ? 1 : 2; }
 
+// Types queries, outputs and 16-bit/fp32 caches are computed in.
 bool valid_dtype(pa_dtype t) { return t == PA_F32 || t == PA_BF16 || t == PA_F16; }
+
+// Types a cache may hold (bit copies accept every one).
+bool valid_storage(pa_dtype t) { return valid_dtype(t) || t == PA_FP8_E4M3; }
+
+bool finite_positive(float x) { return x > 0.f && x <= 3.4028234663852886e38f; }
 
 bool valid_group(int32_t h, int32_t hkv) {
   if (h <= 0 || hkv <= 0 || h % hkv != 0) return false;
@@ -80,7 +86,7 @@ extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value,
                                           pa_layout layout, void* stream) {
   if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks <= 0)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: non-positive size");
-  if (!valid_dtype(dtype)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: bad dtype");
+  if (!valid_storage(dtype)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: bad dtype");
   if (layout != PA_LAYOUT_NHD && layout != PA_LAYOUT_HND)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache: bad layout");
   const int eb = elem_bytes(dtype);
@@ -102,13 +108,49 @@ extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value,
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_reshape_and_cache");
 }
 
+extern "C" pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, pa_dtype src_dtype,
+                                              int64_t key_row_stride, int64_t value_row_stride,
+                                              void* key_cache, void* value_cache,
+                                              const int64_t* slot_mapping, int32_t num_tokens,
+                                              int32_t num_kv_heads, int32_t head_size,
+                                              int32_t block_size, int32_t num_blocks,
+                                              pa_layout layout, float k_scale, float v_scale,
+                                              void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache_fp8: non-positive size");
+  if (!valid_dtype(src_dtype))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache_fp8: source dtype must be f32, bf16 or f16");
+  if (layout != PA_LAYOUT_NHD && layout != PA_LAYOUT_HND)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache_fp8: bad layout");
+  if (!finite_positive(k_scale) || !finite_positive(v_scale))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache_fp8: scales must be positive and finite");
+  if (head_size % 16 != 0)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache_fp8: head_size must be a multiple of 16");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache_fp8: null pointer");
+  const int eb = elem_bytes(src_dtype);
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (key_row_stride < row || value_row_stride < row || (key_row_stride * eb) % 16 ||
+      (value_row_stride * eb) % 16)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache_fp8: row stride too small or not 16-byte aligned");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_reshape_and_cache_fp8: pointers must be 16-byte aligned");
+  pa::PoolGeom g{num_kv_heads, head_size, block_size, num_blocks, layout};
+  hipError_t e = pa::launch_reshape_and_cache_fp8(key, value, src_dtype, key_row_stride,
+                                                  value_row_stride, key_cache, value_cache,
+                                                  slot_mapping, num_tokens, g, k_scale, v_scale,
+                                                  (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_reshape_and_cache_fp8");
+}
+
 extern "C" pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs,
                                     int32_t num_pairs, int32_t num_kv_heads, int32_t head_size,
                                     int32_t block_size, int32_t num_blocks, pa_dtype dtype,
                                     void* stream) {
   if (num_pairs < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks <= 0)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_copy_blocks: non-positive size");
-  if (!valid_dtype(dtype)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_copy_blocks: bad dtype");
+  if (!valid_storage(dtype)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_copy_blocks: bad dtype");
   if (num_pairs == 0) return PA_OK;
   if (!key_cache || !value_cache || !block_pairs)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_copy_blocks: null pointer");
@@ -175,8 +217,8 @@ namespace {
 // Checks shared by the decode entry points; fills `a` (workspace pointers
 // included when split) and resolves partition_size -1.
 pa_status decode_prepare(const char* fn, void* out, pa_dtype out_dtype, const void* query,
-                         const void* key_cache, const void* value_cache, pa_dtype kv_dtype,
-                         pa_layout layout, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         pa_dtype q_dtype, const void* key_cache, const void* value_cache,
+                         pa_dtype kv_dtype, pa_layout layout, const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
                          int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                          int32_t block_size, int32_t num_blocks, float scale,
@@ -189,8 +231,13 @@ pa_status decode_prepare(const char* fn, void* out, pa_dtype out_dtype, const vo
   };
   if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "negative size or no blocks");
-  if (!valid_dtype(kv_dtype) || (out_dtype != PA_F32 && out_dtype != kv_dtype))
+  if (kv_dtype == PA_FP8_E4M3) {
+    if ((q_dtype != PA_BF16 && q_dtype != PA_F16) || (out_dtype != PA_F32 && out_dtype != q_dtype))
+      return fail(PA_ERR_INVALID_ARGUMENT, "FP8 cache: query must be bf16 or f16, out f32 or the query type");
+  } else if (!valid_dtype(kv_dtype) || q_dtype != kv_dtype ||
+             (out_dtype != PA_F32 && out_dtype != kv_dtype)) {
     return fail(PA_ERR_INVALID_ARGUMENT, "bad kv/out dtype");
+  }
   if (layout != PA_LAYOUT_NHD && layout != PA_LAYOUT_HND)
     return fail(PA_ERR_INVALID_ARGUMENT, "bad layout");
   if (!valid_group(num_heads, num_kv_heads))
@@ -219,6 +266,7 @@ pa_status decode_prepare(const char* fn, void* out, pa_dtype out_dtype, const vo
   a->key_cache = key_cache;
   a->value_cache = value_cache;
   a->kv_dtype = kv_dtype;
+  a->q_dtype = q_dtype;
   a->block_tables = block_tables;
   a->max_blocks_per_seq = max_blocks_per_seq;
   a->context_lens = context_lens;
@@ -263,8 +311,10 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                                int32_t num_blocks, float scale, int32_t partition_size,
                                void* workspace, size_t workspace_bytes_, void* stream) {
+  if (kv_dtype == PA_FP8_E4M3)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: FP8 caches are read by pa_decode_fp8");
   pa::DecodeArgs a;
-  pa_status st = decode_prepare("pa_decode", out, out_dtype, query, key_cache, value_cache,
+  pa_status st = decode_prepare("pa_decode", out, out_dtype, query, kv_dtype, key_cache, value_cache,
                                 kv_dtype, layout, block_tables, max_blocks_per_seq, context_lens,
                                 max_context_len, num_seqs, num_heads, num_kv_heads, head_size,
                                 block_size, num_blocks, scale, partition_size, workspace,
@@ -273,6 +323,31 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
   hipError_t e = pa::launch_decode_main(a, (hipStream_t)stream);
   if (e == hipSuccess) e = pa::launch_decode_reduce(a, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode");
+}
+
+extern "C" pa_status pa_decode_fp8(void* out, pa_dtype out_dtype, const void* query,
+                                   pa_dtype q_dtype, const void* key_cache,
+                                   const void* value_cache, float k_scale, float v_scale,
+                                   pa_layout layout, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                   int32_t num_blocks, float scale, int32_t partition_size,
+                                   void* workspace, size_t workspace_bytes_, void* stream) {
+  if (!finite_positive(k_scale) || !finite_positive(v_scale))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_fp8: scales must be positive and finite");
+  pa::DecodeArgs a;
+  pa_status st = decode_prepare("pa_decode_fp8", out, out_dtype, query, q_dtype, key_cache,
+                                value_cache, PA_FP8_E4M3, layout, block_tables,
+                                max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                                num_heads, num_kv_heads, head_size, block_size, num_blocks, scale,
+                                partition_size, workspace, workspace_bytes_, true, true, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  hipError_t e = pa::launch_decode_main(a, (hipStream_t)stream);
+  if (e == hipSuccess) e = pa::launch_decode_reduce(a, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode_fp8");
 }
 
 extern "C" pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const void* query,
@@ -287,8 +362,10 @@ extern "C" pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const v
                                           size_t workspace_bytes_, void* stream) {
   if (partition_size <= 0)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_partitions: partition_size must be > 0");
+  if (kv_dtype == PA_FP8_E4M3)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_partitions: FP8 caches are read by pa_decode_fp8");
   pa::DecodeArgs a;
-  pa_status st = decode_prepare("pa_decode_partitions", out, out_dtype, query, key_cache,
+  pa_status st = decode_prepare("pa_decode_partitions", out, out_dtype, query, kv_dtype, key_cache,
                                 value_cache, kv_dtype, layout, block_tables, max_blocks_per_seq,
                                 context_lens, max_context_len, num_seqs, num_heads, num_kv_heads,
                                 head_size, block_size, num_blocks, scale, partition_size, workspace,
@@ -307,8 +384,8 @@ extern "C" pa_status pa_decode_reduce(void* out, pa_dtype out_dtype, const int32
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_reduce: partition_size must be > 0");
   pa::DecodeArgs a;
   // the reduce reads no cache: geometry fields are placeholders that pass the checks
-  pa_status st = decode_prepare("pa_decode_reduce", out, out_dtype, nullptr, nullptr, nullptr,
-                                out_dtype == PA_F32 ? PA_F32 : out_dtype, PA_LAYOUT_NHD, nullptr,
+  pa_status st = decode_prepare("pa_decode_reduce", out, out_dtype, nullptr, out_dtype, nullptr,
+                                nullptr, out_dtype, PA_LAYOUT_NHD, nullptr,
                                 max_context_len, context_lens, max_context_len, num_seqs,
                                 num_heads, num_kv_heads, head_size, 1, 1, 1.0f, partition_size,
                                 const_cast<void*>(workspace), workspace_bytes_, true, false, &a);
@@ -364,8 +441,10 @@ extern "C" pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void
                                        int32_t partition_size, void* workspace,
                                        size_t workspace_bytes_, void* stream) {
   const char* fn = "pa_decode_cascade";
+  if (kv_dtype == PA_FP8_E4M3)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: the shared-prefix pass needs bf16 or f16 caches");
   pa::DecodeArgs a;
-  pa_status st = decode_prepare(fn, out, out_dtype, query, key_cache, value_cache, kv_dtype, layout,
+  pa_status st = decode_prepare(fn, out, out_dtype, query, kv_dtype, key_cache, value_cache, kv_dtype, layout,
                                 block_tables, max_blocks_per_seq, context_lens, max_context_len,
                                 num_seqs, num_heads, num_kv_heads, head_size, block_size,
                                 num_blocks, scale, 0, nullptr, 0, true, true, &a);
@@ -450,7 +529,7 @@ extern "C" pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query
       max_blocks_per_seq < 0 || num_blocks <= 0)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: negative size or no blocks");
   if (kv_dtype != PA_BF16 && kv_dtype != PA_F16)
-    return pa_fail(valid_dtype(kv_dtype) ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARGUMENT,
+    return pa_fail(valid_storage(kv_dtype) ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARGUMENT,
                    "pa_prefill: kv dtype must be bf16 or f16");
   if (out_dtype != PA_F32 && out_dtype != kv_dtype)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: out dtype must be f32 or the kv dtype");

@@ -29,6 +29,13 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t 
                                     const int64_t* slot_mapping, int32_t num_tokens,
                                     const PoolGeom& g, int elem_bytes, hipStream_t stream);
 
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, pa_dtype src_dtype,
+                                        int64_t key_row_stride, int64_t value_row_stride,
+                                        void* key_cache, void* value_cache,
+                                        const int64_t* slot_mapping, int32_t num_tokens,
+                                        const PoolGeom& g, float k_scale, float v_scale,
+                                        hipStream_t stream);
+
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
                               int32_t num_pairs, int64_t block_bytes, hipStream_t stream);
 
@@ -38,7 +45,10 @@ struct DecodeArgs {
   const void* query;
   const void* key_cache;
   const void* value_cache;
-  pa_dtype kv_dtype;
+  pa_dtype kv_dtype;        // cache element type
+  pa_dtype q_dtype;         // query type (kv_dtype unless the cache is FP8)
+  float k_scale = 1.f;      // FP8 caches: stored code value * scale = element
+  float v_scale = 1.f;
   const int32_t* block_tables;
   int32_t max_blocks_per_seq;
   const int32_t* context_lens;

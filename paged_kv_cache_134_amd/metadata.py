@@ -20,7 +20,7 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-from . import NHD, BlockPool, pa_copy_blocks, pa_reshape_and_cache
+from . import NHD, BlockPool, pa_copy_blocks, pa_reshape_and_cache, pa_reshape_and_cache_fp8
 
 _CHUNK_ROWS = 16384  # rows per set-up upload
 
@@ -46,6 +46,8 @@ def to_device(raw: np.ndarray, dtype: str, device="cuda"):
 
 def nan_pool(shape, dtype: str, device="cuda"):
     torch = _torch()
+    if dtype == "e4m3":  # code 0xFF is NaN
+        return torch.full(shape, 255, dtype=torch.uint8, device=device)
     if dtype == "f32":
         return torch.full(shape, -1, dtype=torch.int32, device=device).view(torch.float32)
     return torch.full(shape, -1, dtype=torch.int16, device=device).view(torch_dtype(dtype))
@@ -70,6 +72,9 @@ class DeviceWorkload:
     step_slots_host: Optional[np.ndarray] = None
     query: object = None
     query_start_loc: object = None  # device int32 [S+1] (prefill)
+    kv_dtype: Optional[str] = None  # "e4m3": FP8 pools written by the quantising write
+    k_scale: float = 1.0
+    v_scale: float = 1.0
     notes: dict = field(default_factory=dict)
 
     @property
@@ -123,20 +128,32 @@ def _write_rows(dw: "DeviceWorkload", k: np.ndarray, v: np.ndarray, slots: np.nd
         kd = to_device(k[a:b], w.dtype)
         vd = to_device(v[a:b], w.dtype)
         sd = torch.from_numpy(np.ascontiguousarray(slots[a:b], dtype=np.int64)).cuda()
-        pa_reshape_and_cache(kd, vd, dw.key_cache, dw.value_cache, sd, dw.layout)
+        _write(dw, kd, vd, sd)
+
+
+def _write(dw: "DeviceWorkload", k, v, slots) -> None:
+    if dw.kv_dtype == "e4m3":
+        pa_reshape_and_cache_fp8(k, v, dw.key_cache, dw.value_cache, slots, dw.k_scale,
+                                 dw.v_scale, dw.layout)
+    else:
+        pa_reshape_and_cache(k, v, dw.key_cache, dw.value_cache, slots, dw.layout)
 
 
 def setup(w, layout: int = NHD, write_step: bool = False, max_blocks: Optional[int] = None,
-          device="cuda") -> DeviceWorkload:
+          device="cuda", kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+          v_scale: float = 1.0) -> DeviceWorkload:
     """Allocate, fill the pools with every position that is not a row of the
-    step, and stage the step's inputs on the device."""
+    step, and stage the step's inputs on the device.  kv_dtype "e4m3": FP8
+    pools, every row written by the quantising write with k_scale / v_scale
+    (queries and new rows keep the workload's dtype)."""
     torch = _torch()
     pool, sids, seq_slots, copies, bt = allocate(w, max_blocks)
     dw = DeviceWorkload(w=w, layout=layout, pool=pool, seq_ids=sids, seq_slots=seq_slots,
-                        copies=copies, block_tables_host=bt)
+                        copies=copies, block_tables_host=bt, kv_dtype=kv_dtype,
+                        k_scale=float(k_scale), v_scale=float(v_scale))
     shape = ((w.NB + 1, w.bs, w.Hkv, w.D) if layout == NHD else (w.NB + 1, w.Hkv, w.bs, w.D))
-    dw.key_cache = nan_pool(shape, w.dtype, device)
-    dw.value_cache = nan_pool(shape, w.dtype, device)
+    dw.key_cache = nan_pool(shape, kv_dtype or w.dtype, device)
+    dw.value_cache = nan_pool(shape, kv_dtype or w.dtype, device)
     # step rows and their slots
     step = np.full(w.T, -1, np.int64)
     step_pos = {}
@@ -185,5 +202,4 @@ def setup(w, layout: int = NHD, write_step: bool = False, max_blocks: Optional[i
 
 def write_step_rows(dw: DeviceWorkload) -> None:
     """The step's cache write: the new rows through their slot_mapping."""
-    pa_reshape_and_cache(dw.step_k, dw.step_v, dw.key_cache, dw.value_cache, dw.step_slots,
-                         dw.layout)
+    _write(dw, dw.step_k, dw.step_v, dw.step_slots)

@@ -84,6 +84,45 @@ def test_argument_errors_enqueue_nothing():
                                     ctypes.c_void_p(256), 3, 8, 128, 16, 4, 1, 0, None) == 1
 
 
+def test_fp8_argument_errors():
+    """Host checks of the FP8 entry points; every call fails (or is empty)
+    before anything is launched."""
+    lib = P._lib
+    v = ctypes.c_void_p(256)
+    F8, BF, F16, F32 = P.PA_FP8_E4M3, P.PA_BF16, P.PA_F16, P.PA_F32
+
+    def write(src=BF, stride=1024, hs=128, ks=0.5, vs=0.5, n=3, ptr=v):
+        return lib.pa_reshape_and_cache_fp8(ptr, ptr, src, stride, stride, ptr, ptr, ptr, n, 8, hs,
+                                            16, 4, 0, ks, vs, None)
+
+    assert write(ks=0.0) == 1 and write(vs=-1.0) == 1
+    assert write(ks=float("inf")) == 1 and write(vs=float("nan")) == 1
+    assert write(src=F8) == 1                 # the source is never FP8
+    assert write(hs=24, stride=192) == 2      # head_size not a multiple of 16
+    assert write(stride=1001) == 1            # row stride below a row
+    assert write(ptr=None) == 1               # null pointers with rows to write
+    assert write(n=0, ptr=None) == 0          # nothing to write
+
+    def dec(q=BF, out=F32, ks=0.5, ps=0, ws=None, n=1):
+        return lib.pa_decode_fp8(v, out, v, q, v, v, ks, 0.5, 0, v, 64, v, 1024, n, 8, 8, 128, 16,
+                                 4, 1.0, ps, ws, 0, None)
+
+    assert dec(ks=0.0) == 1
+    assert dec(q=F8) == 1 and dec(q=F32) == 1  # queries are bf16 or f16
+    assert dec(q=BF, out=F16) == 1             # out is f32 or the query type
+    assert dec(ps=512) == 3                    # split-K without workspace
+    assert dec(n=0) == 0
+    # the 16-bit entry points point FP8 caches elsewhere
+    assert lib.pa_decode(v, 0, v, v, v, F8, 0, v, 64, v, 1024, 1, 8, 8, 128, 16, 4, 1.0, 0, None, 0,
+                         None) == 1
+    assert lib.pa_decode_partitions(v, 0, v, v, v, F8, 0, v, 64, v, 1024, 1, 8, 8, 128, 16, 4, 1.0,
+                                    512, None, 0, None) == 2
+    assert lib.pa_prefill(v, 0, v, v, v, F8, 0, v, 1, v, v, 1, 1, 1, 1, 8, 8, 128, 16, 4, 1.0,
+                          None) == 2
+    assert lib.pa_decode_cascade(v, 0, v, v, v, F8, 0, v, 200, v, 3000, 1792, 100, 32, 32, 128,
+                                 256, 300, 1.0, -1, v, 1 << 30, None) == 2
+
+
 def test_cascade_argument_errors_and_workspace():
     """pa_decode_cascade's host checks (no device needed)."""
     lib = P._lib
