@@ -12,6 +12,9 @@ head size 128, bf16, block size 16, context lengths U[200, 2048], 71 write
 rows of which 7 are padding).  Inputs are seeded synthetic data already
 resident in device memory when the timed region starts.
 
+--kv fp8 runs a decode workload over FP8 (E4M3) pools: the cache write
+quantises, decode reads one byte per element.
+
 Prints ONE JSON line.  `value` = algorithmic KV bytes read per step / step
 time (GB/s) for decode, algorithmic flops / step time (TFLOP/s) for prefill.
 `roofline` covers the dominant kernel, timed with HIP events recorded on the
@@ -63,6 +66,9 @@ def parse():
     ap.add_argument("--cascade", action="store_true",
                     help="shared-prefix decode workloads: attend the common blocks once "
                          "(pa_decode_cascade)")
+    ap.add_argument("--kv", choices=["native", "fp8"], default="native",
+                    help="decode workloads: keep the workload's cache type, or FP8 (E4M3) pools "
+                         "written by the quantising cache write")
     ap.add_argument("--partition", type=int, default=-1,
                     help="decode partition size (-1 auto, 0 single pass)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -109,15 +115,20 @@ def main():
     cfg = args.config if not args.config.isdigit() else int(args.config)
     w = workloads.make(cfg)
     layout = P.NHD if args.layout == "nhd" else P.HND
+    fp8 = args.kv == "fp8"
+    if fp8 and (w.kind != "decode" or args.cascade or w.dtype == "f32"):
+        raise SystemExit("--kv fp8 needs a bf16 decode workload without --cascade")
+    ks, vs = workloads.FP8_K_SCALE, workloads.FP8_V_SCALE
     torch.cuda.set_device(0)
     t0 = time.time()
-    dw = M.setup(w, layout=layout)
+    dw = (M.setup(w, layout=layout, kv_dtype="e4m3", k_scale=ks, v_scale=vs) if fp8
+          else M.setup(w, layout=layout))
     torch.cuda.synchronize()
     log(f"[bench] set-up of {w.name} took {time.time() - t0:.1f}s")
     stream = torch.cuda.current_stream()
 
     S, H, Hkv, D = w.S, w.H, w.Hkv, w.D
-    eb = w.elem_bytes
+    eb = 1 if fp8 else w.elem_bytes  # bytes per cached element
     lens = w.context_lens.astype(np.int64)
     kv_bytes = int(lens.sum()) * Hkv * D * 2 * eb
     out = torch.empty(w.query_shape, dtype=torch.float32, device="cuda")
@@ -150,7 +161,7 @@ def main():
         work_units = S
     elif w.kind == "decode":
         ps = args.partition if args.partition >= 0 else P.pa_decode_auto_partition(
-            S, H, Hkv, P.KV_DTYPE[w.dtype],
+            S, H, Hkv, P.PA_FP8_E4M3 if fp8 else P.KV_DTYPE[w.dtype],
             dw.max_context_len, int(lens.sum()))
         ws = None
         if ps > 0:
@@ -161,12 +172,23 @@ def main():
             ev[0].record(stream)
             M.write_step_rows(dw)
             ev[1].record(stream)
-            if ps > 0:
+            if ps > 0 and fp8:
+                P.pa_decode_partitions_fp8(out, dw.query, dw.key_cache, dw.value_cache,
+                                           dw.block_tables, dw.context_lens, dw.max_context_len,
+                                           w.scale, ks, vs, ps, ws, layout=layout)
+                ev[2].record(stream)
+                P.pa_decode_reduce(out, dw.context_lens, dw.max_context_len, Hkv, ps, ws)
+            elif ps > 0:
                 P.pa_decode_partitions(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
                                        dw.context_lens, dw.max_context_len, w.scale, ps, ws,
                                        layout=layout)
                 ev[2].record(stream)
                 P.pa_decode_reduce(out, dw.context_lens, dw.max_context_len, Hkv, ps, ws)
+            elif fp8:
+                P.pa_decode_fp8(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                dw.context_lens, dw.max_context_len, w.scale, ks, vs,
+                                layout=layout, partition_size=0)
+                ev[2].record(stream)
             else:
                 P.pa_decode(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
                             dw.context_lens, dw.max_context_len, w.scale, layout=layout,
@@ -225,13 +247,19 @@ def main():
     kernels_us = {k: round(t * 1e3, 3) for k, t in zip(kinds, kern_ms) if k}
 
     # sampled parity of the last step's output against the oracle's plain definition
+    # (FP8 pools: the oracle's codes of the same rows, read back times the scales)
     from oracle import attention as A
+    from oracle import fp8 as F8
     got = out.cpu().numpy()
     errs = []
     sample_seqs = sorted({0, S // 2, S - 1}) if w.kind == "decode" else sorted({0, S - 1})
     for s in sample_seqs:
         K, V = w.kv(s)
-        Kf, Vf = A.bits_to_f64(K, w.dtype), A.bits_to_f64(V, w.dtype)
+        if fp8:
+            Kf = F8.dequantize(F8.quantize(K, w.dtype, ks), ks)
+            Vf = F8.dequantize(F8.quantize(V, w.dtype, vs), vs)
+        else:
+            Kf, Vf = A.bits_to_f64(K, w.dtype), A.bits_to_f64(V, w.dtype)
         qf = A.bits_to_f64(w.query, w.dtype)
         for h in sorted({0, H - 1}):
             if w.kind == "decode":
@@ -271,21 +299,24 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
         alg = {"flops_per_step": flops, "causal_pairs_per_head": pairs}
     roof["kernel"] = kinds[dominant]
-    roof["traffic"] = traffic_from_profile(w.name, kind_src)
+    prof_name = w.name + ("-e4m3" if fp8 else "")
+    roof["traffic"] = traffic_from_profile(prof_name, kind_src)
     roof["kernel_source_sha"] = source_sha(kind_src)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds, unit)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds, unit,
+                                                         (ks, vs) if fp8 else None)
     pcache = prefix_cache_probe(w, P) if w.prefix_len >= w.bs else None
 
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
+        "dtype": "e4m3 kv, bf16 q, fp32 accumulate" if fp8 else w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
                    "head_size": D, "block_size": w.bs, "layout": args.layout.upper(),
                    "context_tokens": int(lens.sum()), "write_rows": w.T,
                    "partition_size": ps, "seed": w.seed,
+                   **({"kv_cache_dtype": "e4m3", "k_scale": ks, "v_scale": vs} if fp8 else {}),
                    **({"path": "cascade", **cascade} if cascade else {})},
         "tokens_per_s": round(work_units / (ms_per_step * 1e-3), 1),
         "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4) if unit == "GB/s" else None,
@@ -318,13 +349,14 @@ def prefix_cache_probe(w, P):
             "host_us_per_sequence": round(us, 2)}
 
 
-def cpu_baseline(w, budget_s: float, unit: str):
+def cpu_baseline(w, budget_s: float, unit: str, fp8_scales=None):
     """The fp64 oracle on a bounded sample of the workload, one host thread.
 
     The oracle's pool is built untimed.  Timed: the oracle cache write of the
     step's rows (charged pro rata to the sampled sequences) plus the oracle
     decode / prefill of whole sequences taken in order until the CPU budget
-    is spent.  Reported in the metric's unit over the sample's own work."""
+    is spent.  Reported in the metric's unit over the sample's own work.
+    fp8_scales (k_scale, v_scale): FP8 pools, quantising write."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -332,13 +364,19 @@ def cpu_baseline(w, budget_s: float, unit: str):
     from oracle.state import build_pool, build_state
 
     st = build_state(w)
-    kc, vc = build_pool(w, st)
+    ks, vs = fp8_scales or (1.0, 1.0)
+    kv = "e4m3" if fp8_scales else None
+    kc, vc = build_pool(w, st, kv_dtype=kv, k_scale=ks, v_scale=vs)
     K, V = w.new_rows()
     lens = w.context_lens.astype(np.int64)
+    eb = 1 if fp8_scales else w.elem_bytes
     done, secs, work = [], 0.0, 0.0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        kc, vc = A.write_ref(kc, vc, K, V, st.step_slots, w.bs)
+        if fp8_scales:
+            kc, vc = A.write_ref_fp8(kc, vc, K, V, st.step_slots, w.bs, w.dtype, ks, vs)
+        else:
+            kc, vc = A.write_ref(kc, vc, K, V, st.step_slots, w.bs)
         t_write = time.perf_counter() - t0
         # whole sequences in order, passing over the batch again while the
         # budget lasts (a short workload is timed over several passes)
@@ -347,8 +385,8 @@ def cpu_baseline(w, budget_s: float, unit: str):
             t0 = time.perf_counter()
             if w.kind == "decode":
                 A.decode_ref(w.query[s:s + 1], kc, vc, st.block_tables[s:s + 1], lens[s:s + 1],
-                             w.scale, w.bs, w.dtype)
-                work += float(lens[s]) * w.Hkv * w.D * 2 * w.elem_bytes
+                             w.scale, w.bs, w.dtype, kv_dtype=kv, k_scale=ks, v_scale=vs)
+                work += float(lens[s]) * w.Hkv * w.D * 2 * eb
             else:
                 a, b = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
                 A.prefill_ref(w.query[a:b], kc, vc, st.block_tables[s:s + 1],

@@ -214,6 +214,23 @@ pa_status pa_decode_fp8(void* out, pa_dtype out_dtype, const void* query, pa_dty
                         size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_partitions_fp8 -- the partition half of pa_decode_fp8 with
+ * partition_size > 0 (contract of pa_decode_partitions, with the scales and
+ * query type of pa_decode_fp8; the partials already carry v_scale).
+ * pa_decode_reduce finishes it: pa_decode_fp8 runs exactly these two.
+ */
+pa_status pa_decode_partitions_fp8(void* out, pa_dtype out_dtype, const void* query,
+                                   pa_dtype q_dtype, const void* key_cache,
+                                   const void* value_cache, float k_scale, float v_scale,
+                                   pa_layout layout, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t max_context_len, int32_t num_seqs,
+                                   int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                   float scale, int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * The two halves of split-K decode, for callers that schedule or time them
  * separately; pa_decode with partition_size > 0 runs exactly these two.
  *

@@ -44,7 +44,7 @@ NHD, HND = 0, 1
 EXPORTED = [
     "pa_status_string", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_fp8",
     "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode",
-    "pa_decode_fp8", "pa_decode_partitions",
+    "pa_decode_fp8", "pa_decode_partitions_fp8", "pa_decode_partitions",
     "pa_decode_reduce", "pa_decode_cascade_workspace_size", "pa_decode_cascade", "pa_prefill",
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
     "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
@@ -69,6 +69,9 @@ _sig = {
                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _f32, _f32, _i32, _vp, _i32, _vp,
                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_partitions_fp8": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _f32, _f32, _i32, _vp, _i32,
+                                        _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                        _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
@@ -254,6 +257,24 @@ def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens
                   layout: int = NHD, partition_size: int = -1, workspace=None,
                   stream=None) -> None:
     """Decode attention over E4M3 pools (uint8); query bf16/f16, out float32 or the query type."""
+    _decode_fp8("pa_decode_fp8", out, query, key_cache, value_cache, block_tables, context_lens,
+                max_context_len, scale, k_scale, v_scale, layout, partition_size, workspace,
+                stream)
+
+
+def pa_decode_partitions_fp8(out, query, key_cache, value_cache, block_tables, context_lens,
+                             max_context_len: int, scale: float, k_scale: float, v_scale: float,
+                             partition_size: int, workspace, layout: int = NHD,
+                             stream=None) -> None:
+    """Partition half of split-K decode over E4M3 pools (finish with pa_decode_reduce)."""
+    _decode_fp8("pa_decode_partitions_fp8", out, query, key_cache, value_cache, block_tables,
+                context_lens, max_context_len, scale, k_scale, v_scale, layout, partition_size,
+                workspace, stream)
+
+
+def _decode_fp8(fn, out, query, key_cache, value_cache, block_tables, context_lens,
+                max_context_len, scale, k_scale, v_scale, layout, partition_size, workspace,
+                stream) -> None:
     torch = _torch()
     nb, bs, hkv, d = _geom(key_cache, layout)
     S, H, D = query.shape
@@ -266,7 +287,7 @@ def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens
     ws_ptr, ws_bytes = (None, 0)
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
-    _check("pa_decode_fp8", _lib.pa_decode_fp8(
+    _check(fn, getattr(_lib, fn)(
         _dev(out, "out"), _dtype_code(out), _dev(query, "query"), _dtype_code(query),
         _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), float(k_scale),
         float(v_scale), layout, _dev(block_tables, "block_tables", torch.int32),

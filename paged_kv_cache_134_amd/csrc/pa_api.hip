@@ -325,6 +325,38 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode");
 }
 
+namespace {
+
+// pa_decode_fp8 (with_reduce) and pa_decode_partitions_fp8.
+pa_status decode_fp8(const char* fn, bool with_reduce, void* out, pa_dtype out_dtype,
+                     const void* query, pa_dtype q_dtype, const void* key_cache,
+                     const void* value_cache, float k_scale, float v_scale, pa_layout layout,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                     int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                     void* workspace, size_t workspace_bytes_, void* stream) {
+  char msg[160];
+  if (!finite_positive(k_scale) || !finite_positive(v_scale)) {
+    std::snprintf(msg, sizeof msg, "%s: scales must be positive and finite", fn);
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, msg);
+  }
+  pa::DecodeArgs a;
+  pa_status st = decode_prepare(fn, out, out_dtype, query, q_dtype, key_cache, value_cache,
+                                PA_FP8_E4M3, layout, block_tables, max_blocks_per_seq,
+                                context_lens, max_context_len, num_seqs, num_heads, num_kv_heads,
+                                head_size, block_size, num_blocks, scale, partition_size,
+                                workspace, workspace_bytes_, true, true, &a);
+  if (st != PA_OK || num_seqs == 0 || (!with_reduce && a.partition_size == 0)) return st;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  hipError_t e = pa::launch_decode_main(a, (hipStream_t)stream);
+  if (e == hipSuccess && with_reduce) e = pa::launch_decode_reduce(a, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, fn);
+}
+
+}  // namespace
+
 extern "C" pa_status pa_decode_fp8(void* out, pa_dtype out_dtype, const void* query,
                                    pa_dtype q_dtype, const void* key_cache,
                                    const void* value_cache, float k_scale, float v_scale,
@@ -334,20 +366,26 @@ extern "C" pa_status pa_decode_fp8(void* out, pa_dtype out_dtype, const void* qu
                                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                                    int32_t num_blocks, float scale, int32_t partition_size,
                                    void* workspace, size_t workspace_bytes_, void* stream) {
-  if (!finite_positive(k_scale) || !finite_positive(v_scale))
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_fp8: scales must be positive and finite");
-  pa::DecodeArgs a;
-  pa_status st = decode_prepare("pa_decode_fp8", out, out_dtype, query, q_dtype, key_cache,
-                                value_cache, PA_FP8_E4M3, layout, block_tables,
-                                max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                                num_heads, num_kv_heads, head_size, block_size, num_blocks, scale,
-                                partition_size, workspace, workspace_bytes_, true, true, &a);
-  if (st != PA_OK || num_seqs == 0) return st;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  hipError_t e = pa::launch_decode_main(a, (hipStream_t)stream);
-  if (e == hipSuccess) e = pa::launch_decode_reduce(a, (hipStream_t)stream);
-  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode_fp8");
+  return decode_fp8("pa_decode_fp8", true, out, out_dtype, query, q_dtype, key_cache, value_cache,
+                    k_scale, v_scale, layout, block_tables, max_blocks_per_seq, context_lens,
+                    max_context_len, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                    num_blocks, scale, partition_size, workspace, workspace_bytes_, stream);
+}
+
+extern "C" pa_status pa_decode_partitions_fp8(
+    void* out, pa_dtype out_dtype, const void* query, pa_dtype q_dtype, const void* key_cache,
+    const void* value_cache, float k_scale, float v_scale, pa_layout layout,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes_, void* stream) {
+  if (partition_size <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_partitions_fp8: partition_size must be > 0");
+  return decode_fp8("pa_decode_partitions_fp8", false, out, out_dtype, query, q_dtype, key_cache,
+                    value_cache, k_scale, v_scale, layout, block_tables, max_blocks_per_seq,
+                    context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_size,
+                    block_size, num_blocks, scale, partition_size, workspace, workspace_bytes_,
+                    stream);
 }
 
 extern "C" pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const void* query,
