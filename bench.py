@@ -40,14 +40,23 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16/fp16 MFMA, AMD published
 # source file of each timed kernel (its hash ties a committed counter profile
 # to the kernel it was taken on)
-KERNEL_SOURCES = {"decode_head": "decode_head.hip", "decode_group": "decode_group.hip",
-                  "prefill": "prefill.hip", "write": "cache_ops.hip"}
+# (with the headers they include, so a change to shared device code also
+# retires the profile)
+KERNEL_SOURCES = {
+    "decode_head": ["decode_head.hip", "decode_common.h", "kernel_common.h"],
+    "decode_group": ["decode_group.hip", "decode_common.h", "kernel_common.h"],
+    "decode_group_fp8": ["decode_group_fp8.hip", "decode_common.h", "kernel_common.h"],
+    "prefill": ["prefill.hip", "kernel_common.h"],
+}
 
 
-def decode_kernel_kind(w) -> str:
-    """Which decode kernel the library dispatches for this workload (grouped
-    kernel for group sizes 4, 8, 16 with 16-bit caches, else per-head)."""
-    return "decode_group" if w.dtype != "f32" and w.G in (4, 8, 16) else "decode_head"
+def decode_kernel_kind(w, fp8: bool = False) -> str:
+    """Which decode kernel the library dispatches for this workload: the
+    grouped kernels for group sizes 4, 8, 16 (LDS-staged for 16-bit caches,
+    matrix-core for FP8), the per-head kernel otherwise."""
+    if w.dtype == "f32" or w.G not in (4, 8, 16):
+        return "decode_head"
+    return "decode_group_fp8" if fp8 else "decode_group"
 
 
 def log(*a):
@@ -78,9 +87,11 @@ def parse():
 
 
 def source_sha(kind: str) -> str:
-    path = os.path.join(ROOT, "paged_kv_cache_134_amd", "csrc", KERNEL_SOURCES[kind])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "paged_kv_cache_134_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(workload: str, kind: str):
@@ -285,7 +296,7 @@ def main():
         # the cascade's roofline counts the bytes it must read (common blocks
         # once); the value keeps the logical KV bytes of the plain method
         achieved = (cascade["unique_kv_bytes_per_step"] if cascade else kv_bytes) / (dom_ms * 1e-3) / 1e9
-        kind_src = decode_kernel_kind(w)
+        kind_src = decode_kernel_kind(w, fp8)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
         alg = {"kv_bytes_per_step": kv_bytes}

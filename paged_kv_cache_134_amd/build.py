@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libpagedattn.so")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["pa_api.hip", "cache_ops.hip", "decode.hip", "decode_head.hip", "decode_group.hip",
-               "prefill.hip"]
+               "decode_group_fp8.hip", "prefill.hip"]
 CXX_SOURCES = ["pool.cpp"]
 
 

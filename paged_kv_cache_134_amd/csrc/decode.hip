@@ -7,9 +7,11 @@
 // max/sum rescaling) and the block-wise online softmax of the "Paged
 // attention" post (k4i.top, attention over non-contiguous blocks).
 //
-// Two kernels share one contract; the dispatcher picks by GQA group size G
+// Three kernels share one contract; the dispatcher picks by GQA group size G
 // and element type: the per-head kernel (decode_head.hip) for G <= 2 and
-// every fp32 cache, the grouped kernel (decode_group.hip) otherwise.  Both
+// every fp32 cache, the LDS-staged grouped kernel (decode_group.hip) for
+// 16-bit caches otherwise, and the matrix-core grouped kernel
+// (decode_group_fp8.hip) for FP8 caches otherwise.  All
 // use one workgroup of 4 waves per (sequence, kv head, partition), read each
 // kv head's K/V rows once for all G query heads of its group, never load a
 // token at or past the context length (so NaN in unused slots cannot reach

@@ -90,7 +90,8 @@ __device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int pa
 // partitions or 1).
 hipError_t launch_head(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st);
 hipError_t launch_group(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st);
-// FP8 (E4M3) caches; qt = query type (bf16 or f16).
+// FP8 (E4M3) caches; qt = query type (bf16 or f16).  Group sizes 1 and 2 take
+// the per-head kernel, 4, 8 and 16 the matrix-core grouped kernel.
 hipError_t launch_head_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st);
 hipError_t launch_group_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st);
 

@@ -1,5 +1,4 @@
-// Paged decode, grouped kernel (group size 4, 8 or 16 with bf16, f16 or FP8
-// caches).
+// Paged decode, grouped kernel (group size 4, 8 or 16 with bf16/f16 caches).
 //
 // One workgroup of 4 waves per (sequence, kv head, partition) reads the kv
 // head's K/V rows once for all G query heads of its group (contract and
@@ -40,28 +39,21 @@ constexpr int kBtWin = 256;  // block-table entries staged in LDS at a time
 template <int G, int D>
 constexpr int kLdsMinWaves = (G >= 16 && D >= 128) ? 2 : 4;
 
-// FP8: the caches hold E4M3 codes and DT is the query's type.  A global
-// 16-byte piece is then 16 elements; it is converted (exactly) on its way
-// into LDS, K to DT and V to f16, so LDS, QK and PV are as for a 16-bit
-// cache, and no V value can leave f16 range.
-template <pa_dtype DT, int D, int G, bool OFF32, bool FP8 = false>
+template <pa_dtype DT, int D, int G, bool OFF32>
 __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_lds_kernel(
     const DecodeParams p) {
   static_assert(DT != PA_F32, "LDS kernel takes 16-bit elements");
   static_assert(G % kDecodeWaves == 0, "G must be a multiple of 4");
-  constexpr int CB = FP8 ? 1 : 2;                  // cache bytes per element
-  constexpr int RC = D / 8;                        // 16-byte LDS pieces per row
-  constexpr int RG = D * CB / 16;                  // 16-byte global pieces per row
-  constexpr int PIECES = kChunk * RG;              // global pieces per chunk of K (or V)
+  constexpr int RC = D / 8;                        // 16-byte pieces per row
+  constexpr int PIECES = kChunk * RC;              // pieces per chunk of K (or V)
   constexpr int PPT = PIECES / kDecodeThreads;     // pieces per thread per tensor
-  constexpr int RSTEP = kDecodeThreads / RG;       // rows between a thread's pieces
-  constexpr bool WIDE_CHECK = DT == PA_BF16 && !FP8;  // V may leave f16 range
+  constexpr int RSTEP = kDecodeThreads / RC;       // rows between a thread's pieces
   constexpr int HPW = G / kDecodeWaves;            // query heads per wave in QK
   constexpr int DPL = D / 32;                      // output columns per lane in PV
   constexpr int NPI = kChunk / kDecodeWaves / 4;   // PV token-pair iterations per wave
   static_assert(PPT * kDecodeThreads == PIECES, "chunk must split evenly");
   constexpr int KSTR = RC + 1;                     // K row stride in pieces (padded)
-  __shared__ uint4 sKV[kChunk * KSTR + kChunk * RC];  // K (padded rows) then V; reused at the end
+  __shared__ uint4 sKV[kChunk * KSTR + PIECES];    // K (padded rows) then V; reused at the end
   __shared__ __align__(16) _Float16 sPh[kChunk / 2][G][2];  // probabilities, token pairs interleaved
   __shared__ float sAlpha[G];                      // per-head rescale of this chunk
   __shared__ int32_t sResc[kDecodeWaves];          // wave w moved a running max this chunk
@@ -101,12 +93,12 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
   // clamped to the last row (a valid, finite row the chunk loads anyway) and
   // masked where they are used, so every load is unconditional.  Block ids
   // come from the LDS window, so no load waits on another global load.
-  const int prow = tid / RG;
-  const int pcol = tid % RG;
-  const int64_t lane_off = (int64_t)kvh * p.head_stride + pcol * (16 / CB);  // elements
-  const uint32_t blk_b = (uint32_t)(p.blk_stride * CB);
-  const uint32_t tok_b = (uint32_t)(p.tok_stride * CB);
-  const uint32_t lane_b = (uint32_t)(lane_off * CB);
+  const int prow = tid / RC;
+  const int pcol = tid % RC;
+  const int64_t lane_off = (int64_t)kvh * p.head_stride + pcol * 8;  // elements
+  const uint32_t blk_b = (uint32_t)(p.blk_stride * 2);
+  const uint32_t tok_b = (uint32_t)(p.tok_stride * 2);
+  const uint32_t lane_b = (uint32_t)(lane_off * 2);
 
   const int half = lane / 32;  // PV: token parity within a pair
   const int dl = lane % 32;    // PV: output columns dl*DPL .. +DPL-1
@@ -141,8 +133,8 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
         } else {
           const int64_t off = (int64_t)blk[r] * p.blk_stride +
                               (int64_t)(tc[r] & bs_mask) * p.tok_stride + lane_off;
-          kr[r] = load_nt(p.key_cache + off * CB);
-          vr[r] = load_nt(p.value_cache + off * CB);
+          kr[r] = load_nt(p.key_cache + off * 2);
+          vr[r] = load_nt(p.value_cache + off * 2);
         }
       }
     };
@@ -161,7 +153,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
 
     __syncthreads();  // LDS of an abandoned pass is no longer read
     stage_bt();
-    if (WIDE_CHECK && tid == 0) sVwide[0] = sVwide[1] = 0;
+    if (F16 && tid == 0) sVwide[0] = sVwide[1] = 0;
     __syncthreads();  // window staged
     // One chunk in flight in registers while the previous one is consumed
     // from LDS.  ci counts chunks (its parity selects the V-range flag).
@@ -169,22 +161,10 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
       __syncthreads();  // previous chunk fully consumed (also every read of the window)
 #pragma unroll
       for (int r = 0; r < PPT; ++r) {  // piece tid + 256 r: row prow + RSTEP r, column pcol
-        if constexpr (FP8) {
-          uint4 k0, k1, v0, v1;
-          fp8x16_to_pairs<DT>(kr[r], k0, k1);
-          fp8x16_to_pairs<PA_F16>(vr[r], v0, v1);
-          uint4* kd = &sK[(prow + RSTEP * r) * KSTR + 2 * pcol];
-          uint4* vd = &sV[(prow + RSTEP * r) * RC + 2 * pcol];
-          kd[0] = k0;
-          kd[1] = k1;
-          vd[0] = v0;
-          vd[1] = v1;
-        } else {
-          sK[(prow + RSTEP * r) * KSTR + pcol] = kr[r];
-          sV[tid + kDecodeThreads * r] = vr[r];
-        }
+        sK[(prow + RSTEP * r) * KSTR + pcol] = kr[r];
+        sV[tid + kDecodeThreads * r] = vr[r];
       }
-      if constexpr (F16 && WIDE_CHECK) {
+      if constexpr (F16 && DT == PA_BF16) {
         // largest |v| bit pattern of this thread's V pieces (sign cleared)
         u16x2_t mx = {0, 0};
 #pragma unroll
@@ -203,7 +183,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
         stage_bt();
       }
       __syncthreads();
-      if constexpr (F16 && WIDE_CHECK) {
+      if constexpr (F16 && DT == PA_BF16) {
         if (tid == 0) sVwide[(ci + 1) & 1] = 0;  // its last reader was the previous chunk
         if (__builtin_amdgcn_readfirstlane(sVwide[ci & 1]) != 0) return false;  // uniform
       }
@@ -304,7 +284,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
 #pragma unroll
           for (int c = 0; c < DPL; ++c) {
             const uint32_t xa = wa[c / 2], xb = wb[c / 2];
-            if constexpr (DT == PA_BF16 && !FP8) {
+            if constexpr (DT == PA_BF16) {
               const float fa = __uint_as_float((c & 1) ? (xa & 0xFFFF0000u) : (xa << 16));
               const float fb = __uint_as_float((c & 1) ? (xb & 0xFFFF0000u) : (xb << 16));
               vv[c] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa, fb));
@@ -374,28 +354,26 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
   };
 
   if (!run(std::true_type{})) {
-    if constexpr (WIDE_CHECK) run(std::false_type{});
+    if constexpr (DT == PA_BF16) run(std::false_type{});
   }
 }
 
-template <pa_dtype DT, int D, bool OFF32, bool FP8>
+template <pa_dtype DT, int D, bool OFF32>
 hipError_t launch_lds(const DecodeParams& p, int G, dim3 grid, hipStream_t st) {
   dim3 block(kDecodeThreads);
   switch (G) {
-    case 4: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 4, OFF32, FP8>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 8, OFF32, FP8>), grid, block, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 16, OFF32, FP8>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 4, OFF32>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 8, OFF32>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_lds_kernel<DT, D, 16, OFF32>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <pa_dtype DT, bool FP8 = false>
+template <pa_dtype DT>
 hipError_t launch_d(const DecodeParams& p, int D, int G, dim3 grid, hipStream_t st) {
-  if (D == 64)
-    return p.off32 ? launch_lds<DT, 64, true, FP8>(p, G, grid, st) : launch_lds<DT, 64, false, FP8>(p, G, grid, st);
-  if (D == 128)
-    return p.off32 ? launch_lds<DT, 128, true, FP8>(p, G, grid, st) : launch_lds<DT, 128, false, FP8>(p, G, grid, st);
+  if (D == 64) return p.off32 ? launch_lds<DT, 64, true>(p, G, grid, st) : launch_lds<DT, 64, false>(p, G, grid, st);
+  if (D == 128) return p.off32 ? launch_lds<DT, 128, true>(p, G, grid, st) : launch_lds<DT, 128, false>(p, G, grid, st);
   return hipErrorInvalidValue;
 }
 
@@ -405,14 +383,6 @@ hipError_t launch_group(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 g
   switch (dt) {
     case PA_BF16: return launch_d<PA_BF16>(p, D, G, grid, st);
     case PA_F16: return launch_d<PA_F16>(p, D, G, grid, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_group_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st) {
-  switch (qt) {
-    case PA_BF16: return launch_d<PA_BF16, true>(p, D, G, grid, st);
-    case PA_F16: return launch_d<PA_F16, true>(p, D, G, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,337 @@
+// Paged decode over FP8 (E4M3) caches, grouped kernel (group size 4, 8 or
+// 16; bf16 or f16 queries) on matrix cores.
+//
+// One workgroup of 4 waves per (sequence, kv head, partition), as in the
+// other decode kernels (contract and sources in decode.hip).  The partition
+// is walked in rounds of 64 tokens; wave w takes tokens 16 w .. 16 w + 15 of
+// each round and keeps its own softmax state, so the waves never wait for
+// one another until the final merge.  Per 16-token tile:
+//   QK       S[16 tokens x 16 heads] = K Q^T on v_mfma_f32_16x16x32 (bf16 or
+//            f16 by the query's type).  The A operand comes straight from
+//            the cache into registers (lane = token l % 16 and quarter l / 16
+//            of the row; each load instruction reads 64 contiguous bytes of
+//            every row) and converts exactly from E4M3 to the query's type;
+//            the B operand is the group's query vectors, held in registers
+//            for the whole partition (heads past G are zero).
+//   softmax  a lane holds 4 tokens of head l % 16.  The running maximum
+//            moves only when some score exceeds it by more than 2^8; the
+//            probabilities are rounded to f16 once and the normaliser sums
+//            the rounded values.
+//   PV       the tile's V rows pass through the wave's own LDS region as f16
+//            (exact for every E4M3 value) and are accumulated on f16 v_dot2,
+//            a lane owning D/32 columns of every head (the two half-waves
+//            take alternate token pairs).
+// Each wave keeps two tiles of K/V in flight (the next two rounds) and reads
+// the block ids it needs from the table two rounds ahead of the rows they
+// locate.  The waves' (max, sum, output) states are merged at the end by the
+// log-sum-exp rule.  With 16-bit caches the LDS-staged grouped kernel
+// (decode_group.hip) is faster and is used instead.
+#include <hip/hip_runtime.h>
+
+#include "decode_common.h"
+
+namespace pa {
+namespace dec {
+namespace {
+
+constexpr int kTile = 16;                     // tokens per wave per round
+constexpr int kRound = kTile * kDecodeWaves;  // tokens per workgroup per round
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <pa_dtype DT>
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  if constexpr (DT == PA_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// LDS written by some lanes of a wave and then read by others: keeps the
+// compiler from moving the accesses across (a wave's LDS operations run in
+// order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int G, int D>
+constexpr int kMfmaMinWaves = (G >= 16 && D >= 128) ? 2 : 3;
+
+template <pa_dtype DT, int D, int G, bool OFF32>
+__global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_fp8_mfma_kernel(
+    const DecodeParams p) {
+  static_assert(DT == PA_BF16 || DT == PA_F16, "queries are bf16 or f16");
+  static_assert(G == 4 || G == 8 || G == 16, "group size 4, 8 or 16");
+  constexpr int KB = D / 32;            // MFMA k-blocks of 32 elements
+  constexpr int NLD = D / 64;           // 16-byte loads per lane per row (a quarter row)
+  constexpr int RC = D / 8;             // 16-byte LDS pieces per V row
+  constexpr int VSTR = RC + 1;          // padded LDS row stride in pieces
+  constexpr int DPL = D / 32;           // output columns per lane in PV
+  constexpr int kWaveV = kTile * VSTR;                 // pieces of one wave's V region
+  constexpr int kWaveP = (kTile / 2) * G;              // f16 pairs of one wave's P region
+  constexpr int kLdsMain = (kDecodeWaves * kWaveV) * 16 + kDecodeWaves * kWaveP * 4;
+  constexpr int kLdsMerge = kDecodeWaves * G * D * 4;
+  constexpr int kLds = kLdsMain > kLdsMerge ? kLdsMain : kLdsMerge;
+  __shared__ __align__(16) char smem[kLds];
+  __shared__ float sM[kDecodeWaves][G], sL[kDecodeWaves][G];
+
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int s = blockIdx.x / p.num_kv_heads;
+  const int part = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+
+  const int L = p.context_lens[s];
+  int t0 = 0, t1 = L;
+  if (p.partition_size > 0) {
+    t0 = p.key_begin + part * p.partition_size;
+    if (t0 >= L) return;
+    t1 = min(L, t0 + p.partition_size);
+  }
+
+  const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+  const int lbs = p.log2_bs;
+  const int bs_mask = (1 << lbs) - 1;
+
+  const int tl = lane % kTile;  // QK: token of the tile, and head of the B operand / scores
+  const int q4 = lane / kTile;  // quarter of the row this lane loads
+
+  // Element d held in slot e of MFMA k-block j by lanes of quarter q4: a
+  // lane's 16-byte loads are pieces q4, q4 + 4, ... of the row (16 elements
+  // each), piece i feeding blocks 2 i and 2 i + 1.  The query operand uses
+  // the same map.
+  auto dmap = [&](int j) -> int { return 16 * (q4 + 4 * (j >> 1)) + 8 * (j & 1); };
+
+  // B operand: the query vector of head tl (zero past the group).
+  uint4 qb[KB];
+  {
+    const char* qrow = (const char*)p.query +
+                       (((int64_t)s * p.num_heads + (int64_t)kvh * G + min(tl, G - 1)) * D) * 2;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const uint4 v = load16(qrow + dmap(j) * 2);
+      qb[j] = tl < G ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  const uint32_t blk_b = (uint32_t)p.blk_stride;  // one byte per element
+  const uint32_t tok_b = (uint32_t)p.tok_stride;
+  const int64_t lane_off = (int64_t)kvh * p.head_stride + q4 * 16;  // bytes
+
+  uint4* sV = reinterpret_cast<uint4*>(smem) + wave * kWaveV;
+  uint32_t* sP = reinterpret_cast<uint32_t*>(smem + kDecodeWaves * kWaveV * 16) + wave * kWaveP;
+
+  const int half = lane / 32;  // PV: token parity of the pairs this half-wave takes
+  const int dl = lane % 32;    // PV: output columns dl * DPL .. + DPL - 1
+
+  auto block_of = [&](int ts) -> int32_t { return bt[min(ts + tl, t1 - 1) >> lbs]; };
+  // K and V pieces of the lane's token in tile ts (rows past the end are
+  // clamped to the last row: valid, finite, masked where used)
+  auto fetch = [&](int ts, int32_t blk, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
+    const int t = min(ts + tl, t1 - 1);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (OFF32) {
+        const uint32_t off =
+            (uint32_t)blk * blk_b + (uint32_t)(t & bs_mask) * tok_b + (uint32_t)lane_off + 64 * i;
+        kr[i] = load16(p.key_cache + off);
+        vr[i] = load16(p.value_cache + off);
+      } else {
+        const int64_t off = (int64_t)blk * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride +
+                            lane_off + 64 * i;
+        kr[i] = load16(p.key_cache + off);
+        vr[i] = load16(p.value_cache + off);
+      }
+    }
+  };
+
+  float m_ref = -INFINITY, l_lane = 0.f;  // softmax state of head tl (this wave's tokens)
+  float acc[G][DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+
+  // Consumes tile ts from (kr, vr), then refills them with the tile two
+  // rounds ahead (its block ids were read two rounds ago).
+  auto tile = [&](int ts, uint4 (&kr)[NLD], uint4 (&vr)[NLD], int32_t& blk_ahead) {
+    // ---- K as MFMA A operands (exact E4M3 -> query type), V into LDS as f16
+    uint4 ka[KB];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      fp8x16_to_pairs<DT>(kr[i], ka[2 * i], ka[2 * i + 1]);
+      uint4 v0, v1;
+      fp8x16_to_pairs<PA_F16>(vr[i], v0, v1);
+      sV[tl * VSTR + 2 * (q4 + 4 * i)] = v0;
+      sV[tl * VSTR + 2 * (q4 + 4 * i) + 1] = v1;
+    }
+    if (ts + 2 * kRound - kTile * wave < t1) {
+      fetch(ts + 2 * kRound, blk_ahead, kr, vr);
+      blk_ahead = block_of(ts + 4 * kRound);
+    }
+
+    // ---- QK on matrix cores: the lane holds tokens 4 q4 + r of head tl
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KB; ++j) sc = mfma_16x16x32<DT>(ka[j], qb[j], sc);
+
+    float z[4];
+    bool need = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool valid = tl < G && ts + 4 * q4 + r < t1;
+      z[r] = valid ? sc[r] * p.scale_log2e : -INFINITY;
+      need |= z[r] > m_ref + kLazyRescale;
+    }
+    if (__any(need)) {  // move the running maximum of every head to the tile's
+      float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m_ref, mt);
+      const float alpha = exp2_diff(m_ref, mn);
+      m_ref = mn;
+      l_lane *= alpha;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float a = __shfl(alpha, h);  // lane h holds head h
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[h][e] *= a;
+      }
+    }
+    _Float16 ph[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ph[r] = (_Float16)(z[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref));
+      l_lane += (float)ph[r];
+    }
+    if (tl < G) {  // token pairs (4 q4, 4 q4 + 1) and (4 q4 + 2, 4 q4 + 3) of head tl
+      sP[(2 * q4) * G + tl] = __builtin_bit_cast(uint32_t, f16x2_t{ph[0], ph[1]});
+      sP[(2 * q4 + 1) * G + tl] = __builtin_bit_cast(uint32_t, f16x2_t{ph[2], ph[3]});
+    }
+    wave_lds_sync();
+
+    // ---- PV: token pairs 2 i + half of the tile, D/32 columns of every head
+#pragma unroll
+    for (int i = 0; i < kTile / 4; ++i) {
+      const int pr = 2 * i + half;
+      const char* va = reinterpret_cast<const char*>(sV + (2 * pr) * VSTR) + dl * DPL * 2;
+      const char* vb = va + VSTR * 16;
+      uint32_t wa[DPL / 2], wb[DPL / 2];
+      if constexpr (DPL == 4) {
+        const uint2 a2 = *reinterpret_cast<const uint2*>(va);
+        const uint2 b2 = *reinterpret_cast<const uint2*>(vb);
+        wa[0] = a2.x; wa[1] = a2.y; wb[0] = b2.x; wb[1] = b2.y;
+      } else {
+        wa[0] = *reinterpret_cast<const uint32_t*>(va);
+        wb[0] = *reinterpret_cast<const uint32_t*>(vb);
+      }
+      uint32_t pw[G];
+      const uint4* pq = reinterpret_cast<const uint4*>(sP + pr * G);
+#pragma unroll
+      for (int h4 = 0; h4 < G / 4; ++h4) {
+        const uint4 x = pq[h4];
+        pw[4 * h4] = x.x; pw[4 * h4 + 1] = x.y; pw[4 * h4 + 2] = x.z; pw[4 * h4 + 3] = x.w;
+      }
+      uint32_t vv[DPL];  // (row 2 pr, row 2 pr + 1) f16 pairs per column
+#pragma unroll
+      for (int c = 0; c < DPL; ++c)
+        vv[c] = __builtin_amdgcn_perm(wb[c / 2], wa[c / 2], (c & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < DPL; ++c)
+          acc[h][c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[h]),
+                                             __builtin_bit_cast(f16x2_t, vv[c]), acc[h][c], false);
+    }
+    wave_lds_sync();  // this tile's V and P are consumed before the next tile's stores
+  };
+
+  // Two tile buffers alternate, so two tiles per wave are always in flight.
+  const int ts0 = t0 + kTile * wave;
+  uint4 ka_[NLD], va_[NLD], kb_[NLD], vb_[NLD];
+  fetch(ts0, block_of(ts0), ka_, va_);
+  if (ts0 + kRound - kTile * wave < t1) fetch(ts0 + kRound, block_of(ts0 + kRound), kb_, vb_);
+  int32_t bid_a = block_of(ts0 + 2 * kRound), bid_b = block_of(ts0 + 3 * kRound);
+  for (int ts = ts0; ts - kTile * wave < t1; ts += 2 * kRound) {
+    tile(ts, ka_, va_, bid_a);
+    if (ts + kRound - kTile * wave >= t1) break;
+    tile(ts + kRound, kb_, vb_, bid_b);
+  }
+  // this wave's statistics of head tl (summed over the four quarters)
+  l_lane += __shfl_xor(l_lane, 16);
+  l_lane += __shfl_xor(l_lane, 32);
+  const float m_out = m_ref, l_out = l_lane;
+
+  // ---- merge: half-waves, then waves (log-sum-exp rule)
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
+  if (lane < G) {
+    sM[wave][lane] = m_out;
+    sL[wave][lane] = l_out;
+  }
+  __syncthreads();  // every wave's loop is done: the LDS rows are free
+  float* sAcc = reinterpret_cast<float*>(smem);  // [waves][G][D]
+  if (half == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sAcc[(wave * G + h) * D + dl * DPL + e] = acc[h][e];
+  }
+  __syncthreads();
+  const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
+  for (int i = tid; i < G * D; i += kDecodeThreads) {
+    const int h = i / D, d = i % D;
+    float M = sM[0][h];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sM[w][h]);
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float a = exp2_diff(sM[w][h], M);
+      lsum += a * sL[w][h];
+      o += a * sAcc[(w * G + h) * D + d];
+    }
+    emit(p, head0 + h, part, d, D, M, lsum, o, single_partition(p, L));
+  }
+}
+
+template <pa_dtype DT, int D, bool OFF32>
+hipError_t launch_g(const DecodeParams& p, int G, dim3 grid, hipStream_t st) {
+  dim3 block(kDecodeThreads);
+  switch (G) {
+    case 4: hipLaunchKernelGGL((decode_fp8_mfma_kernel<DT, D, 4, OFF32>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_fp8_mfma_kernel<DT, D, 8, OFF32>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_fp8_mfma_kernel<DT, D, 16, OFF32>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <pa_dtype DT>
+hipError_t launch_d(const DecodeParams& p, int D, int G, dim3 grid, hipStream_t st) {
+  if (D == 64) return p.off32 ? launch_g<DT, 64, true>(p, G, grid, st) : launch_g<DT, 64, false>(p, G, grid, st);
+  if (D == 128) return p.off32 ? launch_g<DT, 128, true>(p, G, grid, st) : launch_g<DT, 128, false>(p, G, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_group_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st) {
+  switch (qt) {
+    case PA_BF16: return launch_d<PA_BF16>(p, D, G, grid, st);
+    case PA_F16: return launch_d<PA_F16>(p, D, G, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dec
+}  // namespace pa

@@ -158,7 +158,10 @@ def test_fp8_decode_f16_query_and_f16_output(G):
 def test_fp8_matches_bf16_decode_of_the_dequantised_cache():
     """Decode over FP8 pools equals decode over bf16 pools holding the
     dequantised values when the scales are powers of two (every value
-    value(code) * scale is then a bf16), up to the kernels' rounding."""
+    value(code) * scale is then a bf16), up to the kernels' rounding: both
+    round the probabilities to f16 (relative error <= 2^-11 each) against
+    their own running maxima, so they may differ by about twice that times
+    |V| (a wrong scale would be off by far more)."""
     need_gpu()
     over = dict(S=4, H=16, Hkv=2, len_median=400, len_cap=1200)
     w = workloads.make(3, **over)
@@ -175,4 +178,4 @@ def test_fp8_matches_bf16_decode_of_the_dequantised_cache():
     P.pa_decode(out_bf, dw.query, kb, vb, dw.block_tables, dw.context_lens, dw.max_context_len,
                 w.scale, partition_size=0)
     torch.cuda.synchronize()
-    assert np.max(np.abs(out_f8.cpu().numpy() - out_bf.cpu().numpy())) <= 1e-4
+    assert np.max(np.abs(out_f8.cpu().numpy() - out_bf.cpu().numpy())) <= 1e-3

@@ -152,3 +152,51 @@ def test_cascade_decode_full_size_sampled():
             worst = max(worst, float(np.max(np.abs(got[s, h] - ref))))
     announce("max-abs", worst)
     assert worst <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("layout", ["nhd", "hnd"])
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_fp8_decode_full_size_sampled(cfg, layout):
+    """FP8 pools at full size, as `bench.py --kv fp8` runs them: sampled pool
+    codes bit-exact against the oracle's quantisation of the same rows, and
+    sampled outputs against the plain definition over the codes read back."""
+    from oracle import fp8 as F
+    need_gpu()
+    w = workloads.make(cfg)
+    ks, vs = workloads.FP8_K_SCALE, workloads.FP8_V_SCALE
+    lay = P.NHD if layout == "nhd" else P.HND
+    announce("full-size fp8 decode", w.name, layout)
+    dw = M.setup(w, layout=lay, write_step=True, kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    st = build_state(w)
+    ps = P.pa_decode_auto_partition(w.S, w.H, w.Hkv, P.PA_FP8_E4M3, dw.max_context_len,
+                                   int(w.context_lens.sum()))
+    ws = torch.empty(max(16, P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, ps)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+    P.pa_decode_partitions_fp8(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                               dw.context_lens, dw.max_context_len, w.scale, ks, vs, ps, ws,
+                               layout=lay)
+    P.pa_decode_reduce(out, dw.context_lens, dw.max_context_len, w.Hkv, ps, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    lens = w.context_lens
+    seqs = sorted({0, w.S // 2, w.S - 1, int(np.argmax(lens)), int(np.argmin(lens))})
+    qf = A.bits_to_f64(w.query, w.dtype)
+    worst = 0.0
+    for s in seqs:
+        K, V = w.kv(s)
+        kq, vq = F.quantize(K, w.dtype, ks), F.quantize(V, w.dtype, vs)
+        # the device pool holds exactly these codes at the sequence's slots
+        idx = torch.from_numpy(st.seq_slots[s].astype(np.int64)).cuda()
+        blk, off = idx // w.bs, idx % w.bs
+        kd = dw.key_cache[blk, off] if lay == P.NHD else dw.key_cache[blk, :, off]
+        vd = dw.value_cache[blk, off] if lay == P.NHD else dw.value_cache[blk, :, off]
+        assert np.array_equal(kd.cpu().numpy(), kq) and np.array_equal(vd.cpu().numpy(), vq), s
+        Kf, Vf = F.dequantize(kq, ks), F.dequantize(vq, vs)
+        for h in sorted({0, w.G - 1, w.H // 2, w.H - 1}):
+            g = h // w.G
+            ref, _ = A.attention_dense(qf[s, h], Kf[:, g], Vf[:, g], w.scale)
+            worst = max(worst, float(np.max(np.abs(got[s, h] - ref))))
+    announce("max-abs", worst)
+    assert worst <= TOL[w.dtype]
