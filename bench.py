@@ -9,11 +9,11 @@ One step = one pass of the whole path over one batch of the workload:
                      packed prefill over the paged cache.
 Default workload: the 7B-like MHA decode layer (64 sequences, 32 heads,
 head size 128, bf16, block size 16, context lengths U[200, 2048], 71 write
-rows of which 7 are padding).  Inputs are seeded synthetic data already
+rows of which 7 are padding) over head-major (HND) pools.  Inputs are seeded synthetic data already
 resident in device memory when the timed region starts.
 
---kv fp8 runs a decode workload over FP8 (E4M3) pools: the cache write
-quantises, decode reads one byte per element.
+--kv fp8 runs a workload over FP8 (E4M3) pools: the cache write quantises,
+decode and prefill read one byte per element.
 
 Prints ONE JSON line.  `value` = algorithmic KV bytes read per step / step
 time (GB/s) for decode, algorithmic flops / step time (TFLOP/s) for prefill.
@@ -71,13 +71,15 @@ def parse():
                     help="untimed warm-up steps; -1 (default): as many as fill 0.3 s (at least 5), "
                          "so clocks have settled before the timed steps")
     ap.add_argument("--config", default="2", help="workload: 1, 2, 3, 4, 5a, 5b, 5c")
-    ap.add_argument("--layout", choices=["nhd", "hnd"], default="nhd")
+    ap.add_argument("--layout", choices=["nhd", "hnd"], default="hnd",
+                    help="pool layout: hnd (head-major, default: a kv head's block is one "
+                         "contiguous run) or nhd")
     ap.add_argument("--cascade", action="store_true",
                     help="shared-prefix decode workloads: attend the common blocks once "
                          "(pa_decode_cascade)")
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
-                    help="decode workloads: keep the workload's cache type, or FP8 (E4M3) pools "
-                         "written by the quantising cache write")
+                    help="keep the workload's cache type, or FP8 (E4M3) pools written by the "
+                         "quantising cache write")
     ap.add_argument("--partition", type=int, default=-1,
                     help="decode partition size (-1 auto, 0 single pass)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -127,8 +129,8 @@ def main():
     w = workloads.make(cfg)
     layout = P.NHD if args.layout == "nhd" else P.HND
     fp8 = args.kv == "fp8"
-    if fp8 and (w.kind != "decode" or args.cascade or w.dtype == "f32"):
-        raise SystemExit("--kv fp8 needs a bf16 decode workload without --cascade")
+    if fp8 and (args.cascade or w.dtype == "f32"):
+        raise SystemExit("--kv fp8 needs a bf16 workload without --cascade")
     ks, vs = workloads.FP8_K_SCALE, workloads.FP8_V_SCALE
     torch.cuda.set_device(0)
     t0 = time.time()
@@ -223,9 +225,14 @@ def main():
             ev[0].record(stream)
             M.write_step_rows(dw)
             ev[1].record(stream)
-            P.pa_prefill(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
-                         dw.query_start_loc, dw.context_lens, max_q, dw.max_context_len, w.scale,
-                         layout=layout)
+            if fp8:
+                P.pa_prefill_fp8(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                 dw.query_start_loc, dw.context_lens, max_q, dw.max_context_len,
+                                 w.scale, ks, vs, layout=layout)
+            else:
+                P.pa_prefill(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                             dw.query_start_loc, dw.context_lens, max_q, dw.max_context_len,
+                             w.scale, layout=layout)
             ev[2].record(stream)
             ev[3].record(stream)
         kinds = ["reshape_and_cache", "prefill", None]
@@ -401,7 +408,8 @@ def cpu_baseline(w, budget_s: float, unit: str, fp8_scales=None):
             else:
                 a, b = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
                 A.prefill_ref(w.query[a:b], kc, vc, st.block_tables[s:s + 1],
-                              np.array([0, b - a]), lens[s:s + 1], w.scale, w.bs, w.dtype)
+                              np.array([0, b - a]), lens[s:s + 1], w.scale, w.bs, w.dtype,
+                              kv_dtype=kv, k_scale=ks, v_scale=vs)
                 n, L = b - a, int(lens[s])
                 work += 4.0 * w.D * w.H * (n * (L - n) + n * (n + 1) / 2)
             secs += time.perf_counter() - t0

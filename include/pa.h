@@ -56,8 +56,8 @@ typedef enum {
  * byte per element.  A cache element type only ([vllm] §6.3 kv_cache_dtype
  * with k_scale / v_scale, §8 FP8 KV-cache quantisation): it is written by
  * pa_reshape_and_cache_fp8 (or bit-copied by pa_reshape_and_cache /
- * pa_copy_blocks) and read by pa_decode_fp8; queries and outputs stay
- * 16-bit or fp32. */
+ * pa_copy_blocks) and read by pa_decode_fp8 and pa_prefill_fp8; queries
+ * and outputs stay 16-bit or fp32. */
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Cache layouts ([vllm] §3.3).  A block is contiguous in both. */
@@ -340,6 +340,24 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query,
                      int32_t max_context_len, int32_t num_heads,
                      int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                      int32_t num_blocks, float scale, void* stream);
+
+/*
+ * pa_prefill_fp8 -- pa_prefill over FP8 (E4M3) pools written by
+ * pa_reshape_and_cache_fp8 ([vllm] §6.2 with the §6.3 cache types): the
+ * cached key t reads back as value(code) * k_scale and the value as
+ * value(code) * v_scale.  The query is q_dtype (PA_BF16 or PA_F16); out_dtype
+ * is PA_F32 or q_dtype; k_scale, v_scale positive and finite.  Every other
+ * argument and precondition is as in pa_prefill.
+ */
+pa_status pa_prefill_fp8(void* out, pa_dtype out_dtype, const void* query, pa_dtype q_dtype,
+                         const void* key_cache, const void* value_cache,
+                         float k_scale, float v_scale, pa_layout layout,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* query_start_loc, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                         int32_t max_context_len, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                         int32_t num_blocks, float scale, void* stream);
 
 /*
  * pa_check_metadata -- synchronous host-side check of device metadata (tests

@@ -45,7 +45,7 @@ EXPORTED = [
     "pa_status_string", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_fp8",
     "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode",
     "pa_decode_fp8", "pa_decode_partitions_fp8", "pa_decode_partitions",
-    "pa_decode_reduce", "pa_decode_cascade_workspace_size", "pa_decode_cascade", "pa_prefill",
+    "pa_decode_reduce", "pa_decode_cascade_workspace_size", "pa_decode_cascade", "pa_prefill", "pa_prefill_fp8",
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
     "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
     "pa_pool_num_free", "pa_pool_refcount", "pa_pool_add_seq_cached", "pa_pool_num_cached",
@@ -80,6 +80,8 @@ _sig = {
                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
+    "pa_prefill_fp8": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _f32, _f32, _i32, _vp, _i32, _vp, _vp,
+                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "pa_check_metadata": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _pi32, ctypes.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
@@ -377,6 +379,29 @@ def pa_prefill(out, query, key_cache, value_cache, block_tables, query_start_loc
         _dev(value_cache, "value_cache"), _dtype_code(key_cache), layout,
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(query_start_loc, "query_start_loc", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, T, int(max_query_len),
+        int(max_context_len), H, hkv, d, bs, nb, float(scale), _stream(stream)))
+
+
+def pa_prefill_fp8(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                   context_lens, max_query_len: int, max_context_len: int, scale: float,
+                   k_scale: float, v_scale: float, layout: int = NHD, stream=None) -> None:
+    """Causal packed prefill over E4M3 pools (uint8); query bf16/f16 [T, H, D]."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    T, H, D = query.shape
+    if D != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_tokens, num_heads, head_size]")
+    if _dtype_code(key_cache) != PA_FP8_E4M3 or value_cache.dtype != key_cache.dtype:
+        raise TypeError("FP8 pools are uint8 (or float8_e4m3fn)")
+    S = block_tables.shape[0]
+    if query_start_loc.shape != (S + 1,) or context_lens.shape != (S,):
+        raise ValueError("query_start_loc [S+1] and context_lens [S] required")
+    _check("pa_prefill_fp8", _lib.pa_prefill_fp8(
+        _dev(out, "out"), _dtype_code(out), _dev(query, "query"), _dtype_code(query),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), float(k_scale),
+        float(v_scale), layout, _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(query_start_loc, "query_start_loc", torch.int32),
         _dev(context_lens, "context_lens", torch.int32), S, T, int(max_query_len),
         int(max_context_len), H, hkv, d, bs, nb, float(scale), _stream(stream)))
 

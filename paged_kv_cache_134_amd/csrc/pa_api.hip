@@ -555,43 +555,54 @@ extern "C" pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void
 }
 
 // ---------------------------------------------------------------- prefill
-extern "C" pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query,
-                                const void* key_cache, const void* value_cache, pa_dtype kv_dtype,
-                                pa_layout layout, const int32_t* block_tables,
-                                int32_t max_blocks_per_seq, const int32_t* query_start_loc,
-                                const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
-                                int32_t max_query_len, int32_t max_context_len, int32_t num_heads,
-                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                                int32_t num_blocks, float scale, void* stream) {
+namespace {
+
+// pa_prefill (q_dtype == kv_dtype, 16-bit) and pa_prefill_fp8.
+pa_status prefill_impl(const char* fn, void* out, pa_dtype out_dtype, const void* query,
+                       pa_dtype q_dtype, const void* key_cache, const void* value_cache,
+                       pa_dtype kv_dtype, float k_scale, float v_scale, pa_layout layout,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* query_start_loc, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                       int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                       int32_t head_size, int32_t block_size, int32_t num_blocks, float scale,
+                       void* stream) {
+  char msg[200];
+  auto fail = [&](pa_status st, const char* what) {
+    std::snprintf(msg, sizeof msg, "%s: %s", fn, what);
+    return pa_fail(st, msg);
+  };
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
       max_blocks_per_seq < 0 || num_blocks <= 0)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: negative size or no blocks");
-  if (kv_dtype != PA_BF16 && kv_dtype != PA_F16)
-    return pa_fail(valid_storage(kv_dtype) ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARGUMENT,
-                   "pa_prefill: kv dtype must be bf16 or f16");
-  if (out_dtype != PA_F32 && out_dtype != kv_dtype)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: out dtype must be f32 or the kv dtype");
+    return fail(PA_ERR_INVALID_ARGUMENT, "negative size or no blocks");
+  if (q_dtype != PA_BF16 && q_dtype != PA_F16)
+    return fail(valid_storage(q_dtype) ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARGUMENT,
+                "query (and 16-bit cache) dtype must be bf16 or f16");
+  if (out_dtype != PA_F32 && out_dtype != q_dtype)
+    return fail(PA_ERR_INVALID_ARGUMENT, "out dtype must be f32 or the query dtype");
   if (layout != PA_LAYOUT_NHD && layout != PA_LAYOUT_HND)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: bad layout");
+    return fail(PA_ERR_INVALID_ARGUMENT, "bad layout");
   if (!valid_group(num_heads, num_kv_heads))
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill: num_heads / num_kv_heads must be 1, 2, 4, 8 or 16");
+    return fail(PA_ERR_UNSUPPORTED, "num_heads / num_kv_heads must be 1, 2, 4, 8 or 16");
   if (head_size != 64 && head_size != 128)
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_size must be 64 or 128");
+    return fail(PA_ERR_UNSUPPORTED, "head_size must be 64 or 128");
   if (!pow2_in(block_size, 1, 1024))
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size must be a power of two in [1, 1024]");
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be a power of two in [1, 1024]");
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: max_context_len exceeds max_blocks_per_seq * block_size");
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len exceeds max_blocks_per_seq * block_size");
   if (max_query_len > max_context_len)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: max_query_len exceeds max_context_len");
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_query_len exceeds max_context_len");
   if (num_heads > 65535 || num_seqs > 65535)
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill: at most 65535 heads and 65535 sequences");
-  if (!(scale == scale)) return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: scale is NaN");
+    return fail(PA_ERR_UNSUPPORTED, "at most 65535 heads and 65535 sequences");
+  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale is NaN");
+  if (!finite_positive(k_scale) || !finite_positive(v_scale))
+    return fail(PA_ERR_INVALID_ARGUMENT, "scales must be positive and finite");
   if (num_seqs == 0 || num_tokens == 0) return PA_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !query_start_loc ||
       !context_lens)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: null pointer");
+    return fail(PA_ERR_INVALID_ARGUMENT, "null pointer");
   if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill: out, query and caches must be 16-byte aligned");
+    return fail(PA_ERR_INVALID_ARGUMENT, "out, query and caches must be 16-byte aligned");
   pa::PrefillArgs a{};
   a.out = out;
   a.out_dtype = out_dtype;
@@ -599,6 +610,9 @@ extern "C" pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query
   a.key_cache = key_cache;
   a.value_cache = value_cache;
   a.kv_dtype = kv_dtype;
+  a.q_dtype = q_dtype;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.block_tables = block_tables;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.query_start_loc = query_start_loc;
@@ -610,7 +624,43 @@ extern "C" pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query
   a.geom = pa::PoolGeom{num_kv_heads, head_size, block_size, num_blocks, layout};
   a.scale = scale;
   hipError_t e = pa::launch_prefill(a, (hipStream_t)stream);
-  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_prefill");
+  return e == hipSuccess ? PA_OK : hip_fail(e, fn);
+}
+
+}  // namespace
+
+extern "C" pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query,
+                                const void* key_cache, const void* value_cache, pa_dtype kv_dtype,
+                                pa_layout layout, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* query_start_loc,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens,
+                                int32_t max_query_len, int32_t max_context_len, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                int32_t num_blocks, float scale, void* stream) {
+  if (kv_dtype == PA_FP8_E4M3)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_prefill: FP8 caches are read by pa_prefill_fp8");
+  return prefill_impl("pa_prefill", out, out_dtype, query, kv_dtype, key_cache, value_cache,
+                      kv_dtype, 1.f, 1.f, layout, block_tables, max_blocks_per_seq,
+                      query_start_loc, context_lens, num_seqs, num_tokens, max_query_len,
+                      max_context_len, num_heads, num_kv_heads, head_size, block_size,
+                      num_blocks, scale, stream);
+}
+
+extern "C" pa_status pa_prefill_fp8(void* out, pa_dtype out_dtype, const void* query,
+                                    pa_dtype q_dtype, const void* key_cache,
+                                    const void* value_cache, float k_scale, float v_scale,
+                                    pa_layout layout, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* query_start_loc,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_tokens, int32_t max_query_len,
+                                    int32_t max_context_len, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                    int32_t num_blocks, float scale, void* stream) {
+  return prefill_impl("pa_prefill_fp8", out, out_dtype, query, q_dtype, key_cache, value_cache,
+                      PA_FP8_E4M3, k_scale, v_scale, layout, block_tables, max_blocks_per_seq,
+                      query_start_loc, context_lens, num_seqs, num_tokens, max_query_len,
+                      max_context_len, num_heads, num_kv_heads, head_size, block_size,
+                      num_blocks, scale, stream);
 }
 
 // ----------------------------------------------------------- metadata check

@@ -81,7 +81,10 @@ struct PrefillArgs {
   const void* query;
   const void* key_cache;
   const void* value_cache;
-  pa_dtype kv_dtype;
+  pa_dtype kv_dtype;        // cache element type
+  pa_dtype q_dtype;         // query type (kv_dtype unless the cache is FP8)
+  float k_scale = 1.f;      // FP8 caches: stored code value * scale = element
+  float v_scale = 1.f;
   const int32_t* block_tables;
   int32_t max_blocks_per_seq;
   const int32_t* query_start_loc;

@@ -36,7 +36,11 @@
 //     multiply V are exactly the ones that are divided out; QK^T uses the
 //     stored type with fp32 accumulation;
 //   * a wave whose rows are all padding, or that sees none of a tile's keys,
-//     skips that tile's products.
+//     skips that tile's products;
+//   * FP8 (E4M3) caches: K converts exactly to the query's type and V to f16
+//     on their way into LDS, so the products are those of a 16-bit cache;
+//     k_scale is folded into the softmax scale and v_scale into the final
+//     normalisation.
 #include <hip/hip_runtime.h>
 
 #include "kernel_common.h"
@@ -73,7 +77,8 @@ struct PrefillParams {
   int32_t num_heads;
   int32_t num_kv_heads;
   int32_t log2_bs;
-  float scale_log2e;
+  float scale_log2e;  // softmax scale * log2(e), times k_scale for FP8 caches
+  float v_scale;      // FP8 caches: applied with the normalisation (else 1)
   pa_dtype out_dtype;
   int32_t q_tiles;   // query tiles per sequence (of the longest)
   int32_t num_work;  // (sequence, head) pairs: num_heads * num_seqs (prefix mode: (head, key part))
@@ -105,21 +110,35 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
-// D = head size.  OFF32: both caches span less than 4 GiB, so rows are
-// addressed by 32-bit byte offsets from the cache base.  PREFIX: the
-// shared-prefix pass of a cascade -- every query row sees every key of its
-// key partition (no causal mask) and writes a (max, sum, unnormalised
-// output) partial instead of a normalised row.
-template <pa_dtype DT, int D, bool OFF32, bool PREFIX>
+// 8 E4M3 codes as floats.
+__device__ __forceinline__ void fp8x8_to_f32(const uint4& v, float* out) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, false);
+  const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, true);
+  out[0] = a.x; out[1] = a.y; out[2] = b.x; out[3] = b.y;
+  out[4] = c.x; out[5] = c.y; out[6] = d.x; out[7] = d.y;
+}
+
+// D = head size; DT = the query's type (and the cache's, unless FP8).
+// OFF32: both caches span less than 4 GiB, so rows are addressed by 32-bit
+// byte offsets from the cache base.  PREFIX: the shared-prefix pass of a
+// cascade -- every query row sees every key of its key partition (no causal
+// mask) and writes a (max, sum, unnormalised output) partial instead of a
+// normalised row.  FP8: the caches hold E4M3 codes.
+template <pa_dtype DT, int D, bool OFF32, bool PREFIX, bool FP8>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillParams p) {
+  static_assert(!(FP8 && PREFIX), "the shared-prefix pass reads 16-bit caches");
+  constexpr int CB = FP8 ? 1 : 2;               // cache bytes per element
   constexpr int KS = D / 16;                    // 16-wide k-steps over the head dim (QK)
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
   constexpr int KROW = D * 2 + 16;              // LDS bytes per K row (padded)
   constexpr int VROW = kBN * 2 + 8;             // LDS bytes per V^T row (padded)
-  constexpr int KCH = D / 8;                    // 16-byte chunks per K/V row
-  constexpr int KPT = kBN * KCH / kPrefillThreads;        // K chunks per thread per tile
+  constexpr int KCH = D / 8;                    // 16-byte LDS chunks per K row
+  constexpr int GCH = D * CB / 16;              // 16-byte cache chunks per K row
+  constexpr int KPT = kBN * GCH / kPrefillThreads;        // cache chunks per thread per tile
   constexpr int VITEMS = (kBN / 4) * KCH;      // V items of 4 keys x 8 columns per tile
-  static_assert(KPT * kPrefillThreads == kBN * KCH, "K tile must split evenly");
+  static_assert(KPT * kPrefillThreads == kBN * GCH, "K tile must split evenly");
   static_assert(VITEMS <= kPrefillThreads, "one V item per thread");
   __shared__ __attribute__((aligned(16))) char sK[kBN * KROW];
   __shared__ __attribute__((aligned(16))) char sV[D * VROW];
@@ -195,15 +214,15 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   const int lbs = p.log2_bs;
   const int bs_mask = (1 << lbs) - 1;
   const int64_t head_off = (int64_t)kvh * p.head_stride;
-  const uint32_t blk_b = (uint32_t)(p.blk_stride * 2);
-  const uint32_t tok_b = (uint32_t)(p.tok_stride * 2);
+  const uint32_t blk_b = (uint32_t)(p.blk_stride * CB);
+  const uint32_t tok_b = (uint32_t)(p.tok_stride * CB);
   // byte offset of row t (in block blk) at element column col
   auto row_off = [&](int32_t blk, int t, int col) -> int64_t {
     if constexpr (OFF32)
       return (int64_t)((uint32_t)blk * blk_b + (uint32_t)(t & bs_mask) * tok_b +
-                       (uint32_t)((head_off + col) * 2));
+                       (uint32_t)((head_off + col) * CB));
     else
-      return ((int64_t)blk * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride + head_off + col) * 2;
+      return ((int64_t)blk * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride + head_off + col) * CB;
   };
 
   // Block ids come from an LDS window of the table (entries wb0 ..
@@ -224,7 +243,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   // consecutive keys of one 8-column slice: one block-table lookup each
   // (blocks of >= 4 tokens hold an aligned group of 4 keys).
   constexpr int KTPR = kPrefillThreads / kBN;  // threads per K row
-  static_assert(KTPR * KPT == KCH, "K row split");
+  static_assert(KTPR * KPT == GCH, "K row split");
   const int k_row = tid / KTPR, k_cg = (tid % KTPR) * KPT;
   const int v_item = min(tid, VITEMS - 1);
   const int v_kq = v_item % (kBN / 4), v_dq = v_item / (kBN / 4);
@@ -237,7 +256,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     TileRegs r;
     {
       const int t = min(k0 + k_row, kend - 1);
-      const char* src = p.key_cache + row_off(s_bt[(t >> lbs) - wb0], t, k_cg * 8);
+      const char* src = p.key_cache + row_off(s_bt[(t >> lbs) - wb0], t, k_cg * (16 / CB));
 #pragma unroll
       for (int i = 0; i < KPT; ++i) r.k[i] = load16(src + i * 16);
     }
@@ -247,7 +266,13 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = min(k0 + v_kq * 4 + e, kend - 1);
-        r.v[e] = load16(p.value_cache + row_off(bs_ge4 ? blk0 : s_bt[(t >> lbs) - wb0], t, v_dq * 8));
+        const char* src = p.value_cache + row_off(bs_ge4 ? blk0 : s_bt[(t >> lbs) - wb0], t, v_dq * 8);
+        if constexpr (FP8) {  // 8 codes
+          const uint2 c8 = *reinterpret_cast<const uint2*>(src);
+          r.v[e] = make_uint4(c8.x, c8.y, 0, 0);
+        } else {
+          r.v[e] = load16(src);
+        }
       }
     }
     return r;
@@ -265,16 +290,30 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   for (int k0 = k_lo; k0 < kend; k0 += kBN) {
     // ---- registers -> LDS: K row-major, V transposed to [d][key] in f16
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) store16(sK + k_row * KROW + (k_cg + i) * 16, tr.k[i]);
+    for (int i = 0; i < KPT; ++i) {
+      if constexpr (FP8) {  // 16 codes -> two 16-byte chunks of the query's type
+        uint4 lo, hi;
+        fp8x16_to_pairs<DT>(tr.k[i], lo, hi);
+        store16(sK + k_row * KROW + (k_cg + i) * 32, lo);
+        store16(sK + k_row * KROW + (k_cg + i) * 32 + 16, hi);
+      } else {
+        store16(sK + k_row * KROW + (k_cg + i) * 16, tr.k[i]);
+      }
+    }
     if (VITEMS == kPrefillThreads || tid < VITEMS) {  // head size 64: half the threads stage no V
+      float fv[4][8];  // FP8: the 8 columns of each of the 4 keys
+      if constexpr (FP8) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) fp8x8_to_f32(tr.v[k], fv[k]);
+      }
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         // columns e, e+1 of keys v_kq*4 .. +3
         float f0[4], f1[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          f0[k] = chunk_elem<DT>(tr.v[k], e);
-          f1[k] = chunk_elem<DT>(tr.v[k], e + 1);
+          f0[k] = FP8 ? fv[k][e] : chunk_elem<DT>(tr.v[k], e);
+          f1[k] = FP8 ? fv[k][e + 1] : chunk_elem<DT>(tr.v[k], e + 1);
         }
         *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e) * VROW + v_kq * 8) =
             make_uint2(pk_f16(f0[0], f0[1]), pk_f16(f0[2], f0[3]));
@@ -399,7 +438,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     return;
   }
   if (j < n) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
     const int64_t row = ((int64_t)(q_begin + j) * p.num_heads + h) * D;
     // four consecutive columns per group g
 #pragma unroll
@@ -426,7 +465,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 }
 
 template <pa_dtype DT, int D>
-hipError_t launch_pd(PrefillParams p, int num_seqs, int max_q, bool off32, hipStream_t st) {
+hipError_t launch_pd(PrefillParams p, int num_seqs, int max_q, bool off32, bool fp8, hipStream_t st) {
   const bool prefix = p.prefix_keys > 0;
   p.q_tiles = ((prefix ? p.num_rows : max_q) + kBM - 1) / kBM;
   const int64_t pairs = (int64_t)p.num_heads * (prefix ? p.key_parts : num_seqs);
@@ -434,16 +473,22 @@ hipError_t launch_pd(PrefillParams p, int num_seqs, int max_q, bool off32, hipSt
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   p.num_work = (int)pairs;
   dim3 grid((unsigned)blocks), block(kPrefillThreads);
+  if (prefix && fp8) return hipErrorInvalidValue;
   if (prefix) {
     if (off32)
-      hipLaunchKernelGGL((prefill_kernel<DT, D, true, true>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((prefill_kernel<DT, D, true, true, false>), grid, block, 0, st, p);
     else
-      hipLaunchKernelGGL((prefill_kernel<DT, D, false, true>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((prefill_kernel<DT, D, false, true, false>), grid, block, 0, st, p);
+  } else if (fp8) {
+    if (off32)
+      hipLaunchKernelGGL((prefill_kernel<DT, D, true, false, true>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<DT, D, false, false, true>), grid, block, 0, st, p);
   } else {
     if (off32)
-      hipLaunchKernelGGL((prefill_kernel<DT, D, true, false>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((prefill_kernel<DT, D, true, false, false>), grid, block, 0, st, p);
     else
-      hipLaunchKernelGGL((prefill_kernel<DT, D, false, false>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((prefill_kernel<DT, D, false, false, false>), grid, block, 0, st, p);
   }
   return hipGetLastError();
 }
@@ -474,7 +519,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.num_heads = a.num_heads;
   p.num_kv_heads = g.num_kv_heads;
   p.log2_bs = __builtin_ctz((unsigned)g.block_size);
-  p.scale_log2e = a.scale * kLog2e;
+  p.scale_log2e = a.scale * a.k_scale * kLog2e;
+  p.v_scale = a.v_scale;
   p.out_dtype = a.out_dtype;
   p.num_rows = a.num_tokens;
   p.prefix_keys = a.prefix_keys;
@@ -483,13 +529,16 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.part_out = a.part_out;
   p.part_ml = a.part_ml;
   p.max_partitions = a.max_partitions;
-  const bool off32 = (int64_t)g.num_blocks * p.blk_stride * 2 <= (int64_t)UINT32_MAX;
-  if (a.kv_dtype == PA_BF16) {
-    if (g.head_size == 64) return launch_pd<PA_BF16, 64>(p, a.num_seqs, a.max_query_len, off32, stream);
-    if (g.head_size == 128) return launch_pd<PA_BF16, 128>(p, a.num_seqs, a.max_query_len, off32, stream);
-  } else if (a.kv_dtype == PA_F16) {
-    if (g.head_size == 64) return launch_pd<PA_F16, 64>(p, a.num_seqs, a.max_query_len, off32, stream);
-    if (g.head_size == 128) return launch_pd<PA_F16, 128>(p, a.num_seqs, a.max_query_len, off32, stream);
+  const bool fp8 = a.kv_dtype == PA_FP8_E4M3;
+  const int64_t elem = fp8 ? 1 : 2;
+  const bool off32 = (int64_t)g.num_blocks * p.blk_stride * elem <= (int64_t)UINT32_MAX;
+  const pa_dtype qt = fp8 ? a.q_dtype : a.kv_dtype;
+  if (qt == PA_BF16) {
+    if (g.head_size == 64) return launch_pd<PA_BF16, 64>(p, a.num_seqs, a.max_query_len, off32, fp8, stream);
+    if (g.head_size == 128) return launch_pd<PA_BF16, 128>(p, a.num_seqs, a.max_query_len, off32, fp8, stream);
+  } else if (qt == PA_F16) {
+    if (g.head_size == 64) return launch_pd<PA_F16, 64>(p, a.num_seqs, a.max_query_len, off32, fp8, stream);
+    if (g.head_size == 128) return launch_pd<PA_F16, 128>(p, a.num_seqs, a.max_query_len, off32, fp8, stream);
   }
   return hipErrorInvalidValue;
 }

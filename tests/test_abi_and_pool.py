@@ -122,6 +122,15 @@ def test_fp8_argument_errors():
     assert lib.pa_decode_cascade(v, 0, v, v, v, F8, 0, v, 200, v, 3000, 1792, 100, 32, 32, 128,
                                  256, 300, 1.0, -1, v, 1 << 30, None) == 2
 
+    def pre(q=BF, out=F32, ks=0.5, n=4):
+        return lib.pa_prefill_fp8(v, out, v, q, v, v, ks, 0.5, 0, v, 8, v, v, 1, n, n, 100, 8, 8,
+                                  128, 16, 8, 1.0, None)
+
+    assert pre(ks=float("nan")) == 1 and pre(ks=-2.0) == 1
+    assert pre(q=F8) == 2 and pre(q=F32) == 2   # queries are bf16 or f16
+    assert pre(out=F16) == 1                    # out is f32 or the query type
+    assert pre(n=0) == 0                        # no rows
+
 
 def test_cascade_argument_errors_and_workspace():
     """pa_decode_cascade's host checks (no device needed)."""

@@ -179,3 +179,43 @@ def test_fp8_matches_bf16_decode_of_the_dequantised_cache():
                 w.scale, partition_size=0)
     torch.cuda.synchronize()
     assert np.max(np.abs(out_f8.cpu().numpy() - out_bf.cpu().numpy())) <= 1e-3
+
+
+@pytest.mark.parametrize("layout", [P.NHD, P.HND])
+@pytest.mark.parametrize("name,cfg,over", [
+    ("packed-literal-2heads", "5b", dict(H=2, Hkv=2)),
+    ("packed-gqa", "5b", dict(H=8, Hkv=2, packed_lens=[85, 120, 45, 210, 1, 64])),
+    ("prefix-suffix", "5c", dict(S=4, H=2, Hkv=2, prefix=600, suffix_lo=20, suffix_hi=200)),
+    ("prefix-suffix-d64-bs16", "5c", dict(S=3, H=4, Hkv=1, D=64, bs=16, prefix=300,
+                                          suffix_lo=60, suffix_hi=150)),
+])
+def test_fp8_prefill_small(name, cfg, over, layout):
+    """Causal packed prefill over FP8 pools against the oracle reading the
+    same codes back (value * scale)."""
+    need_gpu()
+    w = workloads.make(cfg, **over)
+    announce("fp8 prefill", name, "layout", layout)
+    dw = _setup(w, layout)
+    st = build_state(w)
+    kc, vc = build_pool(w, st, layout=layout, include_step=True, kv_dtype="e4m3", k_scale=KS,
+                        v_scale=VS)
+    assert _same_codes(_codes(dw.key_cache), kc)
+    ref = A.prefill_ref(w.query, kc, vc, st.block_tables, w.query_start_loc, w.context_lens,
+                        w.scale, w.bs, w.dtype, layout, kv_dtype="e4m3", k_scale=KS, v_scale=VS)
+    for qdt in (torch.bfloat16, torch.float16):
+        q = dw.query.to(qdt)
+        if qdt == torch.float16:
+            qb = q.cpu().view(torch.int16).numpy().view(np.uint16)
+            ref = A.prefill_ref(qb, kc, vc, st.block_tables, w.query_start_loc, w.context_lens,
+                                w.scale, w.bs, "f16", layout, kv_dtype="e4m3", k_scale=KS,
+                                v_scale=VS)
+        out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+        P.pa_prefill_fp8(out, q, dw.key_cache, dw.value_cache, dw.block_tables, dw.query_start_loc,
+                         dw.context_lens, int(w.query_lens.max()), dw.max_context_len, w.scale,
+                         KS, VS, layout=layout)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        err, where = max_abs(got, ref)
+        announce("query", qdt, "max-abs", err)
+        assert np.all(np.isfinite(got))
+        assert err <= TOL["bf16"], (name, qdt, err, where)
