@@ -137,6 +137,30 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache,
                          void* stream);
 
 /*
+ * pa_swap_blocks -- whole-block copies from one pair of pools to another,
+ * e.g. a preempted sequence's blocks out to a host pool and back in later
+ * ([k4i] "relation to continuous batching": when the pool runs out, the
+ * scheduler may swap blocks to CPU memory).  For pair i, block
+ * block_pairs[i][0] of each source pool is copied bit for bit to block
+ * block_pairs[i][1] of the matching destination pool (K to K, V to V), in
+ * pair order.
+ *   src_key_cache, src_value_cache, dst_key_cache, dst_value_cache: device
+ *       memory or pinned host memory (hipHostMalloc); the direction of each
+ *       copy follows from the addresses
+ *   block_pairs (host) int32 [num_pairs][2], read during the call
+ *   block_bytes bytes of one block (block_size * num_kv_heads * head_size *
+ *       element size)
+ * The copies are enqueued on `stream` (asynchronous; with pinned host memory
+ * they overlap other work).  Block ids are checked against src_num_blocks /
+ * dst_num_blocks before anything is enqueued.  num_pairs == 0 is a no-op.
+ */
+pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                         void* dst_key_cache, void* dst_value_cache,
+                         const int32_t* block_pairs, int32_t num_pairs,
+                         int64_t block_bytes, int32_t src_num_blocks,
+                         int32_t dst_num_blocks, void* stream);
+
+/*
  * pa_decode -- one query token per sequence attends to its cached context
  * through its block table ([vllm] §3.1, §6.2, §7.2; [k4i] attention over
  * non-contiguous blocks).

@@ -43,7 +43,7 @@ NHD, HND = 0, 1
 
 EXPORTED = [
     "pa_status_string", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_fp8",
-    "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode",
+    "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode",
     "pa_decode_fp8", "pa_decode_partitions_fp8", "pa_decode_partitions",
     "pa_decode_reduce", "pa_decode_cascade_workspace_size", "pa_decode_cascade", "pa_prefill", "pa_prefill_fp8",
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
@@ -63,6 +63,7 @@ _sig = {
     "pa_reshape_and_cache_fp8": (_i32, [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _pi32, _i32, _i64, _i32, _i32, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64]),
     "pa_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
@@ -216,6 +217,28 @@ def pa_copy_blocks(key_cache, value_cache, block_pairs, layout: int = NHD, strea
         _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
         _dev(block_pairs, "block_pairs", torch.int32) if n else None, n, hkv, d, bs, nb,
         _dtype_code(key_cache), _stream(stream)))
+
+
+def pa_swap_blocks(src_key, src_value, dst_key, dst_value, block_pairs, stream=None) -> None:
+    """Copy whole blocks between pools (device or pinned host tensors of one
+    geometry and dtype): block_pairs [n, 2] (host ints) = (source block,
+    destination block)."""
+    torch = _torch()
+    for t, name in ((src_key, "src_key"), (src_value, "src_value"), (dst_key, "dst_key"),
+                    (dst_value, "dst_value")):
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor")
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be device memory or pinned host memory")
+    if src_value.shape != src_key.shape or dst_key.shape[1:] != src_key.shape[1:] or \
+            dst_value.shape != dst_key.shape or len({t.dtype for t in (src_key, src_value, dst_key, dst_value)}) != 1:
+        raise ValueError("pools must share block geometry and dtype")
+    pairs = np.ascontiguousarray(np.asarray(block_pairs, dtype=np.int32).reshape(-1, 2))
+    block_bytes = src_key[0].numel() * src_key.element_size()
+    _check("pa_swap_blocks", _lib.pa_swap_blocks(
+        src_key.data_ptr(), src_value.data_ptr(), dst_key.data_ptr(), dst_value.data_ptr(),
+        pairs.ctypes.data_as(_pi32), len(pairs), block_bytes, src_key.shape[0], dst_key.shape[0],
+        _stream(stream)))
 
 
 def pa_decode_workspace_size(num_seqs: int, num_heads: int, head_size: int, max_context_len: int,

@@ -162,6 +162,37 @@ extern "C" pa_status pa_copy_blocks(void* key_cache, void* value_cache, const in
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_copy_blocks");
 }
 
+extern "C" pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                                    void* dst_key_cache, void* dst_value_cache,
+                                    const int32_t* block_pairs, int32_t num_pairs,
+                                    int64_t block_bytes, int32_t src_num_blocks,
+                                    int32_t dst_num_blocks, void* stream) {
+  if (num_pairs < 0 || block_bytes <= 0 || src_num_blocks <= 0 || dst_num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_swap_blocks: non-positive size");
+  if (num_pairs == 0) return PA_OK;
+  if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache || !block_pairs)
+    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_swap_blocks: null pointer");
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int32_t sb = block_pairs[2 * i], db = block_pairs[2 * i + 1];
+    if (sb < 0 || sb >= src_num_blocks || db < 0 || db >= dst_num_blocks)
+      return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_swap_blocks: block id out of range");
+  }
+  const hipStream_t st = (hipStream_t)stream;
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int64_t so = (int64_t)block_pairs[2 * i] * block_bytes;
+    const int64_t dof = (int64_t)block_pairs[2 * i + 1] * block_bytes;
+    hipError_t e = hipMemcpyAsync(static_cast<char*>(dst_key_cache) + dof,
+                                  static_cast<const char*>(src_key_cache) + so, block_bytes,
+                                  hipMemcpyDefault, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(static_cast<char*>(dst_value_cache) + dof,
+                         static_cast<const char*>(src_value_cache) + so, block_bytes,
+                         hipMemcpyDefault, st);
+    if (e != hipSuccess) return hip_fail(e, "pa_swap_blocks");
+  }
+  return PA_OK;
+}
+
 // ----------------------------------------------------------------- decode
 namespace {
 

@@ -132,6 +132,22 @@ def test_fp8_argument_errors():
     assert pre(n=0) == 0                        # no rows
 
 
+def test_swap_blocks_host_checks():
+    """pa_swap_blocks checks every block id on the host and enqueues nothing
+    on failure."""
+    lib = P._lib
+    v = ctypes.c_void_p(256)
+    pairs = (ctypes.c_int32 * 4)(0, 3, 5, 4)
+    assert lib.pa_swap_blocks(v, v, v, v, pairs, 2, 4096, 8, 4, None) == 1    # destination 4 of 4 blocks
+    bad_src = (ctypes.c_int32 * 2)(8, 0)
+    assert lib.pa_swap_blocks(v, v, v, v, bad_src, 1, 4096, 8, 4, None) == 1  # source 8 of 8 blocks
+    neg = (ctypes.c_int32 * 2)(0, -1)
+    assert lib.pa_swap_blocks(v, v, v, v, neg, 1, 4096, 8, 4, None) == 1
+    assert lib.pa_swap_blocks(None, v, v, v, pairs, 1, 4096, 8, 4, None) == 1
+    assert lib.pa_swap_blocks(None, None, None, None, None, 0, 4096, 8, 4, None) == 0
+    assert lib.pa_swap_blocks(v, v, v, v, pairs, 1, 0, 8, 4, None) == 1
+
+
 def test_cascade_argument_errors_and_workspace():
     """pa_decode_cascade's host checks (no device needed)."""
     lib = P._lib

@@ -301,3 +301,43 @@ def test_cascade_decode_small(name, over, layout):
         err, where = max_abs(got, ref)
         announce("partition", part, "max-abs", err)
         assert err <= TOL[w.dtype], (name, part, err, where)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_swap_blocks_out_and_back(kv):
+    """Blocks of a filled pool swapped out to a pinned host pool and back into
+    a fresh device pool: every copied block bit-exact (a bit copy by
+    definition), every other block untouched."""
+    need_gpu()
+    w = workloads.make(3, S=3, H=8, Hkv=2, len_median=200, len_cap=600)
+    announce("swap blocks", kv)
+    if kv == "e4m3":
+        dw = M.setup(w, layout=P.HND, write_step=True, kv_dtype="e4m3",
+                     k_scale=workloads.FP8_K_SCALE, v_scale=workloads.FP8_V_SCALE)
+    else:
+        dw = M.setup(w, layout=P.HND, write_step=True)
+    rng = np.random.default_rng(5)
+    nb = dw.key_cache.shape[0]
+    out_pairs = np.stack([rng.permutation(nb)[:7], rng.permutation(11)[:7]], 1)  # device -> host slots
+    host_k = torch.zeros((11,) + tuple(dw.key_cache.shape[1:]), dtype=dw.key_cache.dtype).pin_memory()
+    host_v = torch.zeros_like(host_k).pin_memory()
+    P.pa_swap_blocks(dw.key_cache, dw.value_cache, host_k, host_v, out_pairs)
+    torch.cuda.synchronize()
+    raw = lambda t: t.cpu().contiguous().view(torch.uint8).numpy()  # noqa: E731
+    kd, vd = raw(dw.key_cache), raw(dw.value_cache)
+    hk, hv = raw(host_k), raw(host_v)
+    for s_, d_ in out_pairs:
+        assert np.array_equal(hk[d_], kd[s_]) and np.array_equal(hv[d_], vd[s_])
+    untouched = sorted(set(range(11)) - set(out_pairs[:, 1].tolist()))
+    assert not hk[untouched].any() and not hv[untouched].any()
+    # back into a fresh device pool at other block ids
+    back_k = torch.zeros_like(dw.key_cache)
+    back_v = torch.zeros_like(dw.value_cache)
+    in_pairs = np.stack([out_pairs[:, 1], rng.permutation(nb)[:7]], 1)
+    P.pa_swap_blocks(host_k, host_v, back_k, back_v, in_pairs)
+    torch.cuda.synchronize()
+    bk, bv = raw(back_k), raw(back_v)
+    for (s_, _), (_, d_) in zip(out_pairs, in_pairs):
+        assert np.array_equal(bk[d_], kd[s_]) and np.array_equal(bv[d_], vd[s_])
+    rest = sorted(set(range(nb)) - set(in_pairs[:, 1].tolist()))
+    assert not bk[rest].any() and not bv[rest].any()
