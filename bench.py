@@ -129,8 +129,8 @@ def main():
     w = workloads.make(cfg)
     layout = P.NHD if args.layout == "nhd" else P.HND
     fp8 = args.kv == "fp8"
-    if fp8 and (args.cascade or w.dtype == "f32"):
-        raise SystemExit("--kv fp8 needs a bf16 workload without --cascade")
+    if fp8 and w.dtype == "f32":
+        raise SystemExit("--kv fp8 needs a bf16 workload")
     ks, vs = workloads.FP8_K_SCALE, workloads.FP8_V_SCALE
     torch.cuda.set_device(0)
     t0 = time.time()
@@ -164,9 +164,15 @@ def main():
             ev[0].record(stream)
             M.write_step_rows(dw)
             ev[1].record(stream)
-            P.pa_decode_cascade(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
-                                dw.context_lens, dw.max_context_len, common, w.scale, ws,
-                                layout=layout, partition_size=ps)
+            if fp8:
+                P.pa_decode_cascade_fp8(out, dw.query, dw.key_cache, dw.value_cache,
+                                        dw.block_tables, dw.context_lens, dw.max_context_len,
+                                        common, w.scale, ks, vs, ws, layout=layout,
+                                        partition_size=ps)
+            else:
+                P.pa_decode_cascade(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                    dw.context_lens, dw.max_context_len, common, w.scale, ws,
+                                    layout=layout, partition_size=ps)
             ev[2].record(stream)
             ev[3].record(stream)
         kinds = ["reshape_and_cache", "decode_cascade", None]

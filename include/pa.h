@@ -334,6 +334,22 @@ pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void* query,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_cascade_fp8 -- pa_decode_cascade over FP8 (E4M3) pools, with the
+ * query type, scales and read-back of pa_decode_fp8 ([vllm] §6.3, §6.4).
+ * Same workspace (pa_decode_cascade_workspace_size) and preconditions.
+ */
+pa_status pa_decode_cascade_fp8(void* out, pa_dtype out_dtype, const void* query,
+                                pa_dtype q_dtype, const void* key_cache,
+                                const void* value_cache, float k_scale, float v_scale,
+                                pa_layout layout, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, int32_t common_prefix_len,
+                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                float scale, int32_t partition_size, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill -- causal attention of packed query rows over the paged cache
  * ([vllm] §6.2 flash_attn_varlen_func with cu_seqlens_q = query_start_loc,
  * seqlen_k = seq_lens, block_table, causal = True; [packed] §2.3).

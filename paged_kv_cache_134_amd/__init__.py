@@ -45,7 +45,7 @@ EXPORTED = [
     "pa_status_string", "pa_last_error", "pa_reshape_and_cache", "pa_reshape_and_cache_fp8",
     "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode_auto_partition", "pa_decode",
     "pa_decode_fp8", "pa_decode_partitions_fp8", "pa_decode_partitions",
-    "pa_decode_reduce", "pa_decode_cascade_workspace_size", "pa_decode_cascade", "pa_prefill", "pa_prefill_fp8",
+    "pa_decode_reduce", "pa_decode_cascade_workspace_size", "pa_decode_cascade", "pa_decode_cascade_fp8", "pa_prefill", "pa_prefill_fp8",
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
     "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
     "pa_pool_num_free", "pa_pool_refcount", "pa_pool_add_seq_cached", "pa_pool_num_cached",
@@ -79,6 +79,9 @@ _sig = {
     "pa_decode_cascade_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_cascade": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32,
                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_cascade_fp8": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _f32, _f32, _i32, _vp, _i32,
+                                     _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                     _i32, _vp, _sz, _vp]),
     "pa_prefill": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "pa_prefill_fp8": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _f32, _f32, _i32, _vp, _i32, _vp, _vp,
@@ -351,6 +354,30 @@ def pa_decode_cascade(out, query, key_cache, value_cache, block_tables, context_
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
 
+
+
+def pa_decode_cascade_fp8(out, query, key_cache, value_cache, block_tables, context_lens,
+                          max_context_len: int, common_prefix_len: int, scale: float,
+                          k_scale: float, v_scale: float, workspace, layout: int = NHD,
+                          partition_size: int = -1, stream=None) -> None:
+    """pa_decode_cascade over E4M3 pools (uint8); query bf16/f16."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    S, H, D = query.shape
+    if D != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_seqs, num_heads, head_size]")
+    if _dtype_code(key_cache) != PA_FP8_E4M3 or value_cache.dtype != key_cache.dtype:
+        raise TypeError("FP8 pools are uint8 (or float8_e4m3fn)")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables [S, max_blocks] and context_lens [S] required")
+    _check("pa_decode_cascade_fp8", _lib.pa_decode_cascade_fp8(
+        _dev(out, "out"), _dtype_code(out), _dev(query, "query"), _dtype_code(query),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), float(k_scale),
+        float(v_scale), layout, _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context_len), int(common_prefix_len), S, H, hkv, d, bs, nb, float(scale),
+        int(partition_size), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 def pa_decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens,
                          max_context_len: int, scale: float, partition_size: int, workspace,

@@ -499,35 +499,39 @@ extern "C" size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num
                          npp + cascade_suffix_parts(max_context_len, common_prefix_len, ps));
 }
 
-extern "C" pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void* query,
-                                       const void* key_cache, const void* value_cache,
-                                       pa_dtype kv_dtype, pa_layout layout,
-                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                       const int32_t* context_lens, int32_t max_context_len,
-                                       int32_t common_prefix_len, int32_t num_seqs,
-                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
-                                       int32_t block_size, int32_t num_blocks, float scale,
-                                       int32_t partition_size, void* workspace,
-                                       size_t workspace_bytes_, void* stream) {
-  const char* fn = "pa_decode_cascade";
-  if (kv_dtype == PA_FP8_E4M3)
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: the shared-prefix pass needs bf16 or f16 caches");
+namespace {
+
+// pa_decode_cascade (q_dtype == kv_dtype, 16-bit) and pa_decode_cascade_fp8.
+pa_status cascade_impl(const char* fn, void* out, pa_dtype out_dtype, const void* query,
+                       pa_dtype q_dtype, const void* key_cache, const void* value_cache,
+                       pa_dtype kv_dtype, float k_scale, float v_scale, pa_layout layout,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t max_context_len,
+                       int32_t common_prefix_len, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                       int32_t num_blocks, float scale, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes_, void* stream) {
+  char msg[200];
+  auto fail = [&](pa_status st, const char* what) {
+    std::snprintf(msg, sizeof msg, "%s: %s", fn, what);
+    return pa_fail(st, msg);
+  };
+  if (!finite_positive(k_scale) || !finite_positive(v_scale))
+    return fail(PA_ERR_INVALID_ARGUMENT, "scales must be positive and finite");
   pa::DecodeArgs a;
-  pa_status st = decode_prepare(fn, out, out_dtype, query, kv_dtype, key_cache, value_cache, kv_dtype, layout,
-                                block_tables, max_blocks_per_seq, context_lens, max_context_len,
-                                num_seqs, num_heads, num_kv_heads, head_size, block_size,
-                                num_blocks, scale, 0, nullptr, 0, true, true, &a);
+  pa_status st = decode_prepare(fn, out, out_dtype, query, q_dtype, key_cache, value_cache,
+                                kv_dtype, layout, block_tables, max_blocks_per_seq, context_lens,
+                                max_context_len, num_seqs, num_heads, num_kv_heads, head_size,
+                                block_size, num_blocks, scale, 0, nullptr, 0, true, true, &a);
   if (st != PA_OK) return st;
-  if (kv_dtype != PA_BF16 && kv_dtype != PA_F16)
-    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: the shared-prefix pass needs bf16 or f16 caches");
+  if (q_dtype != PA_BF16 && q_dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "the shared-prefix pass needs bf16 or f16 queries and caches (or FP8 caches)");
   if (common_prefix_len <= 0 || common_prefix_len % block_size != 0 ||
       common_prefix_len > max_context_len)
-    return pa_fail(PA_ERR_INVALID_ARGUMENT,
-                   "pa_decode_cascade: common_prefix_len must be a positive multiple of block_size "
-                   "and at most max_context_len");
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "common_prefix_len must be a positive multiple of block_size and at most max_context_len");
   if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0))
-    return pa_fail(PA_ERR_INVALID_ARGUMENT,
-                   "pa_decode_cascade: partition_size must be -1, 0 or a positive multiple of 16");
+    return fail(PA_ERR_INVALID_ARGUMENT, "partition_size must be -1, 0 or a positive multiple of 16");
   if (num_seqs == 0) return PA_OK;
   const int32_t suffix = max_context_len - common_prefix_len;
   int32_t ps = partition_size > 0 ? partition_size
@@ -538,16 +542,15 @@ extern "C" pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void
   const int32_t kp = cascade_key_part(num_seqs, num_heads, common_prefix_len);
   const int64_t npp = (common_prefix_len + kp - 1) / kp;
   const int64_t parts = npp + cascade_suffix_parts(max_context_len, common_prefix_len, ps);
-  if (parts > 65535) return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: more than 65535 partitions");
+  if (parts > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 partitions");
   const size_t need = workspace_bytes(num_seqs, num_heads, head_size, parts);
   if (!workspace || workspace_bytes_ < need) {
-    char msg[200];
     std::snprintf(msg, sizeof msg, "%s: needs %zu workspace bytes, got %zu", fn, need,
                   workspace ? workspace_bytes_ : (size_t)0);
     return pa_fail(PA_ERR_WORKSPACE_TOO_SMALL, msg);
   }
   if (!aligned16(workspace) || !aligned16(out))
-    return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_cascade: workspace and out must be 16-byte aligned");
+    return fail(PA_ERR_INVALID_ARGUMENT, "workspace and out must be 16-byte aligned");
   const size_t out_b = (size_t)num_seqs * num_heads * parts * head_size * sizeof(float);
   a.partition_size = ps;
   a.max_partitions = (int32_t)parts;
@@ -556,6 +559,8 @@ extern "C" pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void
   a.key_begin = common_prefix_len;
   a.part_base = (int32_t)npp;
   a.all_partial = true;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
 
   // 1. shared prefix: every sequence's query against the common blocks
   //    (block_tables row 0), once, on matrix cores
@@ -564,6 +569,9 @@ extern "C" pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void
   pr.key_cache = key_cache;
   pr.value_cache = value_cache;
   pr.kv_dtype = kv_dtype;
+  pr.q_dtype = q_dtype;
+  pr.k_scale = k_scale;
+  pr.v_scale = v_scale;
   pr.out_dtype = PA_F32;
   pr.block_tables = block_tables;
   pr.max_blocks_per_seq = max_blocks_per_seq;
@@ -583,6 +591,41 @@ extern "C" pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void
   if (e == hipSuccess) e = pa::launch_decode_main(a, (hipStream_t)stream);
   if (e == hipSuccess) e = pa::launch_decode_reduce(a, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : hip_fail(e, fn);
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_cascade(void* out, pa_dtype out_dtype, const void* query,
+                                       const void* key_cache, const void* value_cache,
+                                       pa_dtype kv_dtype, pa_layout layout,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t common_prefix_len, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t num_blocks, float scale,
+                                       int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes_, void* stream) {
+  if (kv_dtype == PA_FP8_E4M3)
+    return pa_fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: FP8 caches are read by pa_decode_cascade_fp8");
+  return cascade_impl("pa_decode_cascade", out, out_dtype, query, kv_dtype, key_cache, value_cache,
+                      kv_dtype, 1.f, 1.f, layout, block_tables, max_blocks_per_seq, context_lens,
+                      max_context_len, common_prefix_len, num_seqs, num_heads, num_kv_heads,
+                      head_size, block_size, num_blocks, scale, partition_size, workspace,
+                      workspace_bytes_, stream);
+}
+
+extern "C" pa_status pa_decode_cascade_fp8(
+    void* out, pa_dtype out_dtype, const void* query, pa_dtype q_dtype, const void* key_cache,
+    const void* value_cache, float k_scale, float v_scale, pa_layout layout,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t common_prefix_len, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes_, void* stream) {
+  return cascade_impl("pa_decode_cascade_fp8", out, out_dtype, query, q_dtype, key_cache,
+                      value_cache, PA_FP8_E4M3, k_scale, v_scale, layout, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, common_prefix_len,
+                      num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks, scale,
+                      partition_size, workspace, workspace_bytes_, stream);
 }
 
 // ---------------------------------------------------------------- prefill

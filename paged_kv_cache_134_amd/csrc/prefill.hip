@@ -125,10 +125,10 @@ __device__ __forceinline__ void fp8x8_to_f32(const uint4& v, float* out) {
 // byte offsets from the cache base.  PREFIX: the shared-prefix pass of a
 // cascade -- every query row sees every key of its key partition (no causal
 // mask) and writes a (max, sum, unnormalised output) partial instead of a
-// normalised row.  FP8: the caches hold E4M3 codes.
+// normalised row.  FP8: the caches hold E4M3 codes (partials then carry
+// v_scale, as the decode kernels' partials do).
 template <pa_dtype DT, int D, bool OFF32, bool PREFIX, bool FP8>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillParams p) {
-  static_assert(!(FP8 && PREFIX), "the shared-prefix pass reads 16-bit caches");
   constexpr int CB = FP8 ? 1 : 2;               // cache bytes per element
   constexpr int KS = D / 16;                    // 16-wide k-steps over the head dim (QK)
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
@@ -423,13 +423,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     if (j < n) {
       const int64_t pi = ((int64_t)j * p.num_heads + h) * p.max_partitions + s;
       float* po = p.part_out + pi * D;
+      const float vsc = p.v_scale;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           store16(po + db * 32 + 8 * g + 4 * hf,
-                  make_uint4(__float_as_uint(o[db][4 * g]), __float_as_uint(o[db][4 * g + 1]),
-                             __float_as_uint(o[db][4 * g + 2]), __float_as_uint(o[db][4 * g + 3])));
+                  make_uint4(__float_as_uint(o[db][4 * g] * vsc), __float_as_uint(o[db][4 * g + 1] * vsc),
+                             __float_as_uint(o[db][4 * g + 2] * vsc), __float_as_uint(o[db][4 * g + 3] * vsc)));
       if (hf == 0) {
         p.part_ml[2 * pi] = m;
         p.part_ml[2 * pi + 1] = lt;
@@ -473,8 +474,12 @@ hipError_t launch_pd(PrefillParams p, int num_seqs, int max_q, bool off32, bool 
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   p.num_work = (int)pairs;
   dim3 grid((unsigned)blocks), block(kPrefillThreads);
-  if (prefix && fp8) return hipErrorInvalidValue;
-  if (prefix) {
+  if (prefix && fp8) {
+    if (off32)
+      hipLaunchKernelGGL((prefill_kernel<DT, D, true, true, true>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<DT, D, false, true, true>), grid, block, 0, st, p);
+  } else if (prefix) {
     if (off32)
       hipLaunchKernelGGL((prefill_kernel<DT, D, true, true, false>), grid, block, 0, st, p);
     else

@@ -131,6 +131,18 @@ def test_fp8_argument_errors():
     assert pre(out=F16) == 1                    # out is f32 or the query type
     assert pre(n=0) == 0                        # no rows
 
+    # an explicit partition size fixes the workspace the call needs, so the
+    # too-small case fails its check before any launch
+    n256 = P.pa_decode_cascade_workspace_size(100, 32, 128, 3000, 1792, 256)
+
+    def cas(q=BF, ks=0.5, ws=v, wsb=n256 - 16, prefix=1792):
+        return lib.pa_decode_cascade_fp8(v, 0, v, q, v, v, ks, 0.5, 0, v, 200, v, 3000, prefix, 100,
+                                         32, 32, 128, 256, 300, 1.0, 256, ws, wsb, None)
+
+    assert cas(ks=0.0) == 1 and cas(q=F32) == 1
+    assert cas(prefix=1800) == 1                # not block-aligned
+    assert cas() == 3 and cas(ws=None, wsb=0) == 3  # workspace too small / missing
+
 
 def test_swap_blocks_host_checks():
     """pa_swap_blocks checks every block id on the host and enqueues nothing

@@ -219,3 +219,36 @@ def test_fp8_prefill_small(name, cfg, over, layout):
         announce("query", qdt, "max-abs", err)
         assert np.all(np.isfinite(got))
         assert err <= TOL["bf16"], (name, qdt, err, where)
+
+
+@pytest.mark.parametrize("layout", [P.NHD, P.HND])
+@pytest.mark.parametrize("name,over", [
+    ("mha", dict(S=5, H=4, Hkv=4, prefix=600, suffix_lo=20, suffix_hi=90)),
+    ("gqa", dict(S=6, H=16, Hkv=2, prefix=700, suffix_lo=1, suffix_hi=300)),
+])
+def test_fp8_cascade_decode_small(name, over, layout):
+    """Shared-prefix (cascade) decode over FP8 pools equals the plain
+    definition over the codes read back."""
+    need_gpu()
+    w = workloads.make("5a", **over)
+    announce("fp8 cascade", name, "layout", layout)
+    dw = _setup(w, layout)
+    st = build_state(w)
+    common = (w.prefix_len // w.bs) * w.bs
+    kc, vc = build_pool(w, st, layout=layout, include_step=True, kv_dtype="e4m3", k_scale=KS,
+                        v_scale=VS)
+    ref = A.decode_ref(w.query, kc, vc, st.block_tables, w.context_lens, w.scale, w.bs, w.dtype,
+                       layout, kv_dtype="e4m3", k_scale=KS, v_scale=VS)
+    for part in (-1, 0, 64):
+        out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+        nbytes = P.pa_decode_cascade_workspace_size(w.S, w.H, w.D, dw.max_context_len, common, part)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        P.pa_decode_cascade_fp8(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                dw.context_lens, dw.max_context_len, common, w.scale, KS, VS, ws,
+                                layout=layout, partition_size=part)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        err, where = max_abs(got, ref)
+        announce("partition", part, "max-abs", err)
+        assert np.all(np.isfinite(got))
+        assert err <= TOL["bf16"], (name, part, err, where)
