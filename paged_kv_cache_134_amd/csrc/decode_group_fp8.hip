@@ -83,7 +83,10 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
 
   const int kvh = blockIdx.x % p.num_kv_heads;
   const int s = blockIdx.x / p.num_kv_heads;
-  const int part = blockIdx.y;
+  // partitions are dispatched last-first: only long contexts have high
+  // partitions, so the longest-running workgroups start early and short
+  // ones fill the tail
+  const int part = gridDim.y - 1 - blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
