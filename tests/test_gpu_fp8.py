@@ -29,6 +29,8 @@ SMALL = {
     "long": (4, dict(S=2, H=16, Hkv=2, lens=[3000, 2049])),
     "g2-d64": (2, dict(S=4, H=8, Hkv=4, D=64, len_lo=50, len_hi=400, n_pad=1)),
     "g16": (3, dict(S=3, H=32, Hkv=2, len_median=400, len_cap=900)),
+    "g4-d64-bs8": (3, dict(S=4, H=8, Hkv=2, D=64, bs=8, len_median=250, len_cap=800)),
+    "g16-d64": (3, dict(S=3, H=32, Hkv=2, D=64, len_median=300, len_cap=700)),
 }
 
 

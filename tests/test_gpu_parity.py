@@ -27,6 +27,12 @@ SMALL = {
     "gqa": (3, dict(S=8, H=16, Hkv=2, len_median=300, len_cap=1500)),
     "long": (4, dict(S=2, H=16, Hkv=2, lens=[3000, 2049])),
     "shared": ("5a", dict(S=5, H=4, Hkv=4, prefix=600, suffix_lo=20, suffix_hi=90)),
+    # every group size and both head sizes of the two decode kernels
+    "g2-d64": (2, dict(S=4, H=8, Hkv=4, D=64, len_lo=50, len_hi=400, n_pad=1)),
+    "g4": (3, dict(S=5, H=16, Hkv=4, len_median=300, len_cap=1000)),
+    "g4-d64-bs8": (3, dict(S=4, H=8, Hkv=2, D=64, bs=8, len_median=250, len_cap=800)),
+    "g16": (3, dict(S=3, H=32, Hkv=2, len_median=400, len_cap=900)),
+    "g16-d64": (3, dict(S=3, H=32, Hkv=2, D=64, len_median=300, len_cap=700)),
 }
 
 
