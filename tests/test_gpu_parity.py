@@ -176,6 +176,8 @@ def test_f16_decode(G):
     ("prefix-suffix", "5c", dict(S=4, H=2, Hkv=2, prefix=600, suffix_lo=20, suffix_hi=200)),
     ("prefix-suffix-bs16", "5c", dict(S=3, H=2, Hkv=1, bs=16, prefix=300, suffix_lo=60,
                                       suffix_hi=150)),
+    ("d64-g16-bs4", "5c", dict(S=3, H=32, Hkv=2, D=64, bs=4, prefix=200, suffix_lo=1,
+                               suffix_hi=140)),
 ])
 def test_prefill_small(name, cfg, over, layout):
     need_gpu()
