@@ -196,7 +196,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
 /*
  * Partition size for this decode shape (0 = single pass): 512 for the
  * per-head kernel (group size 1 or 2, or fp32), a larger power of two for
- * the grouped kernel while about two workgroups per resident slot remain.
+ * the grouped kernels (group size 4, 8 or 16 with bf16, f16 or
+ * PA_FP8_E4M3 caches) while about two workgroups per resident slot remain.
  * total_context_len is the sum of context_lens when the caller knows it
  * (<= 0: unknown, num_seqs * max_context_len is assumed); partition_size -1
  * in the decode calls resolves with it unknown.  Never below 512, so a
