@@ -1,5 +1,5 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-bench times (NHD pools, split-K decode with the automatic partition size),
+bench times (HND pools, split-K decode with the automatic partition size),
 on sampled outputs the oracle computes one by one, plus properties that hold
 at any size (every output finite, sampled pool slots bit-exact).
 
@@ -58,7 +58,7 @@ def test_decode_full_size_sampled(cfg):
     need_gpu()
     w = workloads.make(cfg)
     announce("full-size decode", w.name)
-    dw = M.setup(w, write_step=True)
+    dw = M.setup(w, layout=P.HND, write_step=True)
     st = build_state(w)
     assert np.array_equal(dw.block_tables_host, st.block_tables)
     ps = P.pa_decode_auto_partition(w.S, w.H, w.Hkv, P.KV_DTYPE[w.dtype], dw.max_context_len,
@@ -68,7 +68,7 @@ def test_decode_full_size_sampled(cfg):
                      dtype=torch.uint8, device="cuda")
     out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
     P.pa_decode_partitions(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
-                           dw.context_lens, dw.max_context_len, w.scale, ps, ws)
+                           dw.context_lens, dw.max_context_len, w.scale, ps, ws, layout=dw.layout)
     P.pa_decode_reduce(out, dw.context_lens, dw.max_context_len, w.Hkv, ps, ws)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
@@ -94,12 +94,13 @@ def test_prefill_full_size_sampled(cfg):
     need_gpu()
     w = workloads.make(cfg)
     announce("full-size prefill", w.name)
-    dw = M.setup(w, write_step=True)
+    dw = M.setup(w, layout=P.HND, write_step=True)
     st = build_state(w)
     assert np.array_equal(dw.block_tables_host, st.block_tables)
     out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
     P.pa_prefill(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables, dw.query_start_loc,
-                 dw.context_lens, int(w.query_lens.max()), dw.max_context_len, w.scale)
+                 dw.context_lens, int(w.query_lens.max()), dw.max_context_len, w.scale,
+                 layout=dw.layout)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
@@ -128,7 +129,7 @@ def test_cascade_decode_full_size_sampled():
     need_gpu()
     w = workloads.make("5a")
     announce("full-size cascade decode", w.name)
-    dw = M.setup(w, write_step=True)
+    dw = M.setup(w, layout=P.HND, write_step=True)
     st = build_state(w)
     common = (w.prefix_len // w.bs) * w.bs
     nbc = common // w.bs
@@ -137,7 +138,7 @@ def test_cascade_decode_full_size_sampled():
                      dtype=torch.uint8, device="cuda")
     out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
     P.pa_decode_cascade(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
-                        dw.context_lens, dw.max_context_len, common, w.scale, ws)
+                        dw.context_lens, dw.max_context_len, common, w.scale, ws, layout=dw.layout)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
