@@ -266,8 +266,8 @@ pa_status pa_decode_partitions_fp8(void* out, pa_dtype out_dtype, const void* qu
  * sum_t 2^(z_t - m_p) V_t (fp32).  Partitions at or past L are not written.
  * Heads of sequences whose whole context is one partition (L <=
  * partition_size) get their final row written to `out` directly instead.
- * partition_size must be > 0 (or -1 resolving to > 0); other arguments as in
- * pa_decode.
+ * partition_size must be > 0 (PA_ERR_INVALID_ARGUMENT otherwise); other
+ * arguments as in pa_decode.
  *
  * pa_decode_reduce -- merges the ceil(L / partition_size) partitions of every
  * (sequence, head) with L > partition_size using the log-sum-exp rule
