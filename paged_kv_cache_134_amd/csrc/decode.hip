@@ -32,7 +32,8 @@ namespace {
 // Split-K reduce ("V2" reduce): for one (sequence, head), M = max_p m_p and
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over the partitions
 // that hold tokens.  One wave per (sequence, head), D/64 columns per lane,
-// 8 partitions' loads in flight together.  Heads whose context is a single
+// 8 partitions' loads in flight together; with at most 8 partitions the
+// maximum, sums and outputs come in one round trip.  Heads whose context is a single
 // partition were written directly by the partition kernel.
 constexpr int kReduceThreads = 256;
 
@@ -50,13 +51,42 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   const float* ml = p.part_ml + sh * p.max_partitions * 2;
   const float* po = p.part_out + sh * p.max_partitions * D + lane * CPL;
 
-  float M = -INFINITY;
-  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[2 * i]);
-  M = wave_max(M);
-
   float o[CPL], lsum = 0.f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) o[c] = 0.f;
+  if (np > 0 && np <= 8) {
+    // one round trip: every partial's (max, sum, output) is requested
+    // together, the maximum taken from what arrived
+    float mv[8], lv[8], ov[8][CPL];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int kk = min(k, np - 1);  // (repeats of the last partial are not used)
+      mv[k] = ml[2 * kk];
+      lv[k] = ml[2 * kk + 1];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ov[k][c] = po[(int64_t)kk * D + c];
+    }
+    float M = mv[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) M = k < np ? fmaxf(M, mv[k]) : M;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < np) {
+        const float a = exp2_diff(mv[k], M);
+        lsum += a * lv[k];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[c] += a * ov[k][c];
+      }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) store_out(p.out, sh * D + lane * CPL + c, o[c] * inv, p.out_dtype);
+    return;
+  }
+
+  float M = -INFINITY;
+  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[2 * i]);
+  M = wave_max(M);
   int i = 0;
   for (; i + 8 <= np; i += 8) {
     float mv[8], lv[8], ov[8][CPL];
