@@ -17,15 +17,21 @@
 //            moves only when some score exceeds it by more than 2^8; the
 //            probabilities are rounded to f16 once and the normaliser sums
 //            the rounded values.
-//   PV       the tile's V rows pass through the wave's own LDS region as f16
-//            (exact for every E4M3 value) and are accumulated on f16 v_dot2,
-//            a lane owning D/32 columns of every head (the two half-waves
-//            take alternate token pairs).
+//   PV       O^T[16 d x 16 heads] += V^T P^T on v_mfma_f32_16x16x16_f16,
+//            one product per 16 columns.  The B operand is the lane's own
+//            four probabilities: the QK product left tokens 4 q4 .. +3 of
+//            head l % 16 in exactly the B layout, so P never leaves the
+//            registers.  The A operand (16 columns x 16 tokens) is read
+//            transposed from the tile's V rows, which pass through the wave's
+//            own LDS region as f16 (exact for every E4M3 value); a lane then
+//            holds O[head l % 16][16 b + 4 q4 .. +3] for every block b.
 // Each wave keeps two tiles of K/V in flight (the next two rounds) and reads
 // the block ids it needs from the table two rounds ahead of the rows they
 // locate.  The waves' (max, sum, output) states are merged at the end by the
-// log-sum-exp rule.  With 16-bit caches the LDS-staged grouped kernel
-// (decode_group.hip) is faster and is used instead.
+// log-sum-exp rule.  Heads past G are zero in the query operand, so their
+// scores, probabilities and outputs are never used.  With 16-bit caches the
+// LDS-staged grouped kernel (decode_group.hip) is faster and is used
+// instead.
 #include <hip/hip_runtime.h>
 
 #include "decode_common.h"
@@ -40,6 +46,7 @@ constexpr int kRound = kTile * kDecodeWaves;  // tokens per workgroup per round
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 template <pa_dtype DT>
 __device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
@@ -72,10 +79,9 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   constexpr int NLD = D / 64;           // 16-byte loads per lane per row (a quarter row)
   constexpr int RC = D / 8;             // 16-byte LDS pieces per V row
   constexpr int VSTR = RC + 1;          // padded LDS row stride in pieces
-  constexpr int DPL = D / 32;           // output columns per lane in PV
+  constexpr int DB = D / 16;            // PV: 16-column blocks of O^T
   constexpr int kWaveV = kTile * VSTR;                 // pieces of one wave's V region
-  constexpr int kWaveP = (kTile / 2) * G;              // f16 pairs of one wave's P region
-  constexpr int kLdsMain = (kDecodeWaves * kWaveV) * 16 + kDecodeWaves * kWaveP * 4;
+  constexpr int kLdsMain = (kDecodeWaves * kWaveV) * 16;
   constexpr int kLdsMerge = kDecodeWaves * G * D * 4;
   constexpr int kLds = kLdsMain > kLdsMerge ? kLdsMain : kLdsMerge;
   __shared__ __align__(16) char smem[kLds];
@@ -129,10 +135,9 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   const int64_t lane_off = (int64_t)kvh * p.head_stride + q4 * 16;  // bytes
 
   uint4* sV = reinterpret_cast<uint4*>(smem) + wave * kWaveV;
-  uint32_t* sP = reinterpret_cast<uint32_t*>(smem + kDecodeWaves * kWaveV * 16) + wave * kWaveP;
-
-  const int half = lane / 32;  // PV: token parity of the pairs this half-wave takes
-  const int dl = lane % 32;    // PV: output columns dl * DPL .. + DPL - 1
+  // PV A operand: V^T[d = 16 b + tl][token 4 q4 + j], j = 0..3, read from the
+  // wave's f16 rows (row stride VSTR pieces)
+  const _Float16* vh = reinterpret_cast<const _Float16*>(sV) + (4 * q4) * (VSTR * 8) + tl;
 
   auto block_of = [&](int ts) -> int32_t { return bt[min(ts + tl, t1 - 1) >> lbs]; };
   // K and V pieces of the lane's token in tile ts (rows past the end are
@@ -156,11 +161,10 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   };
 
   float m_ref = -INFINITY, l_lane = 0.f;  // softmax state of head tl (this wave's tokens)
-  float acc[G][DPL];
+  // O^T blocks: lane holds O[head tl][d = 16 b + 4 q4 + j]
+  f32x4_t o[DB];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+  for (int b = 0; b < DB; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Consumes tile ts from (kr, vr), then refills them with the tile two
   // rounds ahead (its block ids were read two rounds ago).
@@ -202,11 +206,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
       m_ref = mn;
       l_lane *= alpha;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float a = __shfl(alpha, h);  // lane h holds head h
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[h][e] *= a;
-      }
+      for (int b = 0; b < DB; ++b) o[b] *= alpha;  // the lane's own head
     }
     _Float16 ph[4];
 #pragma unroll
@@ -214,46 +214,22 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
       ph[r] = (_Float16)(z[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref));
       l_lane += (float)ph[r];
     }
-    if (tl < G) {  // token pairs (4 q4, 4 q4 + 1) and (4 q4 + 2, 4 q4 + 3) of head tl
-      sP[(2 * q4) * G + tl] = __builtin_bit_cast(uint32_t, f16x2_t{ph[0], ph[1]});
-      sP[(2 * q4 + 1) * G + tl] = __builtin_bit_cast(uint32_t, f16x2_t{ph[2], ph[3]});
-    }
-    wave_lds_sync();
+    wave_lds_sync();  // the tile's V rows are visible to the whole wave
 
-    // ---- PV: token pairs 2 i + half of the tile, D/32 columns of every head
+    // ---- PV on matrix cores: O^T[16 d x 16 heads] += V^T[16 d x 16 tokens]
+    // P^T[16 tokens x 16 heads] per block of 16 columns
+    // (v_mfma_f32_16x16x16_f16).  The B operand is this lane's own four
+    // probabilities (tokens 4 q4 .. +3 of head tl, where the QK product put
+    // them; zero past the group and the context).
+    const f16x4_t pb = {ph[0], ph[1], ph[2], ph[3]};
 #pragma unroll
-    for (int i = 0; i < kTile / 4; ++i) {
-      const int pr = 2 * i + half;
-      const char* va = reinterpret_cast<const char*>(sV + (2 * pr) * VSTR) + dl * DPL * 2;
-      const char* vb = va + VSTR * 16;
-      uint32_t wa[DPL / 2], wb[DPL / 2];
-      if constexpr (DPL == 4) {
-        const uint2 a2 = *reinterpret_cast<const uint2*>(va);
-        const uint2 b2 = *reinterpret_cast<const uint2*>(vb);
-        wa[0] = a2.x; wa[1] = a2.y; wb[0] = b2.x; wb[1] = b2.y;
-      } else {
-        wa[0] = *reinterpret_cast<const uint32_t*>(va);
-        wb[0] = *reinterpret_cast<const uint32_t*>(vb);
-      }
-      uint32_t pw[G];
-      const uint4* pq = reinterpret_cast<const uint4*>(sP + pr * G);
+    for (int b = 0; b < DB; ++b) {
+      f16x4_t a;
 #pragma unroll
-      for (int h4 = 0; h4 < G / 4; ++h4) {
-        const uint4 x = pq[h4];
-        pw[4 * h4] = x.x; pw[4 * h4 + 1] = x.y; pw[4 * h4 + 2] = x.z; pw[4 * h4 + 3] = x.w;
-      }
-      uint32_t vv[DPL];  // (row 2 pr, row 2 pr + 1) f16 pairs per column
-#pragma unroll
-      for (int c = 0; c < DPL; ++c)
-        vv[c] = __builtin_amdgcn_perm(wb[c / 2], wa[c / 2], (c & 1) ? 0x07060302u : 0x05040100u);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int c = 0; c < DPL; ++c)
-          acc[h][c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[h]),
-                                             __builtin_bit_cast(f16x2_t, vv[c]), acc[h][c], false);
+      for (int j = 0; j < 4; ++j) a[j] = vh[j * (VSTR * 8) + 16 * b];
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, o[b], 0, 0, 0);
     }
-    wave_lds_sync();  // this tile's V and P are consumed before the next tile's stores
+    wave_lds_sync();  // this tile's V is consumed before the next tile's stores
   };
 
   // Two tile buffers alternate, so two tiles per wave are always in flight.
@@ -272,22 +248,19 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   l_lane += __shfl_xor(l_lane, 32);
   const float m_out = m_ref, l_out = l_lane;
 
-  // ---- merge: half-waves, then waves (log-sum-exp rule)
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
+  // ---- merge of the waves (log-sum-exp rule)
   if (lane < G) {
     sM[wave][lane] = m_out;
     sL[wave][lane] = l_out;
   }
   __syncthreads();  // every wave's loop is done: the LDS rows are free
   float* sAcc = reinterpret_cast<float*>(smem);  // [waves][G][D]
-  if (half == 0) {
+  if (tl < G) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) sAcc[(wave * G + h) * D + dl * DPL + e] = acc[h][e];
+    for (int b = 0; b < DB; ++b)
+      store16(sAcc + (wave * G + tl) * D + 16 * b + 4 * q4,
+              make_uint4(__float_as_uint(o[b][0]), __float_as_uint(o[b][1]), __float_as_uint(o[b][2]),
+                         __float_as_uint(o[b][3])));
   }
   __syncthreads();
   const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
