@@ -183,7 +183,10 @@ pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
  *                        reduce ("V2", [vllm] §7.3); a multiple of 16
  *                   -1 = chosen by the library from the shape
  *   workspace    (device) >= pa_decode_workspace_size(...) bytes when split-K
- *                is used (may be NULL for partition_size 0)
+ *                is used (may be NULL for partition_size 0): the partials
+ *                and, for the grouped kernels, the partition kernel's
+ *                dispatch list (largest partitions first); no content is
+ *                needed on entry
  * Supported: head_size 64 or 128; num_heads / num_kv_heads in {1,2,4,8,16};
  * block_size a power of two in [1, 1024]; PA_LAYOUT_NHD or PA_LAYOUT_HND.
  * Results are bitwise deterministic for a fixed launch configuration and do

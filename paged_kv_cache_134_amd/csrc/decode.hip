@@ -46,6 +46,11 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   const int lane = threadIdx.x % kWave;
   const int s = (int)(sh / p.num_heads);
   const int L = p.context_lens[s];
+  if (L == 0 && !p.all_partial) {  // empty context: no partition holds a token, the row is zero
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) store_out(p.out, sh * D + lane * CPL + c, 0.f, p.out_dtype);
+    return;
+  }
   if (single_partition(p, L)) return;
   const int np = p.part_base + (L > p.key_begin ? (L - p.key_begin + p.partition_size - 1) / p.partition_size : 0);
   const float* ml = p.part_ml + sh * p.max_partitions * 2;
@@ -116,6 +121,87 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   for (int c = 0; c < CPL; ++c) store_out(p.out, sh * D + lane * CPL + c, o[c] * inv, p.out_dtype);
 }
 
+// ------------------------------------------------------------ dispatch list
+// Split-K dispatch list, one workgroup.  Hardware dispatch starts workgroups
+// in id order, so the list orders the partitions largest first: every full
+// partition (partition_size tokens), sequence by sequence, then each
+// sequence's shorter last partition in kItemBuckets classes of decreasing
+// size (a class spans partition_size / kItemBuckets tokens; the order
+// within a class is whatever the LDS atomics give).  Long work then starts
+// early and the shortest fills the end (longest-processing-time-first
+// scheduling), and no empty workgroup is dispatched before the last item:
+// the grid's unused tail is dispatched last and exits at once.  Only an
+// order: every partial and the reduce are those of the (pairs, partitions)
+// grid, so results do not depend on it.
+constexpr int kItemBuckets = 64;
+
+__global__ __launch_bounds__(kDecodeThreads) void decode_items_kernel(const DecodeParams p) {
+  __shared__ int32_t red[kDecodeWaves];
+  __shared__ int32_t sCnt[kItemBuckets];  // shorter partitions per size class, then the class cursors
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int S = p.num_seqs, hkv = p.num_kv_heads, P = p.partition_size;
+  int4* items = reinterpret_cast<int4*>(p.items);
+  auto bucket = [&](int r) { return (P - r) * kItemBuckets / P; };  // r in [1, P): 0 = longest
+  // exclusive prefix of x over the workgroup; total = the sum
+  auto scan = [&](int x, int& total) -> int {
+    int incl = x;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane == kWave - 1) red[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      if (w < wave) before += red[w];
+      total += red[w];
+    }
+    __syncthreads();  // red is rewritten by the next scan
+    return before + incl - x;
+  };
+  if (tid < kItemBuckets) sCnt[tid] = 0;
+  __syncthreads();
+  // full partitions in sequence order; shorter ones counted per class
+  int full_base = 0, rem_total = 0;
+  for (int i0 = 0; i0 < S; i0 += kDecodeThreads) {
+    const int i = i0 + tid;
+    const int L = i < S ? p.context_lens[i] : 0;
+    const int f = L / P, r = L - f * P;
+    int nf;
+    const int fx = scan(f, nf);
+    for (int y = 0; y < f; ++y)
+      for (int k = 0; k < hkv; ++k) items[(int64_t)(full_base + fx + y) * hkv + k] = make_int4(i, k, y, 0);
+    if (r > 0) atomicAdd(&sCnt[bucket(r)], 1);
+    full_base += nf;
+  }
+  __syncthreads();
+  if (wave == 0) {  // class cursors: after the full partitions, longest class first
+    const int c = lane < kItemBuckets ? sCnt[lane] : 0;
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane < kItemBuckets) sCnt[lane] = full_base + incl - c;
+    rem_total = __shfl(incl, kWave - 1);
+  }
+  __syncthreads();
+  for (int i0 = 0; i0 < S; i0 += kDecodeThreads) {  // shorter partitions at their class cursors
+    const int i = i0 + tid;
+    const int L = i < S ? p.context_lens[i] : 0;
+    const int f = L / P, r = L - f * P;
+    if (r > 0) {
+      const int pos = atomicAdd(&sCnt[bucket(r)], 1);
+      for (int k = 0; k < hkv; ++k) items[(int64_t)pos * hkv + k] = make_int4(i, k, f, 0);
+    }
+  }
+  if (tid == 0) *p.item_count = (full_base + rem_total) * hkv;
+}
+
 DecodeParams make_params(const DecodeArgs& a) {
   const PoolGeom& g = a.geom;
   DecodeParams p{};
@@ -150,6 +236,9 @@ DecodeParams make_params(const DecodeArgs& a) {
   p.out_dtype = a.out_dtype;
   const int64_t elem = a.kv_dtype == PA_F32 ? 4 : a.kv_dtype == PA_FP8_E4M3 ? 1 : 2;
   p.off32 = (int64_t)g.num_blocks * p.blk_stride * elem <= (int64_t)UINT32_MAX;
+  p.item_count = a.item_count;
+  p.items = a.items;
+  p.num_seqs = a.num_seqs;
   return p;
 }
 
@@ -162,13 +251,33 @@ bool decode_uses_group_kernel(pa_dtype kv_dtype, int G) {
 
 hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
-  const dec::DecodeParams p = dec::make_params(a);
+  dec::DecodeParams p = dec::make_params(a);
   const PoolGeom& g = a.geom;
   const int G = a.num_heads / g.num_kv_heads;
   dim3 grid((unsigned)(a.num_seqs * g.num_kv_heads),
             a.partition_size > 0 ? a.max_partitions - a.part_base : 1);
   if (grid.y == 0) return hipSuccess;
   const bool group = decode_uses_group_kernel(a.kv_dtype, G);
+  // The grouped kernels' split-K over whole contexts (not a cascade's
+  // suffixes) of many (sequence, kv head) pairs takes the largest-first
+  // dispatch list: on the lognormal 70B-like batch (1,024 pairs) 169 -> 158
+  // us (bf16) and 108 -> 101 us (FP8), the list's one-workgroup launch
+  // included.  Few pairs (the long-context batch: 64, every partition full)
+  // and the per-head kernel (uniform 7B-like batch) gain no order and would
+  // only pay the launch, so they keep the grid.
+  const int64_t items = (int64_t)grid.x * grid.y;
+  const bool listed = a.items && a.partition_size > 0 && a.key_begin == 0 && a.part_base == 0 &&
+                      !a.all_partial && group && grid.x >= 2u * (unsigned)device_cus() &&
+                      items <= 0x7FFFFFFF;
+  if (listed) {
+    hipLaunchKernelGGL(dec::decode_items_kernel, dim3(1), dim3(dec::kDecodeThreads), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    grid = dim3((unsigned)items);
+  } else {
+    p.items = nullptr;
+    p.item_count = nullptr;
+  }
   if (a.kv_dtype == PA_FP8_E4M3)
     return group ? dec::launch_group_fp8(p, a.q_dtype, g.head_size, G, grid, stream)
                  : dec::launch_head_fp8(p, a.q_dtype, g.head_size, G, grid, stream);

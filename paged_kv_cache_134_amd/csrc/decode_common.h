@@ -46,7 +46,32 @@ struct DecodeParams {
   float v_scale;            // FP8 caches: V scale, applied to the merged output (else 1)
   pa_dtype out_dtype;
   bool off32;  // every byte offset into either cache fits in 32 bits
+  // Split-K dispatch list (null: the grid is (pairs, partitions)): workgroup
+  // b takes item b -- (sequence, kv head, partition) -- while b < *item_count.
+  int32_t* item_count;
+  int32_t* items;
+  int32_t num_seqs;
 };
+
+// The (sequence, kv head, partition) of this workgroup: from the dispatch
+// list when there is one, else from the (pairs, partitions) grid, partitions
+// taken last-first when last_first (only long contexts have high
+// partitions, so their workgroups start early).  False: nothing to do.
+__device__ __forceinline__ bool decode_item(const DecodeParams& p, bool last_first, int& s, int& kvh,
+                                            int& part) {
+  if (p.items) {
+    if ((int)blockIdx.x >= *p.item_count) return false;
+    const int4 it = reinterpret_cast<const int4*>(p.items)[blockIdx.x];
+    s = __builtin_amdgcn_readfirstlane(it.x);
+    kvh = __builtin_amdgcn_readfirstlane(it.y);
+    part = __builtin_amdgcn_readfirstlane(it.z);
+    return true;
+  }
+  kvh = blockIdx.x % p.num_kv_heads;
+  s = blockIdx.x / p.num_kv_heads;
+  part = last_first ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
+  return true;
+}
 
 // Maximum over the 64 lanes of a wave (every lane receives it).
 __device__ __forceinline__ float wave_max(float x) {

@@ -63,12 +63,8 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
   uint4* sK = sKV;
   uint4* sV = sKV + kChunk * KSTR;
 
-  const int kvh = blockIdx.x % p.num_kv_heads;
-  const int s = blockIdx.x / p.num_kv_heads;
-  // partitions are dispatched last-first: only long contexts have high
-  // partitions, so the longest-running workgroups start early and short
-  // ones fill the tail
-  const int part = gridDim.y - 1 - blockIdx.y;
+  int s, kvh, part;
+  if (!decode_item(p, true, s, kvh, part)) return;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);

@@ -87,12 +87,8 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   __shared__ __align__(16) char smem[kLds];
   __shared__ float sM[kDecodeWaves][G], sL[kDecodeWaves][G];
 
-  const int kvh = blockIdx.x % p.num_kv_heads;
-  const int s = blockIdx.x / p.num_kv_heads;
-  // partitions are dispatched last-first: only long contexts have high
-  // partitions, so the longest-running workgroups start early and short
-  // ones fill the tail
-  const int part = gridDim.y - 1 - blockIdx.y;
+  int s, kvh, part;
+  if (!decode_item(p, true, s, kvh, part)) return;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);

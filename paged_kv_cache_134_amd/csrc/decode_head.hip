@@ -39,9 +39,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
   static_assert(LPT >= 1 && LPT <= kWave && (kWave % LPT) == 0, "bad head size");
   __shared__ int32_t s_bt[kWindow + 1];
 
-  const int kvh = blockIdx.x % p.num_kv_heads;
-  const int s = blockIdx.x / p.num_kv_heads;
-  const int part = blockIdx.y;
+  int s, kvh, part;
+  if (!decode_item(p, false, s, kvh, part)) return;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int tg = lane / LPT;  // lane group (token row) within the wave

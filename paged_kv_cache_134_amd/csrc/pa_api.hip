@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -48,10 +49,18 @@ int64_t partitions_for(int32_t max_context_len, int32_t partition_size) {
   return partition_size > 0 ? (max_context_len + (int64_t)partition_size - 1) / partition_size : 0;
 }
 
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Split-K workspace: partial outputs [S, H, parts, D] fp32, partial (max,
+// sum) [S, H, parts, 2] fp32, then the dispatch list of the partition
+// kernel: a 256-byte header (item count) and one 16-byte item per (sequence,
+// kv head, partition), num_heads bounding num_kv_heads.  Each part starts on
+// a 256-byte boundary.
 size_t workspace_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_size, int64_t parts) {
   const size_t out_b = (size_t)(num_seqs * num_heads * parts * head_size) * sizeof(float);
   const size_t ml_b = (size_t)(num_seqs * num_heads * parts * 2) * sizeof(float);
-  return ((out_b + 255) / 256) * 256 + ml_b;
+  const size_t items_b = 256 + (size_t)(num_seqs * num_heads * parts) * 4 * sizeof(int32_t);
+  return round256(out_b) + round256(ml_b) + items_b;
 }
 
 }  // namespace
@@ -194,23 +203,24 @@ extern "C" pa_status pa_swap_blocks(const void* src_key_cache, const void* src_v
 }
 
 // ----------------------------------------------------------------- decode
-namespace {
+namespace pa {
 
-// Compute units of the current device (256 on MI355X), asked once.
 int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
+  static std::atomic<int> cus{0};
+  int c = cus.load(std::memory_order_relaxed);
+  if (c == 0) {
     int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+    c = hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                n > 0
+            ? n
+            : 256;
+    cus.store(c, std::memory_order_relaxed);
   }
-  return cus;
+  return c;
 }
 
-}  // namespace
+}  // namespace pa
 
 // Per-head kernel: 512-token partitions as soon as a context is longer.
 // Grouped kernel (one workgroup reads a kv head for all G query heads, so a
@@ -226,7 +236,7 @@ extern "C" int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_heads,
   if (!pa::decode_uses_group_kernel(kv_dtype, num_heads / num_kv_heads)) return 512;
   const int64_t total = total_context_len > 0 ? total_context_len
                                               : (int64_t)num_seqs * max_context_len;
-  const int64_t want = 2 * 4 * (int64_t)device_cus();
+  const int64_t want = 2 * 4 * (int64_t)pa::device_cus();
   for (int32_t ps = 8192; ps > 512; ps /= 2) {
     if (ps >= max_context_len) continue;
     const int64_t wgs = (int64_t)num_kv_heads * (total / ps + num_seqs / 2);
@@ -326,8 +336,12 @@ pa_status decode_prepare(const char* fn, void* out, pa_dtype out_dtype, const vo
     if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     a->max_partitions = (int32_t)parts;
     const size_t out_b = (size_t)num_seqs * num_heads * parts * head_size * sizeof(float);
-    a->part_out = static_cast<float*>(workspace);
-    a->part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((out_b + 255) / 256) * 256);
+    const size_t ml_b = (size_t)num_seqs * num_heads * parts * 2 * sizeof(float);
+    char* w = static_cast<char*>(workspace);
+    a->part_out = reinterpret_cast<float*>(w);
+    a->part_ml = reinterpret_cast<float*>(w + round256(out_b));
+    a->item_count = reinterpret_cast<int32_t*>(w + round256(out_b) + round256(ml_b));
+    a->items = a->item_count + 64;  // after the 256-byte header
   }
   return PA_OK;
 }
@@ -555,7 +569,7 @@ pa_status cascade_impl(const char* fn, void* out, pa_dtype out_dtype, const void
   a.partition_size = ps;
   a.max_partitions = (int32_t)parts;
   a.part_out = static_cast<float*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((out_b + 255) / 256) * 256);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(out_b));
   a.key_begin = common_prefix_len;
   a.part_base = (int32_t)npp;
   a.all_partial = true;

@@ -15,6 +15,9 @@ pa_status pa_fail(pa_status st, const char* msg);
 
 namespace pa {
 
+// Compute units of the current device (256 on MI355X), asked once.
+int device_cus();
+
 // Geometry of a paged K/V pool, in elements.
 struct PoolGeom {
   int32_t num_kv_heads;
@@ -64,6 +67,10 @@ struct DecodeArgs {
   int32_t key_begin = 0;   // cascade: partitions cover [key_begin, L) ...
   int32_t part_base = 0;   // ... and start at this workspace partition
   bool all_partial = false;  // cascade: prefix partials exist, never finish a head early
+  // Split-K dispatch list in the workspace (see launch_decode_main): item
+  // count, then [items][4] int32 (sequence, kv head, partition, 0).
+  int32_t* item_count = nullptr;
+  int32_t* items = nullptr;
 };
 
 // Single pass (partition_size == 0) or the split-K partition kernel.

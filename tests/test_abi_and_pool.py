@@ -185,9 +185,13 @@ def test_cascade_argument_errors_and_workspace():
 
 
 def test_workspace_size():
+    """Split-K workspace: partial outputs, partial (max, sum), then the
+    dispatch list (256-byte header and 16 bytes per (sequence, head,
+    partition)), each part 256-byte aligned."""
     ws = P.pa_decode_workspace_size(8, 64, 128, 131072, 512)
     parts = 256
-    assert ws >= 8 * 64 * parts * (128 + 2) * 4
+    r256 = lambda n: -(-n // 256) * 256  # noqa: E731
+    assert ws == r256(8 * 64 * parts * 128 * 4) + r256(8 * 64 * parts * 2 * 4) + 256 + 8 * 64 * parts * 16
     assert P.pa_decode_workspace_size(8, 64, 128, 131072, 0) == 0
     assert P.pa_decode_workspace_size(8, 64, 128, 100, -1) >= 8 * 64 * 130 * 4
 

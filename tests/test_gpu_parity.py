@@ -17,6 +17,8 @@ from oracle.state import build_pool, build_state
 
 pytestmark = pytest.mark.gpu
 
+KS, VS = workloads.FP8_K_SCALE, workloads.FP8_V_SCALE
+
 P = pytest.importorskip("paged_kv_cache_134_amd")
 from paged_kv_cache_134_amd import metadata as M  # noqa: E402
 
@@ -74,6 +76,75 @@ def test_write_and_decode_small(name, layout):
         err, where = max_abs(got, ref)
         assert np.all(np.isfinite(got))
         assert err <= TOL[w.dtype], f"{name} part={part} err={err} at {where}"
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_empty_contexts_give_zero_rows(G):
+    """Contexts of length 0 (set on the device after the pool is written)
+    give zero rows in every mode: single pass, explicit partitions and the
+    automatic split; the other rows match the oracle."""
+    need_gpu()
+    w = workloads.make(3, S=9, H=4 * G, Hkv=4, len_median=600, len_cap=2500)
+    announce("empty contexts", "G", G)
+    dw = M.setup(w, write_step=True)
+    st = build_state(w)
+    kc, vc = build_pool(w, st, include_step=True)
+    lens = w.context_lens.astype(np.int64).copy()
+    lens[[0, 4, 8]] = 0
+    dw.context_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    ref = A.decode_ref(w.query, kc, vc, st.block_tables, np.maximum(lens, 1), w.scale, w.bs,
+                       w.dtype)
+    for part in (0, 64, 512, -1):
+        got = _decode(dw, part)
+        assert np.all(got[lens == 0] == 0.0), part
+        err, where = max_abs(got[lens > 0], ref[lens > 0])
+        announce("partition", part, "max-abs", err)
+        assert err <= TOL[w.dtype], (part, err, where)
+
+
+@pytest.mark.parametrize("S,Hkv,G,D,kv", [
+    (128, 4, 4, 64, "bf16"),   # 512 pairs: the one-pass list (<= 256 sequences)
+    (300, 2, 8, 64, "bf16"),   # 600 pairs, 300 sequences: the batched list
+    (130, 4, 4, 128, "e4m3"),  # the FP8 grouped kernel reads the same list
+])
+def test_grouped_decode_dispatch_list(S, Hkv, G, D, kv):
+    """Grouped split-K decode over at least 512 (sequence, kv head) pairs
+    runs its partitions from the largest-first dispatch list.  Lognormal
+    lengths, some contexts set to 0 and to exact multiples of the partition
+    size on the device; every row against the oracle, empty ones zero."""
+    need_gpu()
+    w = workloads.make(3, S=S, H=G * Hkv, Hkv=Hkv, D=D, bs=16, len_median=120, len_cap=700)
+    announce("dispatch list", S, Hkv, G, D, kv)
+    fp8 = kv == "e4m3"
+    kw = dict(kv_dtype="e4m3", k_scale=KS, v_scale=VS) if fp8 else {}
+    dw = M.setup(w, write_step=True, **kw)
+    st = build_state(w)
+    kc, vc = build_pool(w, st, include_step=True, **kw)
+    lens = w.context_lens.astype(np.int64).copy()
+    part = 64
+    lens[::17] = 0
+    lens[5::23] = np.minimum(lens[5::23], 2 * part) // part * part  # exact multiples (0 included)
+    dw.context_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    ref = A.decode_ref(w.query, kc, vc, st.block_tables, np.maximum(lens, 1), w.scale, w.bs, w.dtype,
+                       **kw)
+    for ps in (part, -1):
+        out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+        nbytes = P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, ps)
+        ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")  # stale bytes
+        if fp8:
+            P.pa_decode_fp8(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                            dw.context_lens, dw.max_context_len, w.scale, KS, VS, partition_size=ps,
+                            workspace=ws)
+        else:
+            P.pa_decode(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables, dw.context_lens,
+                        dw.max_context_len, w.scale, partition_size=ps, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.all(np.isfinite(got))
+        assert np.all(got[lens == 0] == 0.0)
+        err, where = max_abs(got[lens > 0], ref[lens > 0])
+        announce("partition", ps, "max-abs", err)
+        assert err <= TOL[w.dtype], (ps, err, where)
 
 
 def test_decode_bitwise_placement_invariance_and_determinism():
