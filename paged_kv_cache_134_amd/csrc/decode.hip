@@ -164,11 +164,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_items_kernel(const Deco
   };
   if (tid < kItemBuckets) sCnt[tid] = 0;
   __syncthreads();
-  // full partitions in sequence order; shorter ones counted per class
+  // full partitions in sequence order; shorter ones counted per class.  A
+  // batch of at most kDecodeThreads sequences is read once (L0 is kept for
+  // the second pass).
   int full_base = 0, rem_total = 0;
+  const int L0 = tid < S ? p.context_lens[tid] : 0;
   for (int i0 = 0; i0 < S; i0 += kDecodeThreads) {
     const int i = i0 + tid;
-    const int L = i < S ? p.context_lens[i] : 0;
+    const int L = i0 == 0 ? L0 : i < S ? p.context_lens[i] : 0;
     const int f = L / P, r = L - f * P;
     int nf;
     const int fx = scan(f, nf);
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_items_kernel(const Deco
   __syncthreads();
   for (int i0 = 0; i0 < S; i0 += kDecodeThreads) {  // shorter partitions at their class cursors
     const int i = i0 + tid;
-    const int L = i < S ? p.context_lens[i] : 0;
+    const int L = i0 == 0 ? L0 : i < S ? p.context_lens[i] : 0;
     const int f = L / P, r = L - f * P;
     if (r > 0) {
       const int pos = atomicAdd(&sCnt[bucket(r)], 1);
