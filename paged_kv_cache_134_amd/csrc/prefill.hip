@@ -14,7 +14,9 @@
 //     wave w owns 32 rows, one 32-wide MFMA column block;
 //   * key tiles of 64 keys are gathered through the block table into
 //     registers one tile ahead of use, then into LDS: K row-major (bf16/f16
-//     as stored) and V transposed to [d][key] in f16; keys past the last
+//     as stored) and V transposed to [d][key] in f16, its 4-key groups
+//     reordered within each 16-key slice so that a lane's PV operand is one
+//     16-byte read (row strides of 4 mod 32 dwords: conflict-free); keys past the last
 //     visible position are read as the last visible key (finite data) and
 //     masked, so no unwritten slot is ever read;
 //   * workgroup ids are remapped so the query tiles of one (sequence, head)
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   constexpr int KS = D / 16;                    // 16-wide k-steps over the head dim (QK)
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
   constexpr int KROW = D * 2 + 16;              // LDS bytes per K row (padded)
-  constexpr int VROW = kBN * 2 + 8;             // LDS bytes per V^T row (padded)
+  constexpr int VROW = kBN * 2 + 16;            // LDS bytes per V^T row (padded: 36 dwords)
   constexpr int KCH = D / 8;                    // 16-byte LDS chunks per K row
   constexpr int GCH = D * CB / 16;              // 16-byte cache chunks per K row
   constexpr int KPT = kBN * GCH / kPrefillThreads;        // cache chunks per thread per tile
@@ -245,6 +247,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   constexpr int KTPR = kPrefillThreads / kBN;  // threads per K row
   static_assert(KTPR * KPT == GCH, "K row split");
   const int k_row = tid / KTPR, k_cg = (tid % KTPR) * KPT;
+  // 16-bit caches: chunk i of this thread is 2 q + 8 (i / 2) + i % 2 (q = tid
+  // % 4), so the 8 lanes of one LDS write (2 rows) hit 8 different 4-bank
+  // groups; FP8 caches take KPT consecutive chunks
+  auto k_chunk = [&](int i) { return FP8 ? k_cg + i : 2 * (tid % KTPR) + 8 * (i / 2) + (i % 2); };
   const int v_item = min(tid, VITEMS - 1);
   const int v_kq = v_item % (kBN / 4), v_dq = v_item / (kBN / 4);
   const bool bs_ge4 = lbs >= 2;
@@ -256,9 +262,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     TileRegs r;
     {
       const int t = min(k0 + k_row, kend - 1);
-      const char* src = p.key_cache + row_off(s_bt[(t >> lbs) - wb0], t, k_cg * (16 / CB));
+      const char* src = p.key_cache + row_off(s_bt[(t >> lbs) - wb0], t, 0);
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) r.k[i] = load16(src + i * 16);
+      for (int i = 0; i < KPT; ++i) r.k[i] = load16(src + k_chunk(i) * 16);
     }
     {
       const int tb = min(k0 + v_kq * 4, kend - 1);
@@ -297,10 +303,16 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         store16(sK + k_row * KROW + (k_cg + i) * 32, lo);
         store16(sK + k_row * KROW + (k_cg + i) * 32 + 16, hi);
       } else {
-        store16(sK + k_row * KROW + (k_cg + i) * 16, tr.k[i]);
+        store16(sK + k_row * KROW + k_chunk(i) * 16, tr.k[i]);
       }
     }
     if (VITEMS == kPrefillThreads || tid < VITEMS) {  // head size 64: half the threads stage no V
+      // key group v_kq (keys 4 v_kq .. +3) goes to group slot (v_kq & ~3) +
+      // 2 (v_kq & 1) + ((v_kq >> 1) & 1) of the row: in every 16-key slice
+      // the groups are stored in the order 0, 2, 1, 3, so the 8 keys one
+      // half-wave contracts per product (groups hf and hf + 2) are 16
+      // contiguous bytes
+      const int v_slot = ((v_kq & ~3) + 2 * (v_kq & 1) + ((v_kq >> 1) & 1)) * 8;
       float fv[4][8];  // FP8: the 8 columns of each of the 4 keys
       if constexpr (FP8) {
 #pragma unroll
@@ -315,9 +327,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
           f0[k] = FP8 ? fv[k][e] : chunk_elem<DT>(tr.v[k], e);
           f1[k] = FP8 ? fv[k][e + 1] : chunk_elem<DT>(tr.v[k], e + 1);
         }
-        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e) * VROW + v_kq * 8) =
+        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e) * VROW + v_slot) =
             make_uint2(pk_f16(f0[0], f0[1]), pk_f16(f0[2], f0[3]));
-        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e + 1) * VROW + v_kq * 8) =
+        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e + 1) * VROW + v_slot) =
             make_uint2(pk_f16(f1[0], f1[1]), pk_f16(f1[2], f1[3]));
       }
     }
@@ -396,19 +408,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     // ---- O^T += V^T P^T over 4 slices of 16 keys.  Slice t = (kb, jp) uses
     // this lane's registers 8 jp .. 8 jp + 7 of key block kb, i.e. keys
     // 32 kb + 16 jp + 8 (e/4) + 4 hf + e%4 for e = 0..7; the V^T fragment
-    // takes its contraction slots in the same order.
+    // takes its contraction slots in the same order: keys 4 hf .. +3 and
+    // 8 + 4 hf .. +3 of the slice, one 16-byte read from the reordered row.
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kb = t / 2, jp = t % 2;
       const f16x8_t pb = __builtin_bit_cast(
           f16x8_t, make_uint4(pp[kb][4 * jp], pp[kb][4 * jp + 1], pp[kb][4 * jp + 2], pp[kb][4 * jp + 3]));
-      const int col = (kb * 32 + jp * 16 + hf * 4) * 2;
+      const int col = (kb * 32 + jp * 16) * 2 + hf * 16;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char* vrow = sV + (db * 32 + lq) * VROW + col;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const f16x8_t a = __builtin_bit_cast(f16x8_t, load16(sV + (db * 32 + lq) * VROW + col));
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb, o[db], 0, 0, 0);
       }
     }
