@@ -129,8 +129,15 @@ __device__ __forceinline__ void fp8x8_to_f32(const uint4& v, float* out) {
 // mask) and writes a (max, sum, unnormalised output) partial instead of a
 // normalised row.  FP8: the caches hold E4M3 codes (partials then carry
 // v_scale, as the decode kernels' partials do).
+// Waves per SIMD the register budget is set for: the FP8 kernel's staging
+// registers are half as many (one byte per element), so outside the prefix
+// pass it fits 3 waves without spilling; the others fit 2.
+template <bool PREFIX, bool FP8>
+constexpr int kPrefillMinWaves = (FP8 && !PREFIX) ? 3 : 2;
+
 template <pa_dtype DT, int D, bool OFF32, bool PREFIX, bool FP8>
-__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) void prefill_kernel(
+    const PrefillParams p) {
   constexpr int CB = FP8 ? 1 : 2;               // cache bytes per element
   constexpr int KS = D / 16;                    // 16-wide k-steps over the head dim (QK)
   constexpr int DB = D / 32;                    // 32-row blocks of O^T
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   const int kvh = h / (p.num_heads / p.num_kv_heads);
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: the mask and skip tests branch on scalars
   const int lq = lane % 32;     // query (column) owned by this lane
   const int hf = lane / 32;     // half: k-slice 8 hf .. +7, rows 4 hf .. +3 of each 8
 
@@ -369,17 +376,20 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     // ---- online softmax in the scaled log2 domain; the two halves of the
     // wave hold the two key sets of each query.  Only tiles that reach past
     // some row's last visible key need the mask.
-    const bool need_mask = k0 + kBN - 1 > lim_min;  // wave-uniform
+    if (k0 + kBN - 1 > lim_min) {  // wave-uniform: only such tiles pay for the mask
+      // score (kb, i) is key k0 + 4 hf + (32 kb + 8 (i/4) + i%4)
+      const int rel = lim - k0 - 4 * hf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 8 * (i / 4) + (i % 4) > rel) sc[kb][i] = -INFINITY;
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float z = sc[kb][i];
-        if (need_mask && k0 + kb * 32 + 8 * (i / 4) + 4 * hf + (i % 4) > lim) z = -INFINITY;
-        sc[kb][i] = z;
-        mt = fmaxf(mt, z);
-      }
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sc[kb][i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;  // c > 0: the max commutes with the scale
     if (__any(mt > m + kLazyRescaleP)) {
       const float mn = fmaxf(m, mt);
