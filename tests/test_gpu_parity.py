@@ -249,6 +249,9 @@ def test_f16_decode(G):
                                       suffix_hi=150)),
     ("d64-g16-bs4", "5c", dict(S=3, H=32, Hkv=2, D=64, bs=4, prefix=200, suffix_lo=1,
                                suffix_hi=140)),
+    # blocks smaller than a 4-key staging group: every key looked up on its own
+    ("gqa-bs2", "5c", dict(S=3, H=4, Hkv=2, bs=2, prefix=70, suffix_lo=5, suffix_hi=90)),
+    ("bs1", "5c", dict(S=2, H=2, Hkv=1, bs=1, prefix=33, suffix_lo=1, suffix_hi=70)),
 ])
 def test_prefill_small(name, cfg, over, layout):
     need_gpu()
