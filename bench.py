@@ -38,8 +38,8 @@ if ROOT not in sys.path:
 METRIC = "paged decode KV GB/s (fraction of HBM peak); prefill MFMA util; tokens/s"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16/fp16 MFMA, AMD published
-# source file of each timed kernel (its hash ties a committed counter profile
-# to the kernel it was taken on)
+# source file of each timed kernel (the hash of its code, comments excluded,
+# ties a committed counter profile to the kernel it was taken on)
 # (with the headers they include, so a change to shared device code also
 # retires the profile)
 KERNEL_SOURCES = {
@@ -88,11 +88,19 @@ def parse():
     return ap.parse_args()
 
 
+def code_text(src: str) -> str:
+    """The source with comments removed and whitespace collapsed: edits to
+    comments leave the hash, and so a counter profile, valid."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_sha(kind: str) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "paged_kv_cache_134_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_134_amd", "csrc", name)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -38,11 +38,15 @@
 //     multiply V are exactly the ones that are divided out; QK^T uses the
 //     stored type with fp32 accumulation;
 //   * a wave whose rows are all padding, or that sees none of a tile's keys,
-//     skips that tile's products;
+//     skips that tile's products; the wave index goes through readfirstlane
+//     so these tests, and the causal mask (applied only to tiles that reach
+//     past some row's last visible key), are scalar branches rather than
+//     per-score selects;
 //   * FP8 (E4M3) caches: K converts exactly to the query's type and V to f16
 //     on their way into LDS, so the products are those of a 16-bit cache;
 //     k_scale is folded into the softmax scale and v_scale into the final
-//     normalisation.
+//     normalisation.  Their staging registers are half as many, so outside
+//     the prefix pass they run 3 waves per SIMD (the others 2).
 #include <hip/hip_runtime.h>
 
 #include "kernel_common.h"
