@@ -187,6 +187,8 @@ def test_fp8_matches_bf16_decode_of_the_dequantised_cache():
 @pytest.mark.parametrize("name,cfg,over", [
     ("packed-literal-2heads", "5b", dict(H=2, Hkv=2)),
     ("packed-gqa", "5b", dict(H=8, Hkv=2, packed_lens=[85, 120, 45, 210, 1, 64])),
+    # empty sequences in the packed batch (equal consecutive offsets, no context)
+    ("packed-empty-seqs", "5b", dict(H=4, Hkv=2, packed_lens=[0, 70, 0, 33, 0])),
     ("prefix-suffix", "5c", dict(S=4, H=2, Hkv=2, prefix=600, suffix_lo=20, suffix_hi=200)),
     ("prefix-suffix-d64-bs16", "5c", dict(S=3, H=4, Hkv=1, D=64, bs=16, prefix=300,
                                           suffix_lo=60, suffix_hi=150)),
