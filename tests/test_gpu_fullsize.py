@@ -201,3 +201,45 @@ def test_fp8_decode_full_size_sampled(cfg, layout):
             worst = max(worst, float(np.max(np.abs(got[s, h] - ref))))
     announce("max-abs", worst)
     assert worst <= TOL[w.dtype]
+
+
+def test_fp8_prefill_full_size_sampled():
+    """The prefix-cached suffix prefill over FP8 pools at full size, as
+    `bench.py --config 5c --kv fp8` runs it (the 3-waves-per-SIMD FP8 kernel):
+    sampled pool codes bit-exact against the oracle's quantisation, sampled
+    rows against the plain definition over the codes read back."""
+    from oracle import fp8 as F
+    need_gpu()
+    w = workloads.make("5c")
+    ks, vs = workloads.FP8_K_SCALE, workloads.FP8_V_SCALE
+    announce("full-size fp8 prefill", w.name)
+    dw = M.setup(w, layout=P.HND, write_step=True, kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    st = build_state(w)
+    out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+    P.pa_prefill_fp8(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                     dw.query_start_loc, dw.context_lens, int(w.query_lens.max()),
+                     dw.max_context_len, w.scale, ks, vs, layout=P.HND)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    seqs = sorted({0, w.S // 2, w.S - 1})
+    qf = A.bits_to_f64(w.query, w.dtype)
+    worst = 0.0
+    for s in seqs:
+        K, V = w.kv(s)
+        kq, vq = F.quantize(K, w.dtype, ks), F.quantize(V, w.dtype, vs)
+        idx = torch.from_numpy(st.seq_slots[s].astype(np.int64)).cuda()
+        blk, off = idx // w.bs, idx % w.bs
+        assert np.array_equal(dw.key_cache[blk, :, off].cpu().numpy(), kq), s
+        assert np.array_equal(dw.value_cache[blk, :, off].cpu().numpy(), vq), s
+        Kf, Vf = F.dequantize(kq, ks), F.dequantize(vq, vs)
+        n, L = int(w.query_lens[s]), int(w.context_lens[s])
+        for h in sorted({0, w.H - 1}):
+            g = h // w.G
+            for j in sorted({0, 1, n // 2, n - 1}):
+                a = L - n + j
+                r = int(w.query_start_loc[s]) + j
+                ref, _ = A.attention_dense(qf[r, h], Kf[:a + 1, g], Vf[:a + 1, g], w.scale)
+                worst = max(worst, float(np.max(np.abs(got[r, h] - ref))))
+    announce("max-abs", worst)
+    assert worst <= TOL["bf16"]
