@@ -41,7 +41,10 @@ template <int D>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const DecodeParams p,
                                                                        int64_t num_pairs) {
   constexpr int CPL = D / kWave;  // columns per lane
-  const int64_t sh = (int64_t)blockIdx.x * (kReduceThreads / kWave) + threadIdx.x / kWave;
+  // readfirstlane: the row is wave-uniform, so its index arithmetic and the
+  // loads of its (max, sum) records are scalar
+  const int64_t sh = (int64_t)blockIdx.x * (kReduceThreads / kWave) +
+                     __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (sh >= num_pairs) return;
   const int lane = threadIdx.x % kWave;
   const int s = (int)(sh / p.num_heads);
