@@ -210,39 +210,11 @@ def prefill_ref(query, key_cache, value_cache, block_tables, query_start_loc, co
 
 
 # ------------------------------------------------ block-wise form (cross-check)
-def online_softmax_blocks(q, K, V, scale, block):
-    """Block-by-block online softmax ([k4i] #paged-attention-kernel).
-
-    Running max m, normaliser l and unnormalised output o start at
-    (-inf, 0, 0).  For each block j of ``block`` consecutive keys: a_j =
-    scale * K_j q, m_j = max a_j, l_j = sum exp(a_j - m_j), o_j = exp(a_j -
-    m_j) V_j; then with m' = max(m, m_j): l <- e^(m-m') l + e^(m_j-m') l_j,
-    o <- e^(m-m') o + e^(m_j-m') o_j, m <- m'.  The result is o / l.
-    Written out in float64 only to pin the identity with ``attention_dense``.
-    """
-    q = np.asarray(q, dtype=np.float64)
-    K = np.asarray(K, dtype=np.float64)
-    V = np.asarray(V, dtype=np.float64)
-    m, l, o = -np.inf, 0.0, np.zeros(V.shape[-1])
-    for b0 in range(0, K.shape[0], block):
-        a = scale * (K[b0:b0 + block] @ q)
-        m_j = a.max()
-        e = np.exp(a - m_j)
-        l_j = e.sum()
-        o_j = e @ V[b0:b0 + block]
-        m_new = max(m, m_j)
-        c_old = np.exp(m - m_new) if m != -np.inf else 0.0
-        c_new = np.exp(m_j - m_new)
-        l = c_old * l + c_new * l_j
-        o = c_old * o + c_new * o_j
-        m = m_new
-    return o / l if l > 0 else o
-
-
 def partition_stats(q, K, V, scale):
-    """Per-partition statistics (m_p, l_p, o_p) of split-K decode ([vllm] §7.3,
-    V2): m_p = max of the partition's scores, l_p = sum exp(score - m_p),
-    o_p = sum exp(score - m_p) v (unnormalised)."""
+    """Statistics (m_p, l_p, o_p) of one key range ([vllm] §7.3, V2):
+    m_p = the range's largest score, l_p = sum exp(score - m_p), o_p = sum
+    exp(score - m_p) v (unnormalised).  The softmax over the range alone is
+    o_p / l_p."""
     q = np.asarray(q, dtype=np.float64)
     a = scale * (np.asarray(K, dtype=np.float64) @ q)
     m = a.max()
@@ -250,11 +222,37 @@ def partition_stats(q, K, V, scale):
     return m, e.sum(), e @ np.asarray(V, dtype=np.float64)
 
 
+def combine_stats(x, y):
+    """Statistics of the union of two disjoint key ranges from theirs: both
+    are re-expressed relative to the larger maximum M, after which the
+    normalisers and the unnormalised outputs simply add."""
+    (mx, lx, ox), (my, ly, oy) = x, y
+    M = max(mx, my)
+    cx, cy = np.exp(mx - M), np.exp(my - M)
+    return M, cx * lx + cy * ly, cx * ox + cy * oy
+
+
 def merge_partitions(stats):
-    """Reduce step of split-K ([vllm] §7.3: rescale each partition by its max
-    and merge with the online-softmax correction): M = max_p m_p, out =
-    sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p."""
+    """Reduce step of split-K ([vllm] §7.3): all partitions' statistics
+    combined at once, M = max_p m_p, out = sum_p e^(m_p - M) o_p /
+    sum_p e^(m_p - M) l_p."""
     M = max(m for m, _, _ in stats)
     num = sum(np.exp(m - M) * o for m, _, o in stats)
     den = sum(np.exp(m - M) * l for m, l, _ in stats)
     return num / den
+
+
+def online_softmax_blocks(q, K, V, scale, block):
+    """Attention over K, V taken ``block`` keys at a time ([k4i]
+    #paged-attention-kernel: a sequence's blocks may be visited one by one):
+    the running statistics are the left fold of ``combine_stats`` over the
+    blocks' ``partition_stats``, and the output is o / l of the fold.  Pinned
+    against ``attention_dense`` in float64."""
+    stats = [partition_stats(q, K[b0:b0 + block], V[b0:b0 + block], scale)
+             for b0 in range(0, np.asarray(K).shape[0], block)]
+    if not stats:
+        return np.zeros(np.asarray(V).shape[-1])
+    m, l, o = stats[0]
+    for st in stats[1:]:
+        m, l, o = combine_stats((m, l, o), st)
+    return o / l

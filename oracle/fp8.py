@@ -17,7 +17,8 @@ leave open is read as follows:
 * the stored code of an element x is x / scale, divided in fp32 (IEEE,
   correctly rounded), rounded to the nearest E4M3 value with ties to the
   even code (the one whose mantissa ends in 0), and saturated to +-448
-  (infinities too); NaN stays NaN;
+  (infinities too); NaN stays NaN, as the code 0x7F with the element's
+  sign bit (0xFF for a negative NaN);
 * a stored code reads back as its E4M3 value times the scale (exact in
   float64).
 """
@@ -78,11 +79,15 @@ def f32_of(raw, dtype: str) -> np.ndarray:
 
 def quantize(raw, dtype: str, scale: float) -> np.ndarray:
     """E4M3 codes of stored elements: round(x / scale) with the division in
-    fp32 (the write kernel's precision)."""
+    fp32 (the write kernel's precision).  A NaN element is stored as the NaN
+    code 0x7F carrying the element's own sign bit (the sign of a quotient
+    of NaN is not fixed by IEEE arithmetic, so it is taken from x)."""
     x = f32_of(raw, dtype)
     with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
         y = (x / np.float32(scale)).astype(np.float32)
-    return e4m3_from_f32(y)
+    codes = e4m3_from_f32(y)
+    nan_code = np.where(np.signbit(x), np.uint8(0xFF), np.uint8(0x7F)).astype(np.uint8)
+    return np.where(np.isnan(x), nan_code, codes).astype(np.uint8)
 
 
 def dequantize(codes, scale: float) -> np.ndarray:

@@ -236,6 +236,41 @@ def test_bf16_upcast_exact():
     assert list(A.bits_to_f64(bits, "bf16")) == expect
 
 
+def _binary16_value(c: int) -> float:
+    """IEEE 754 binary16 from its fields: sign bit 15, exponent bits 14..10
+    (bias 15), fraction bits 9..0; exponent 0 holds the subnormals
+    frac * 2^-24, exponent 31 the infinities (fraction 0) and NaNs."""
+    sign = -1.0 if c >> 15 else 1.0
+    e, f = (c >> 10) & 0x1F, c & 0x3FF
+    if e == 0x1F:
+        return sign * np.inf if f == 0 else np.nan
+    if e == 0:
+        return sign * f * 2.0 ** -24
+    return sign * (1.0 + f / 1024.0) * 2.0 ** (e - 15)
+
+
+def test_f16_upcast_exact():
+    """The f16 branches of both oracle upcasts (attention and the FP8 write's
+    source read) against IEEE binary16: printed values of the format, then
+    every one of the 65,536 codes against the field definition.  Reading the
+    bits as bfloat16 instead (0x3C00 would be 2^-7) fails here."""
+    from oracle import fp8 as F
+    bits = np.array([0x3C00, 0xC000, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0x3555, 0x7C00, 0xFC00,
+                     0x8000], np.uint16)
+    expect = [1.0, -2.0, 2.0 ** -24, 1023 * 2.0 ** -24, 2.0 ** -14, 65504.0, 0.333251953125,
+              np.inf, -np.inf, -0.0]
+    for got in (A.bits_to_f64(bits, "f16"), F.f32_of(bits, "f16").astype(np.float64)):
+        assert list(got) == expect
+        assert np.signbit(got[-1])
+    every = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = np.array([_binary16_value(int(c)) for c in every])
+    for got in (A.bits_to_f64(every, "f16"), F.f32_of(every, "f16").astype(np.float64)):
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
 # ------------------------------------------------------------- prefill pins
 def _brute_causal(Q, K, V, scale):
     """Masked dense causal attention in matrix form; query row j of n sits at

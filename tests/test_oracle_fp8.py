@@ -65,6 +65,19 @@ def test_saturation_nan_and_zero():
     assert c[0] & 0x7F == 0x7F and list(c[1:]) == [0x80, 0x00, 0x80, 0x00]
 
 
+def test_nan_elements_keep_their_sign():
+    """A NaN element is stored as S.1111.111 with its own sign bit, from every
+    source type: 0x7F for a positive NaN, 0xFF for a negative one."""
+    f32 = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001], np.uint32)
+    assert list(fp8.quantize(f32, "f32", 0.37)) == [0x7F, 0xFF, 0x7F, 0xFF]
+    bf16 = np.array([0x7FC0, 0xFFC0, 0x7F81, 0xFF81], np.uint16)
+    assert list(fp8.quantize(bf16, "bf16", 1.0)) == [0x7F, 0xFF, 0x7F, 0xFF]
+    f16 = np.array([0x7E00, 0xFE00, 0x7C01, 0xFC01], np.uint16)
+    assert list(fp8.quantize(f16, "f16", 2.5)) == [0x7F, 0xFF, 0x7F, 0xFF]
+    # infinities are not NaN: they saturate to +-448 (0x7E / 0xFE)
+    assert list(fp8.quantize(np.array([0x7C00, 0xFC00], np.uint16), "f16", 1.0)) == [0x7E, 0xFE]
+
+
 def test_round_trip_and_error_bound():
     finite = np.flatnonzero(np.isfinite(fp8.E4M3)).astype(np.uint8)
     assert np.array_equal(fp8.e4m3_from_f32(fp8.E4M3[finite].astype(np.float32)), finite)
