@@ -404,19 +404,51 @@ pa_status pa_prefill_fp8(void* out, pa_dtype out_dtype, const void* query, pa_dt
                          int32_t num_blocks, float scale, void* stream);
 
 /*
- * pa_check_metadata -- synchronous host-side check of device metadata (tests
- * and debugging; copies the arrays to the host after synchronising `stream`).
- * Checks: 0 <= context_lens[s] <= max_blocks_per_seq * block_size; every
- * block-table entry a sequence reads (t < context_lens[s]) lies in
- * [0, num_blocks); non-negative slots are distinct and < num_blocks *
- * block_size.  Any pointer may be NULL to skip its checks.  Returns PA_OK or
- * PA_ERR_METADATA (details in pa_last_error()).
+ * pa_check_metadata -- synchronous host-side check of the device metadata
+ * the kernels trust ([vllm] §3.1 block table, §3.2 slot mapping, §5.4
+ * CommonAttentionMetadata; §6.4 for the cascade's shared blocks).  For
+ * tests and debugging: it synchronises `stream`, copies the arrays to the
+ * host and reads nothing else.  Checks, each skipped when its pointer is
+ * NULL:
+ *   context_lens (device, int32 [num_seqs])
+ *       0 <= context_lens[s] <= max_context_len (the bound the split-K grid,
+ *       workspace and reduce are sized by), and, with block_tables,
+ *       context_lens[s] <= max_blocks_per_seq * block_size;
+ *   block_tables (device, int32 [num_seqs, max_blocks_per_seq])
+ *       every entry a sequence reads (entries below ceil(context_lens[s] /
+ *       block_size); every entry when context_lens is NULL) lies in
+ *       [0, num_blocks);
+ *   slot_mapping (device, int64 [num_tokens])
+ *       non-negative slots are < num_blocks * block_size and distinct
+ *       (negative slots are padding and always pass);
+ *   common_prefix_len > 0 (the cascade's precondition; needs both
+ *       block_tables and context_lens)
+ *       a multiple of block_size, at most every context_lens[s], and
+ *       block_tables[s][0 .. common_prefix_len / block_size - 1] equal to
+ *       row 0's for every s.  0 skips this check.
+ * Sizes must be non-negative, block_size and num_blocks positive
+ * (PA_ERR_INVALID_ARGUMENT).  Returns PA_OK, or PA_ERR_METADATA with the
+ * first violation (array, index, value) in pa_last_error().
  */
 pa_status pa_check_metadata(const int32_t* block_tables,
                             const int32_t* context_lens,
                             const int64_t* slot_mapping, int32_t num_seqs,
-                            int32_t max_blocks_per_seq, int32_t num_tokens,
-                            int32_t block_size, int32_t num_blocks, void* stream);
+                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                            int32_t num_tokens, int32_t block_size, int32_t num_blocks,
+                            int32_t common_prefix_len, void* stream);
+
+/*
+ * Measurement aid (not a step of the method): the practical HBM read
+ * ceiling.  pa_stream_read_probe reads `bytes` (a positive multiple of 16)
+ * of device memory at `buf` (16-byte aligned) exactly once, with the
+ * 16-byte non-temporal loads the decode kernels use for K/V rows, and
+ * writes one 32-bit XOR digest per workgroup to `sink` (device, uint32
+ * [pa_stream_read_probe_sink_words()]) so that no load can be dropped.  One
+ * launch on `stream`; timing it gives the read bandwidth that decode's
+ * algorithmic bandwidth is compared with besides the published peak.
+ */
+int32_t pa_stream_read_probe_sink_words(void);
+pa_status pa_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /*
  * Block pool -- host-side block manager that hands out physical blocks and

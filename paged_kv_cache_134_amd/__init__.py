@@ -49,6 +49,7 @@ EXPORTED = [
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
     "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
     "pa_pool_num_free", "pa_pool_refcount", "pa_pool_add_seq_cached", "pa_pool_num_cached",
+    "pa_stream_read_probe_sink_words", "pa_stream_read_probe",
 ]
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -86,7 +87,7 @@ _sig = {
                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "pa_prefill_fp8": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _f32, _f32, _i32, _vp, _i32, _vp, _vp,
                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
-    "pa_check_metadata": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_check_metadata": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _pi32, ctypes.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_pool_add_seq": (_i32, [_vp, _pi32]),
@@ -99,6 +100,8 @@ _sig = {
     "pa_pool_seq_len": (_i32, [_vp, _i32]),
     "pa_pool_num_free": (_i32, [_vp]),
     "pa_pool_refcount": (_i32, [_vp, _i32]),
+    "pa_stream_read_probe_sink_words": (_i32, []),
+    "pa_stream_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -457,16 +460,47 @@ def pa_prefill_fp8(out, query, key_cache, value_cache, block_tables, query_start
 
 
 def pa_check_metadata(block_tables, context_lens, slot_mapping, num_blocks: int, block_size: int,
-                      stream=None) -> None:
-    """Synchronous host check of device metadata; raises PagedAttnError(PA_ERR_METADATA)."""
-    S = context_lens.shape[0] if context_lens is not None else (
-        block_tables.shape[0] if block_tables is not None else 0)
+                      max_context_len: Optional[int] = None, common_prefix_len: int = 0,
+                      num_seqs: Optional[int] = None, stream=None) -> None:
+    """Synchronous host check of device metadata; raises PagedAttnError(PA_ERR_METADATA).
+
+    Any of the three arrays may be None (its checks are skipped).
+    max_context_len defaults to the table's capacity (max_blocks x
+    block_size), or to 2^31 - 1 without a table.  num_seqs defaults to the
+    rows of context_lens or block_tables."""
+    if num_seqs is None:
+        num_seqs = context_lens.shape[0] if context_lens is not None else (
+            block_tables.shape[0] if block_tables is not None else 0)
     mb = block_tables.shape[1] if block_tables is not None else 0
+    if max_context_len is None:
+        max_context_len = mb * block_size if block_tables is not None else 0x7FFFFFFF
     T = slot_mapping.shape[0] if slot_mapping is not None else 0
+    for t, name, dt in ((block_tables, "block_tables", "int32"), (context_lens, "context_lens", "int32"),
+                        (slot_mapping, "slot_mapping", "int64")):
+        if t is not None:
+            _dev(t, name, getattr(_torch(), dt))
     p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     _check("pa_check_metadata", _lib.pa_check_metadata(
-        p(block_tables), p(context_lens), p(slot_mapping), S, mb, T, block_size, num_blocks,
-        _stream(stream)))
+        p(block_tables), p(context_lens), p(slot_mapping), num_seqs, mb, max_context_len, T,
+        block_size, num_blocks, common_prefix_len, _stream(stream)))
+
+
+def pa_stream_read_probe_sink_words() -> int:
+    return int(_lib.pa_stream_read_probe_sink_words())
+
+
+def pa_stream_read_probe(buf, sink, stream=None) -> None:
+    """Measurement aid: read every byte of the device tensor `buf` once
+    (16-byte non-temporal loads); `sink` is a device int32/uint32 tensor of
+    pa_stream_read_probe_sink_words() elements that receives digests."""
+    torch = _torch()
+    _dev(buf, "buf")
+    _dev(sink, "sink", torch.int32)
+    if sink.numel() < pa_stream_read_probe_sink_words():
+        raise ValueError("sink too small")
+    nbytes = buf.numel() * buf.element_size()
+    _check("pa_stream_read_probe", _lib.pa_stream_read_probe(buf.data_ptr(), nbytes,
+                                                             sink.data_ptr(), _stream(stream)))
 
 
 # ------------------------------------------------------------------ block pool

@@ -23,8 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["pa_api.hip", "cache_ops.hip", "decode.hip", "decode_head.hip", "decode_group.hip",
-               "decode_group_fp8.hip", "prefill.hip"]
+HIP_SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))  # every HIP source
 CXX_SOURCES = ["pool.cpp"]
 
 

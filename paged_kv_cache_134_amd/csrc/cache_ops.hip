@@ -51,7 +51,8 @@ __global__ __launch_bounds__(kWriteThreads) void reshape_and_cache_kernel(
 
 // Quantising write into FP8 (E4M3) pools: one thread per 16-code chunk of a
 // row.  Code = nearest E4M3 of x / scale (fp32 quotient, clamped to +-448
-// first because the conversion instruction does not saturate).
+// first because the conversion instruction does not saturate); a NaN
+// element is stored as 0x7F with the element's sign bit.
 template <pa_dtype ST>
 __device__ __forceinline__ uint4 quantize16(const char* src, float scale) {
   float x[16];
@@ -68,11 +69,27 @@ __device__ __forceinline__ uint4 quantize16(const char* src, float scale) {
     chunk_to_f32<ST>(load16(src), x);
     chunk_to_f32<ST>(load16(src + 16), x + 8);
   }
+  uint32_t nan_mask = 0, neg_mask = 0;  // per element: NaN source, sign bit of the source
 #pragma unroll
-  for (int e = 0; e < 16; ++e) x[e] = e4m3_saturate(x[e] / scale);
-  return make_uint4(f32x4_to_fp8x4(x[0], x[1], x[2], x[3]), f32x4_to_fp8x4(x[4], x[5], x[6], x[7]),
-                    f32x4_to_fp8x4(x[8], x[9], x[10], x[11]),
-                    f32x4_to_fp8x4(x[12], x[13], x[14], x[15]));
+  for (int e = 0; e < 16; ++e) {
+    nan_mask |= (uint32_t)(x[e] != x[e]) << e;
+    neg_mask |= (__float_as_uint(x[e]) >> 31) << e;
+    x[e] = e4m3_saturate(x[e] / scale);
+  }
+  uint32_t w[4] = {f32x4_to_fp8x4(x[0], x[1], x[2], x[3]), f32x4_to_fp8x4(x[4], x[5], x[6], x[7]),
+                   f32x4_to_fp8x4(x[8], x[9], x[10], x[11]),
+                   f32x4_to_fp8x4(x[12], x[13], x[14], x[15])};
+  if (nan_mask) {  // rare: a NaN element is stored as 0x7F with its sign bit
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if ((nan_mask >> e) & 1u) {
+        const uint32_t code = 0x7Fu | (((neg_mask >> e) & 1u) << 7);
+        const int sh = 8 * (e % 4);
+        w[e / 4] = (w[e / 4] & ~(0xFFu << sh)) | (code << sh);
+      }
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 template <int LAYOUT, pa_dtype ST>

@@ -124,6 +124,81 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   for (int c = 0; c < CPL; ++c) store_out(p.out, sh * D + lane * CPL + c, o[c] * inv, p.out_dtype);
 }
 
+// Split-K reduce for many partitions per (sequence, head): one workgroup per
+// (sequence, head).  The maximum comes first (every thread reads a share of
+// the partials' maxima), then wave w merges partitions w, w + 4, w + 8, ...
+// with kWideBatch partials' loads in flight at a time, and the waves' sums
+// meet in LDS.  Same arithmetic as above (each partial weighted by
+// 2^(m_p - M)); only the order of the sum differs, fixed by the launch.
+constexpr int kWideBatch = 16;
+
+template <int D>
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_wide_kernel(const DecodeParams p) {
+  constexpr int CPL = D / kWave;  // columns per lane
+  constexpr int NW = kReduceThreads / kWave;
+  __shared__ float sMax[NW], sSum[NW];
+  __shared__ float sO[NW][D];
+  const int64_t sh = blockIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int s = (int)(sh / p.num_heads);
+  const int L = p.context_lens[s];
+  if (L == 0 && !p.all_partial) {  // empty context: the row is zero
+    for (int d = threadIdx.x; d < D; d += kReduceThreads) store_out(p.out, sh * D + d, 0.f, p.out_dtype);
+    return;
+  }
+  if (single_partition(p, L)) return;
+  const int np = p.part_base + (L > p.key_begin ? (L - p.key_begin + p.partition_size - 1) / p.partition_size : 0);
+  const float* ml = p.part_ml + sh * p.max_partitions * 2;
+  const float* po = p.part_out + sh * p.max_partitions * D + lane * CPL;
+
+  float M = -INFINITY;
+  for (int i = threadIdx.x; i < np; i += kReduceThreads) M = fmaxf(M, ml[2 * i]);
+  M = wave_max(M);
+  if (lane == 0) sMax[wave] = M;
+  __syncthreads();
+  M = sMax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, sMax[w]);
+
+  float o[CPL], lsum = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) o[c] = 0.f;
+  for (int i0 = wave; i0 < np; i0 += NW * kWideBatch) {  // uniform
+    float mv[kWideBatch], lv[kWideBatch], ov[kWideBatch][CPL];
+#pragma unroll
+    for (int k = 0; k < kWideBatch; ++k) {
+      const int i = min(i0 + NW * k, np - 1);  // repeats past the end are not used
+      mv[k] = ml[2 * i];
+      lv[k] = ml[2 * i + 1];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ov[k][c] = po[(int64_t)i * D + c];
+    }
+#pragma unroll
+    for (int k = 0; k < kWideBatch; ++k) {
+      if (i0 + NW * k < np) {
+        const float a = exp2_diff(mv[k], M);
+        lsum += a * lv[k];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[c] += a * ov[k][c];
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) sO[wave][lane * CPL + c] = o[c];
+  if (lane == 0) sSum[wave] = lsum;
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += kReduceThreads) {
+    float ot = 0.f, lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      ot += sO[w][d];
+      lt += sSum[w];
+    }
+    store_out(p.out, sh * D + d, lt > 0.f ? ot / lt : 0.f, p.out_dtype);
+  }
+}
+
 // ------------------------------------------------------------ dispatch list
 // Split-K dispatch list, one workgroup.  Hardware dispatch starts workgroups
 // in id order, so the list orders the partitions largest first: every full
@@ -233,6 +308,7 @@ DecodeParams make_params(const DecodeArgs& a) {
   p.num_kv_heads = g.num_kv_heads;
   p.log2_bs = g.block_size > 0 ? __builtin_ctz((unsigned)g.block_size) : 0;
   p.partition_size = a.partition_size;
+  p.run = 1;
   p.max_partitions = a.max_partitions;
   p.key_begin = a.key_begin;
   p.part_base = a.part_base;
@@ -283,6 +359,25 @@ hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
   } else {
     p.items = nullptr;
     p.item_count = nullptr;
+    // Grouped kernels over the grid: a workgroup walks a run of partitions
+    // (whole 64-token chunks each) so that the grid has about as many
+    // workgroups as the library's own partition choice would give; the
+    // partials stay per partition.  On the long-context batch at 512-token
+    // partitions, one workgroup per partition pays its start-up (lengths,
+    // table window, first loads) 8 times as often.
+    // (16-bit grouped kernel: its partition merge defers the partials' stores
+    // behind the chunk in flight; the FP8 kernel, two tiles in flight per
+    // wave, measured slower with runs than with a workgroup per partition)
+    if (group && a.kv_dtype != PA_FP8_E4M3 && a.partition_size > 0 &&
+        a.partition_size % 64 == 0) {
+      const int32_t span = a.max_context_len - a.key_begin;
+      const int32_t want = pa_decode_auto_partition(a.num_seqs, a.num_heads, g.num_kv_heads,
+                                                    a.kv_dtype, span, 0);
+      if (want > a.partition_size) {
+        p.run = want / a.partition_size;
+        grid.y = (grid.y + p.run - 1) / p.run;
+      }
+    }
   }
   if (a.kv_dtype == PA_FP8_E4M3)
     return group ? dec::launch_group_fp8(p, a.q_dtype, g.head_size, G, grid, stream)
@@ -295,6 +390,18 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0 || a.partition_size <= 0) return hipSuccess;
   const dec::DecodeParams p = dec::make_params(a);
   const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
+  if (a.max_partitions > 8) {  // many partials per row: a workgroup per (sequence, head)
+    if (pairs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (a.geom.head_size == 64)
+      hipLaunchKernelGGL(dec::decode_reduce_wide_kernel<64>, dim3((unsigned)pairs),
+                         dim3(dec::kReduceThreads), 0, stream, p);
+    else if (a.geom.head_size == 128)
+      hipLaunchKernelGGL(dec::decode_reduce_wide_kernel<128>, dim3((unsigned)pairs),
+                         dim3(dec::kReduceThreads), 0, stream, p);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   constexpr int per_block = dec::kReduceThreads / kWave;
   dim3 rgrid((unsigned)((pairs + per_block - 1) / per_block));
   if (a.geom.head_size == 64)

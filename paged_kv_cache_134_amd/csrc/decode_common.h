@@ -38,6 +38,7 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t log2_bs;
   int32_t partition_size;  // 0 = single pass
+  int32_t run;             // split-K: consecutive partitions per workgroup (16-bit grouped kernel; else 1)
   int32_t max_partitions;  // workspace partitions per (sequence, head)
   int32_t key_begin;       // partitions cover keys [key_begin, L) (0 outside cascades)
   int32_t part_base;       // workspace index of partition 0 (earlier slots hold prefix partials)
@@ -56,7 +57,8 @@ struct DecodeParams {
 // The (sequence, kv head, partition) of this workgroup: from the dispatch
 // list when there is one, else from the (pairs, partitions) grid, partitions
 // taken last-first when last_first (only long contexts have high
-// partitions, so their workgroups start early).  False: nothing to do.
+// partitions, so their workgroups start early).  With runs (p.run > 1) the
+// grid's second index counts runs of p.run partitions.  False: nothing to do.
 __device__ __forceinline__ bool decode_item(const DecodeParams& p, bool last_first, int& s, int& kvh,
                                             int& part) {
   if (p.items) {
@@ -109,6 +111,14 @@ __device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int pa
   } else {
     store_out(p.out, head * D + d, lsum > 0.f ? o / lsum : 0.f, p.out_dtype);
   }
+}
+
+// Single pass over an empty context: the group's output rows are zero.
+// Nothing is loaded, so no entry of the (possibly unwritten) block-table row
+// is read.
+__device__ __forceinline__ void emit_zero_rows(const DecodeParams& p, int64_t head0, int G, int D) {
+  for (int i = threadIdx.x; i < G * D; i += kDecodeThreads)
+    store_out(p.out, head0 * D + i, 0.f, p.out_dtype);
 }
 
 // Kernel launches of one decode pass; grid = (num_seqs * num_kv_heads,

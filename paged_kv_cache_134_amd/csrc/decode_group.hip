@@ -22,20 +22,18 @@ namespace dec {
 namespace {
 
 constexpr int kChunk = 64;   // tokens per LDS chunk (one per lane in QK)
-constexpr int kBtWin = 256;  // block-table entries staged in LDS at a time
+constexpr int kBtWin = 128;  // block-table entries staged in LDS at a time
 
-// 4 waves per SIMD (<= 128 VGPRs): with ~34 KB of LDS per workgroup that is
+// 4 waves per SIMD (<= 128 VGPRs): with ~35 KB of LDS per workgroup that is
 // 4 workgroups, i.e. 128 KB of prefetched K/V in flight, per CU.  (G = 16 at
 // head size 128 needs more accumulators and settles for 2.)  OFF32: both
 // caches span less than 4 GiB, so row addresses are 32-bit byte offsets from
 // the cache base.
 //
-// PV runs on v_dot2 with f16 operands: the probabilities are rounded to f16
-// once (the normaliser sums the rounded values), and bf16 V converts to f16
-// exactly while |v| < 65536 (the significand fits; a subnormal f16 loses
-// less than 2^-24).  If a chunk of a bf16 cache holds a larger, infinite or
-// NaN value, the workgroup starts its range again with fp32 products; the
-// two passes are separate loops, so neither carries the other's state.
+// Precision: QK products are exact (bf16/f16 pairs on v_dot2, fp32 sums);
+// the weights 2^(z - m) stay fp32, the normaliser sums those same fp32
+// values, and PV multiplies them with V converted exactly to fp32 (any
+// magnitude, infinities and NaN included).
 template <int G, int D>
 constexpr int kLdsMinWaves = (G >= 16 && D >= 128) ? 2 : 4;
 
@@ -52,30 +50,44 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
   constexpr int DPL = D / 32;                      // output columns per lane in PV
   constexpr int NPI = kChunk / kDecodeWaves / 4;   // PV token-pair iterations per wave
   static_assert(PPT * kDecodeThreads == PIECES, "chunk must split evenly");
+  static_assert(kDecodeWaves * G * D * 4 <= (kChunk * (RC + 1) + PIECES) * 16, "merge fits the tiles");
   constexpr int KSTR = RC + 1;                     // K row stride in pieces (padded)
-  __shared__ uint4 sKV[kChunk * KSTR + PIECES];    // K (padded rows) then V; reused at the end
-  __shared__ __align__(16) _Float16 sPh[kChunk / 2][G][2];  // probabilities, token pairs interleaved
+  __shared__ uint4 sKV[kChunk * KSTR + PIECES];    // K (padded rows) then V; reused by the merges
+  __shared__ __align__(16) float sP[kChunk / 2][G][2];  // probabilities, token pairs interleaved
   __shared__ float sAlpha[G];                      // per-head rescale of this chunk
   __shared__ int32_t sResc[kDecodeWaves];          // wave w moved a running max this chunk
-  __shared__ int32_t sVwide[2];                    // chunk parity: a V value is beyond f16 range
   __shared__ float sM[G], sL[G];
   __shared__ int32_t s_bt[kBtWin];                 // block-table window
+  // merged values of a finished partition awaiting their store (slot k *
+  // 256 + tid holds thread tid's k-th value; only that thread reads it)
+  constexpr int NPT = (G * D + kDecodeThreads - 1) / kDecodeThreads;
+  __shared__ float sPend[NPT * kDecodeThreads];
   uint4* sK = sKV;
   uint4* sV = sKV + kChunk * KSTR;
 
-  int s, kvh, part;
-  if (!decode_item(p, true, s, kvh, part)) return;
+  int s, kvh, item;
+  if (!decode_item(p, true, s, kvh, item)) return;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
+  // Tokens [t0, t1): partitions part0 .. part0 + run - 1 (split-K) or the
+  // whole context (single pass).
   const int L = p.context_lens[s];
-  int t0 = 0, t1 = L;
-  if (p.partition_size > 0) {
-    t0 = p.key_begin + part * p.partition_size;
+  const int P = p.partition_size;
+  int t0 = 0, t1 = L, part0 = 0;
+  if (P > 0) {
+    part0 = item * p.run;
+    t0 = p.key_begin + part0 * P;
     if (t0 >= L) return;
-    t1 = min(L, t0 + p.partition_size);
+    t1 = min(L, t0 + p.run * P);
   }
+  const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
+  if (t1 <= t0) {  // single pass over an empty context (split-K returned above)
+    emit_zero_rows(p, head0, G, D);
+    return;
+  }
+  const bool single = single_partition(p, L);
 
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
   const int lbs = p.log2_bs;
@@ -83,8 +95,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
   const int e_last = (t1 - 1) >> lbs;  // last block-table entry this workgroup reads
 
   // query vectors of this wave's heads as scalar operands (bf16/f16 pairs)
-  const const_u32_ptr qc = (const_u32_ptr)((const char*)p.query +
-      (((int64_t)s * p.num_heads + (int64_t)kvh * G + wave * HPW) * D) * 2);
+  const const_u32_ptr qc = (const_u32_ptr)((const char*)p.query + ((head0 + wave * HPW) * D) * 2);
 
   // Consecutive lanes load consecutive 16-byte chunks of a row, so every
   // load instruction covers whole cache lines (the loads are non-temporal and
@@ -105,221 +116,90 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
   // pairs of token pair wave * 8 + half
   const char* pv_base = reinterpret_cast<const char*>(sV) +
                         (2 * (wave * (kChunk / kDecodeWaves / 2) + half) * RC) * 16 + dl * DPL * 2;
-  const char* pp_base = reinterpret_cast<const char*>(&sPh[wave * (kChunk / kDecodeWaves / 2) + half][0][0]);
+  const char* pp_base = reinterpret_cast<const char*>(&sP[wave * (kChunk / kDecodeWaves / 2) + half][0][0]);
 
-  // One pass over [t0, t1).  F16: PV on f16 v_dot2; returns false, having
-  // written nothing, as soon as a chunk holds a V value beyond f16 range.
-  auto run = [&](auto f16_tag) -> bool {
-    constexpr bool F16 = decltype(f16_tag)::value;
-    int wb0 = t0 >> lbs;  // the window holds entries wb0 .. wb0 + kBtWin - 1 (clamped to e_last)
-    auto stage_bt = [&]() {
-      for (int i = tid; i < kBtWin; i += kDecodeThreads) s_bt[i] = bt[min(wb0 + i, e_last)];
-    };
-    auto fetch = [&](int c0, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
-      int32_t blk[PPT];
-      int tc[PPT];
+  // A run's partitions are walked starting from a different one in every
+  // workgroup (rotation by the workgroup's grid position) and wrapping
+  // around: workgroups with equal work would otherwise reach their partition
+  // boundaries, where the waves merge and no new loads are issued, all at
+  // the same moment, leaving HBM idle chip-wide each time.
+  const int nparts = P > 0 && p.run > 1 ? (t1 - t0 + P - 1) / P : 1;
+  const int rot = nparts > 1 ? (int)((blockIdx.x + blockIdx.y) % (unsigned)nparts) : 0;
+  const int c_first = t0 + rot * P;  // first chunk walked
+  int wb0 = c_first >> lbs;  // the window holds entries wb0 .. wb0 + kBtWin - 1 (clamped to e_last)
+  auto stage_bt = [&]() {
+    for (int i = tid; i < kBtWin; i += kDecodeThreads) s_bt[i] = bt[min(wb0 + i, e_last)];
+  };
+  auto fetch = [&](int c0, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
+    int32_t blk[PPT];
+    int tc[PPT];
 #pragma unroll
-      for (int r = 0; r < PPT; ++r) {
-        tc[r] = min(c0 + prow + RSTEP * r, t1 - 1);
-        blk[r] = s_bt[(tc[r] >> lbs) - wb0];
-      }
+    for (int r = 0; r < PPT; ++r) {
+      tc[r] = min(c0 + prow + RSTEP * r, t1 - 1);
+      blk[r] = s_bt[(tc[r] >> lbs) - wb0];
+    }
 #pragma unroll
-      for (int r = 0; r < PPT; ++r) {
-        if constexpr (OFF32) {
-          const uint32_t off = (uint32_t)blk[r] * blk_b + (uint32_t)(tc[r] & bs_mask) * tok_b + lane_b;
-          kr[r] = load_nt(p.key_cache + off);
-          vr[r] = load_nt(p.value_cache + off);
-        } else {
-          const int64_t off = (int64_t)blk[r] * p.blk_stride +
-                              (int64_t)(tc[r] & bs_mask) * p.tok_stride + lane_off;
-          kr[r] = load_nt(p.key_cache + off * 2);
-          vr[r] = load_nt(p.value_cache + off * 2);
-        }
+    for (int r = 0; r < PPT; ++r) {
+      if constexpr (OFF32) {
+        const uint32_t off = (uint32_t)blk[r] * blk_b + (uint32_t)(tc[r] & bs_mask) * tok_b + lane_b;
+        kr[r] = load_nt(p.key_cache + off);
+        vr[r] = load_nt(p.value_cache + off);
+      } else {
+        const int64_t off = (int64_t)blk[r] * p.blk_stride +
+                            (int64_t)(tc[r] & bs_mask) * p.tok_stride + lane_off;
+        kr[r] = load_nt(p.key_cache + off * 2);
+        vr[r] = load_nt(p.value_cache + off * 2);
       }
-    };
+    }
+  };
 
-    float m_ref[HPW], l_lane[HPW];
+  // Softmax state of the current partition: reference max and lane sums of
+  // this wave's QK heads, and the lane's PV accumulators (its tokens, all
+  // heads, its columns).
+  float m_ref[HPW], l_lane[HPW];
+  float acc[G][DPL];
+  auto reset = [&]() {
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       m_ref[hh] = -INFINITY;
       l_lane[hh] = 0.f;
     }
-    float acc[G][DPL];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-
-    __syncthreads();  // LDS of an abandoned pass is no longer read
-    stage_bt();
-    if (F16 && tid == 0) sVwide[0] = sVwide[1] = 0;
-    __syncthreads();  // window staged
-    // One chunk in flight in registers while the previous one is consumed
-    // from LDS.  ci counts chunks (its parity selects the V-range flag).
-    auto step = [&](int c0, int ci, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) -> bool {
-      __syncthreads();  // previous chunk fully consumed (also every read of the window)
-#pragma unroll
-      for (int r = 0; r < PPT; ++r) {  // piece tid + 256 r: row prow + RSTEP r, column pcol
-        sK[(prow + RSTEP * r) * KSTR + pcol] = kr[r];
-        sV[tid + kDecodeThreads * r] = vr[r];
-      }
-      if constexpr (F16 && DT == PA_BF16) {
-        // largest |v| bit pattern of this thread's V pieces (sign cleared)
-        u16x2_t mx = {0, 0};
-#pragma unroll
-        for (int r = 0; r < PPT; ++r) {
-          const uint32_t w4[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, w4[j] & 0x7FFF7FFFu));
-        }
-        if (max(mx.x, mx.y) >= 0x4780) sVwide[ci & 1] = 1;  // |v| >= 65536, inf or NaN
-      }
-      const int cn = c0 + kChunk;
-      const bool more = cn < t1;
-      if (more && (min(cn + kChunk - 1, t1 - 1) >> lbs) - wb0 >= kBtWin) {  // uniform
-        wb0 = cn >> lbs;
-        stage_bt();
-      }
-      __syncthreads();
-      if constexpr (F16 && DT == PA_BF16) {
-        if (tid == 0) sVwide[(ci + 1) & 1] = 0;  // its last reader was the previous chunk
-        if (__builtin_amdgcn_readfirstlane(sVwide[ci & 1]) != 0) return false;  // uniform
-      }
-      if (more) fetch(cn, kr, vr);  // next chunk in flight
-
-      // ---- QK: lane = token row, this wave's HPW heads
-      const int row = lane;
-      const bool valid = c0 + row < t1;
-      float z[HPW];
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) z[hh] = 0.f;
+  };
+  // Merge of the partition's state -- halves, then waves (the statistics come
+  // from the QK waves) -- written as partition `part`'s partial, or as the
+  // final rows when the context is a single partition.  The chunk tiles'
+  // LDS holds the waves' accumulators meanwhile; the next chunk's loads
+  // stay in flight in registers.
+  // A boundary inside a run parks its merged values in sPend and writes them
+  // once the chunk already in flight has been staged, just before the next
+  // chunk's loads (write_pending): vector memory operations complete in
+  // order, so stores issued while a chunk is in flight would make that
+  // chunk's staging wait for them too, whereas stores issued ahead of the
+  // loads are done by the time those loads are.
+  int pend_part = -1;  // partition of the values in sPend (-1: none)
+  auto write_pending = [&]() {
+    if (pend_part < 0) return;  // uniform
+    // always a partial (a single-partition context has no boundary)
 #pragma unroll 1
-      for (int pc = 0; pc < RC; pc += 4) {
-        uint4 kk[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kk[j] = sK[row * KSTR + pc + j];  // padded rows: conflict-free
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-          const const_u32_ptr qh = qc + hh * (D / 2) + pc * 4;
-          float a = z[hh];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint4 qq = make_uint4(qh[4 * j], qh[4 * j + 1], qh[4 * j + 2], qh[4 * j + 3]);
-            a = dot_chunk<DT>(qq, kk[j], a);
-          }
-          z[hh] = a;
+    for (int k = 0; k < NPT; ++k) {
+      const int i = tid + k * kDecodeThreads;
+      if (i < G * D) {
+        const int h = i / D, d = i % D;
+        const int64_t pi = (head0 + h) * p.max_partitions + p.part_base + pend_part;
+        p.part_out[pi * D + d] = sPend[k * kDecodeThreads + tid] * p.v_scale;
+        if (d == 0) {
+          p.part_ml[2 * pi] = sM[h];
+          p.part_ml[2 * pi + 1] = sL[h];
         }
       }
-      // ---- online softmax of this wave's heads.  The running max moves only
-      // when some token of the chunk exceeds it by more than the headroom, so
-      // the wave-wide maximum is taken only then (a ballot decides).
-      bool resc = false;
-      float alpha[HPW];
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        const int h = wave * HPW + hh;
-        const float zz = valid ? z[hh] * p.scale_log2e : -INFINITY;
-        alpha[hh] = 1.f;
-        if (__any(zz > m_ref[hh] + kLazyRescale)) {
-          const float mn = fmaxf(m_ref[hh], wave_max(zz));
-          alpha[hh] = exp2_diff(m_ref[hh], mn);
-          m_ref[hh] = mn;
-          l_lane[hh] *= alpha[hh];
-          resc = true;
-        }
-        // rounded to f16 once: the PV weights and the normaliser use the
-        // same value
-        const _Float16 ph = (_Float16)(valid ? __builtin_amdgcn_exp2f(zz - m_ref[hh]) : 0.f);
-        l_lane[hh] += (float)ph;
-        sPh[row >> 1][h][row & 1] = ph;
-      }
-      if (lane == 0) {
-        sResc[wave] = resc;
-        if (resc) {
-#pragma unroll
-          for (int hh = 0; hh < HPW; ++hh) sAlpha[wave * HPW + hh] = alpha[hh];
-        }
-      }
-      __syncthreads();
-
-      // ---- PV: wave owns rows 16 wave .. +15 as 8 token pairs; a half-wave
-      // takes pairs (2j, 2j+1) and a lane D/32 columns of all G heads.  Rows
-      // past the end carry p = 0 and finite (clamped) V.
-      // Heads of QK wave w are rescaled only when that wave moved a max.
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        if (__builtin_amdgcn_readfirstlane(sResc[w])) {
-#pragma unroll
-          for (int hh = 0; hh < HPW; ++hh) {
-            const float a = sAlpha[w * HPW + hh];
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[w * HPW + hh][e] *= a;
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < NPI; ++i) {
-        const char* va = pv_base + i * (4 * RC * 16);  // pair wave * 8 + 2 i + half
-        const char* vb = va + RC * 16;
-        uint32_t wa[DPL / 2], wb[DPL / 2];
-        if constexpr (DPL == 4) {
-          const uint2 a2 = *reinterpret_cast<const uint2*>(va);
-          const uint2 b2 = *reinterpret_cast<const uint2*>(vb);
-          wa[0] = a2.x; wa[1] = a2.y; wb[0] = b2.x; wb[1] = b2.y;
-        } else {
-          wa[0] = *reinterpret_cast<const uint32_t*>(va);
-          wb[0] = *reinterpret_cast<const uint32_t*>(vb);
-        }
-        const uint4* pq = reinterpret_cast<const uint4*>(pp_base + i * (2 * G * 4));
-        uint32_t pw[G];
-#pragma unroll
-        for (int h4 = 0; h4 < G / 4; ++h4) {
-          const uint4 pw4 = pq[h4];
-          pw[4 * h4] = pw4.x; pw[4 * h4 + 1] = pw4.y; pw[4 * h4 + 2] = pw4.z; pw[4 * h4 + 3] = pw4.w;
-        }
-        if constexpr (F16) {
-          uint32_t vv[DPL];  // (row 2j, row 2j+1) f16 pairs per column
-#pragma unroll
-          for (int c = 0; c < DPL; ++c) {
-            const uint32_t xa = wa[c / 2], xb = wb[c / 2];
-            if constexpr (DT == PA_BF16) {
-              const float fa = __uint_as_float((c & 1) ? (xa & 0xFFFF0000u) : (xa << 16));
-              const float fb = __uint_as_float((c & 1) ? (xb & 0xFFFF0000u) : (xb << 16));
-              vv[c] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa, fb));
-            } else {
-              vv[c] = __builtin_amdgcn_perm(xb, xa, (c & 1) ? 0x07060302u : 0x05040100u);
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int c = 0; c < DPL; ++c)
-              acc[h][c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[h]),
-                                                 __builtin_bit_cast(f16x2_t, vv[c]), acc[h][c], false);
-        } else {
-          // fp32 products, row 2j then 2j+1
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float pa = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[h] & 0xFFFFu));
-            const float pb = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[h] >> 16));
-#pragma unroll
-            for (int c = 0; c < DPL; ++c) {
-              const float fa = chunk_elem<DT>(make_uint4(wa[c / 2], 0, 0, 0), c & 1);
-              const float fb = chunk_elem<DT>(make_uint4(wb[c / 2], 0, 0, 0), c & 1);
-              acc[h][c] = __builtin_fmaf(pb, fb, __builtin_fmaf(pa, fa, acc[h][c]));
-            }
-          }
-        }
-      }
-      return true;
-    };
-    uint4 kr[PPT], vr[PPT];
-    fetch(t0, kr, vr);
-    for (int c0 = t0, ci = 0; c0 < t1; c0 += kChunk, ++ci)
-      if (!step(c0, ci, kr, vr)) return false;
-
-    // ---- merge: halves, then waves; statistics from the QK waves
+    }
+    pend_part = -1;
+  };
+  auto flush = [&](int part, bool defer) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -332,7 +212,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
         sL[wave * HPW + hh] = lt;
       }
     }
-    __syncthreads();  // last PV done: LDS tiles free for the merge
+    __syncthreads();  // the chunk's last PV reads are done: the tiles are free
     float* sAcc = reinterpret_cast<float*>(sKV);  // [waves][G][D]
     if (half == 0) {
 #pragma unroll
@@ -341,20 +221,168 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
         for (int e = 0; e < DPL; ++e) sAcc[(wave * G + h) * D + dl * DPL + e] = acc[h][e];
     }
     __syncthreads();
-    const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
-    for (int i = tid; i < G * D; i += kDecodeThreads) {
-      const int h = i / D, d = i % D;
-      float o = 0.f;
+#pragma unroll 1
+    for (int k = 0; k < NPT; ++k) {
+      const int i = tid + k * kDecodeThreads;
+      if (i < G * D) {
+        const int h = i / D, d = i % D;
+        float o = 0.f;
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) o += sAcc[(w * G + h) * D + d];
-      emit(p, head0 + h, part, d, D, sM[h], sL[h], o, single_partition(p, L));
+        for (int w = 0; w < kDecodeWaves; ++w) o += sAcc[(w * G + h) * D + d];
+        if (defer)
+          sPend[k * kDecodeThreads + tid] = o;
+        else
+          emit(p, head0 + h, part, d, D, sM[h], sL[h], o, single);
+      }
     }
-    return true;
+    if (defer) pend_part = part;
+    reset();
   };
 
-  if (!run(std::true_type{})) {
-    if constexpr (DT == PA_BF16) run(std::false_type{});
+  // One chunk in flight in registers while the previous one is consumed
+  // from LDS.
+  // cn: the chunk walked after c0 (valid when more).
+  auto step = [&](int c0, int cn, bool more, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
+    __syncthreads();  // previous chunk (or merge) fully consumed, window reads included
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {  // piece tid + 256 r: row prow + RSTEP r, column pcol
+      sK[(prow + RSTEP * r) * KSTR + pcol] = kr[r];
+      sV[tid + kDecodeThreads * r] = vr[r];
+    }
+    if (more && ((cn >> lbs) < wb0 || (min(cn + kChunk - 1, t1 - 1) >> lbs) - wb0 >= kBtWin)) {  // uniform
+      wb0 = cn >> lbs;
+      stage_bt();
+    }
+    __syncthreads();
+    write_pending();              // a finished partition's partial, ahead of the next loads
+    if (more) fetch(cn, kr, vr);  // next chunk in flight
+
+    // ---- QK: lane = token row, this wave's HPW heads
+    const int row = lane;
+    const bool valid = c0 + row < t1;
+    float z[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) z[hh] = 0.f;
+#pragma unroll 1
+    for (int pc = 0; pc < RC; pc += 4) {
+      uint4 kk[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kk[j] = sK[row * KSTR + pc + j];  // padded rows: conflict-free
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const const_u32_ptr qh = qc + hh * (D / 2) + pc * 4;
+        float a = z[hh];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 qq = make_uint4(qh[4 * j], qh[4 * j + 1], qh[4 * j + 2], qh[4 * j + 3]);
+          a = dot_chunk<DT>(qq, kk[j], a);
+        }
+        z[hh] = a;
+      }
+    }
+    // ---- online softmax of this wave's heads.  The running max moves only
+    // when some token of the chunk exceeds it by more than the headroom, so
+    // the wave-wide maximum is taken only then (a ballot decides).
+    bool resc = false;
+    float alpha[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = wave * HPW + hh;
+      const float zz = valid ? z[hh] * p.scale_log2e : -INFINITY;
+      alpha[hh] = 1.f;
+      if (__any(zz > m_ref[hh] + kLazyRescale)) {
+        const float mn = fmaxf(m_ref[hh], wave_max(zz));
+        alpha[hh] = exp2_diff(m_ref[hh], mn);
+        m_ref[hh] = mn;
+        l_lane[hh] *= alpha[hh];
+        resc = true;
+      }
+      // the PV weights and the normaliser use the same fp32 value
+      const float pw = valid ? __builtin_amdgcn_exp2f(zz - m_ref[hh]) : 0.f;
+      l_lane[hh] += pw;
+      sP[row >> 1][h][row & 1] = pw;
+    }
+    if (lane == 0) {
+      sResc[wave] = resc;
+      if (resc) {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) sAlpha[wave * HPW + hh] = alpha[hh];
+      }
+    }
+    __syncthreads();
+
+    // ---- PV: wave owns rows 16 wave .. +15 as 8 token pairs; a half-wave
+    // takes pairs (2j, 2j+1) and a lane D/32 columns of all G heads.  Rows
+    // past the end carry p = 0 and finite (clamped) V.
+    // Heads of QK wave w are rescaled only when that wave moved a max.
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      if (__builtin_amdgcn_readfirstlane(sResc[w])) {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          const float a = sAlpha[w * HPW + hh];
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[w * HPW + hh][e] *= a;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPI; ++i) {
+      const char* va = pv_base + i * (4 * RC * 16);  // pair wave * 8 + 2 i + half
+      const char* vb = va + RC * 16;
+      uint32_t wa[DPL / 2], wb[DPL / 2];
+      if constexpr (DPL == 4) {
+        const uint2 a2 = *reinterpret_cast<const uint2*>(va);
+        const uint2 b2 = *reinterpret_cast<const uint2*>(vb);
+        wa[0] = a2.x; wa[1] = a2.y; wb[0] = b2.x; wb[1] = b2.y;
+      } else {
+        wa[0] = *reinterpret_cast<const uint32_t*>(va);
+        wb[0] = *reinterpret_cast<const uint32_t*>(vb);
+      }
+      float fa[DPL], fb[DPL];
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) {
+        fa[c] = chunk_elem<DT>(make_uint4(wa[c / 2], 0, 0, 0), c & 1);
+        fb[c] = chunk_elem<DT>(make_uint4(wb[c / 2], 0, 0, 0), c & 1);
+      }
+      // weights of the pair for all G heads: (token 2j, token 2j+1) per head
+      const float4* pq = reinterpret_cast<const float4*>(pp_base + i * (2 * G * 2 * 4));
+#pragma unroll
+      for (int h2 = 0; h2 < G / 2; ++h2) {
+        const float4 w4 = pq[h2];  // heads 2 h2 and 2 h2 + 1
+#pragma unroll
+        for (int c = 0; c < DPL; ++c) {
+          acc[2 * h2][c] = __builtin_fmaf(w4.y, fb[c], __builtin_fmaf(w4.x, fa[c], acc[2 * h2][c]));
+          acc[2 * h2 + 1][c] =
+              __builtin_fmaf(w4.w, fb[c], __builtin_fmaf(w4.z, fa[c], acc[2 * h2 + 1][c]));
+        }
+      }
+    }
+  };
+
+  reset();
+  stage_bt();
+  __syncthreads();  // window staged
+  uint4 kr[PPT], vr[PPT];
+  fetch(c_first, kr, vr);
+  // chunks from c_first to the end of the range, then from t0 (whole
+  // chunks: partitions are whole chunks when a run has several)
+  const int n_first = (t1 - c_first + kChunk - 1) / kChunk;  // chunks from c_first on
+  const int nchunks = n_first + (c_first - t0) / kChunk;
+  auto chunk_at = [&](int k) { return k < n_first ? c_first + k * kChunk : t0 + (k - n_first) * kChunk; };
+  int part = part0 + rot;
+  for (int k = 0; k < nchunks; ++k) {  // uniform
+    const int c0 = chunk_at(k);
+    if (nparts > 1) {
+      const int pc = part0 + (c0 - t0) / P;
+      if (pc != part) {
+        flush(part, true);
+        part = pc;
+      }
+    }
+    step(c0, chunk_at(k + 1), k + 1 < nchunks, kr, vr);
   }
+  flush(part, false);
 }
 
 template <pa_dtype DT, int D, bool OFF32>

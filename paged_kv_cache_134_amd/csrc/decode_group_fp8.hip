@@ -27,7 +27,9 @@
 //            holds O[head l % 16][16 b + 4 q4 .. +3] for every block b.
 // Each wave keeps two tiles of K/V in flight (the next two rounds) and reads
 // the block ids it needs from the table two rounds ahead of the rows they
-// locate.  The waves' (max, sum, output) states are merged at the end by the
+// locate.  The probabilities enter PV as two f16 terms, hi = f16(p) and lo =
+// f16(p - hi) (two products on the same V operand), so the weights carry
+// about 22 significant bits; the normaliser sums hi + lo.  The waves' (max, sum, output) states are merged at the end by the
 // log-sum-exp rule.  Heads past G are zero in the query operand, so their
 // scores, probabilities and outputs are never used.  With 16-bit caches the
 // LDS-staged grouped kernel (decode_group.hip) is faster and is used
@@ -87,19 +89,29 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   __shared__ __align__(16) char smem[kLds];
   __shared__ float sM[kDecodeWaves][G], sL[kDecodeWaves][G];
 
-  int s, kvh, part;
-  if (!decode_item(p, true, s, kvh, part)) return;
+  int s, kvh, item;
+  if (!decode_item(p, true, s, kvh, item)) return;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
+  // Tokens [t0, t1): one partition (split-K) or the whole context (single
+  // pass).
   const int L = p.context_lens[s];
+  const int P = p.partition_size;
+  const int part = item;
   int t0 = 0, t1 = L;
-  if (p.partition_size > 0) {
-    t0 = p.key_begin + part * p.partition_size;
+  if (P > 0) {
+    t0 = p.key_begin + part * P;
     if (t0 >= L) return;
-    t1 = min(L, t0 + p.partition_size);
+    t1 = min(L, t0 + P);
   }
+  const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
+  if (t1 <= t0) {  // single pass over an empty context (split-K returned above)
+    emit_zero_rows(p, head0, G, D);
+    return;
+  }
+  const bool single = single_partition(p, L);
 
   const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
   const int lbs = p.log2_bs;
@@ -156,11 +168,16 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
     }
   };
 
-  float m_ref = -INFINITY, l_lane = 0.f;  // softmax state of head tl (this wave's tokens)
+  float m_ref, l_lane;  // softmax state of head tl (this wave's tokens of the partition)
   // O^T blocks: lane holds O[head tl][d = 16 b + 4 q4 + j]
   f32x4_t o[DB];
+  auto reset = [&]() {
+    m_ref = -INFINITY;
+    l_lane = 0.f;
 #pragma unroll
-  for (int b = 0; b < DB; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < DB; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  reset();
 
   // Consumes tile ts from (kr, vr), then refills them with the tile two
   // rounds ahead (its block ids were read two rounds ago).
@@ -204,11 +221,13 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
 #pragma unroll
       for (int b = 0; b < DB; ++b) o[b] *= alpha;  // the lane's own head
     }
-    _Float16 ph[4];
+    _Float16 ph[4], pl[4];  // p = hi + lo, each f16
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      ph[r] = (_Float16)(z[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref));
-      l_lane += (float)ph[r];
+      const float e = z[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
+      ph[r] = (_Float16)e;
+      pl[r] = (_Float16)(e - (float)ph[r]);
+      l_lane += (float)ph[r] + (float)pl[r];
     }
     wave_lds_sync();  // the tile's V rows are visible to the whole wave
 
@@ -217,15 +236,58 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
     // (v_mfma_f32_16x16x16_f16).  The B operand is this lane's own four
     // probabilities (tokens 4 q4 .. +3 of head tl, where the QK product put
     // them; zero past the group and the context).
-    const f16x4_t pb = {ph[0], ph[1], ph[2], ph[3]};
+    const f16x4_t pbh = {ph[0], ph[1], ph[2], ph[3]};
+    const f16x4_t pbl = {pl[0], pl[1], pl[2], pl[3]};
+    // (every block's hi product before the lo products: no product waits on
+    // the one just issued into the same accumulator)
+    f16x4_t a[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      f16x4_t a;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = vh[j * (VSTR * 8) + 16 * b];
-      o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb, o[b], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) a[b][j] = vh[j * (VSTR * 8) + 16 * b];
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(a[b], pbh, o[b], 0, 0, 0);
     }
+#pragma unroll
+    for (int b = 0; b < DB; ++b) o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(a[b], pbl, o[b], 0, 0, 0);
     wave_lds_sync();  // this tile's V is consumed before the next tile's stores
+  };
+
+  // Merge of the waves' states (log-sum-exp rule) -- written as the
+  // partition's partial, or as the final rows of a single-partition context.
+  // The LDS V rows hold the waves' accumulators meanwhile.
+  auto flush = [&]() {
+    // this wave's statistics of head tl (summed over the four quarters)
+    l_lane += __shfl_xor(l_lane, 16);
+    l_lane += __shfl_xor(l_lane, 32);
+    if (lane < G) {
+      sM[wave][lane] = m_ref;
+      sL[wave][lane] = l_lane;
+    }
+    __syncthreads();  // every wave's tiles of the partition are done: the LDS rows are free
+    float* sAcc = reinterpret_cast<float*>(smem);  // [waves][G][D]
+    if (tl < G) {
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+        store16(sAcc + (wave * G + tl) * D + 16 * b + 4 * q4,
+                make_uint4(__float_as_uint(o[b][0]), __float_as_uint(o[b][1]), __float_as_uint(o[b][2]),
+                           __float_as_uint(o[b][3])));
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int i = tid; i < G * D; i += kDecodeThreads) {
+      const int h = i / D, d = i % D;
+      float M = sM[0][h];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sM[w][h]);
+      float lsum = 0.f, ov = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float a = exp2_diff(sM[w][h], M);
+        lsum += a * sL[w][h];
+        ov += a * sAcc[(w * G + h) * D + d];
+      }
+      emit(p, head0 + h, part, d, D, M, lsum, ov, single);
+    }
   };
 
   // Two tile buffers alternate, so two tiles per wave are always in flight.
@@ -239,41 +301,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
     if (ts + kRound - kTile * wave >= t1) break;
     tile(ts + kRound, kb_, vb_, bid_b);
   }
-  // this wave's statistics of head tl (summed over the four quarters)
-  l_lane += __shfl_xor(l_lane, 16);
-  l_lane += __shfl_xor(l_lane, 32);
-  const float m_out = m_ref, l_out = l_lane;
-
-  // ---- merge of the waves (log-sum-exp rule)
-  if (lane < G) {
-    sM[wave][lane] = m_out;
-    sL[wave][lane] = l_out;
-  }
-  __syncthreads();  // every wave's loop is done: the LDS rows are free
-  float* sAcc = reinterpret_cast<float*>(smem);  // [waves][G][D]
-  if (tl < G) {
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-      store16(sAcc + (wave * G + tl) * D + 16 * b + 4 * q4,
-              make_uint4(__float_as_uint(o[b][0]), __float_as_uint(o[b][1]), __float_as_uint(o[b][2]),
-                         __float_as_uint(o[b][3])));
-  }
-  __syncthreads();
-  const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
-  for (int i = tid; i < G * D; i += kDecodeThreads) {
-    const int h = i / D, d = i % D;
-    float M = sM[0][h];
-#pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sM[w][h]);
-    float lsum = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float a = exp2_diff(sM[w][h], M);
-      lsum += a * sL[w][h];
-      o += a * sAcc[(w * G + h) * D + d];
-    }
-    emit(p, head0 + h, part, d, D, M, lsum, o, single_partition(p, L));
-  }
+  flush();
 }
 
 template <pa_dtype DT, int D, bool OFF32>

@@ -754,26 +754,43 @@ extern "C" pa_status pa_prefill_fp8(void* out, pa_dtype out_dtype, const void* q
 // ----------------------------------------------------------- metadata check
 extern "C" pa_status pa_check_metadata(const int32_t* block_tables, const int32_t* context_lens,
                                        const int64_t* slot_mapping, int32_t num_seqs,
-                                       int32_t max_blocks_per_seq, int32_t num_tokens,
-                                       int32_t block_size, int32_t num_blocks, void* stream) {
-  if (num_seqs < 0 || max_blocks_per_seq < 0 || num_tokens < 0 || block_size <= 0 || num_blocks <= 0)
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       int32_t num_tokens, int32_t block_size, int32_t num_blocks,
+                                       int32_t common_prefix_len, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0 || num_tokens < 0 ||
+      block_size <= 0 || num_blocks <= 0 || common_prefix_len < 0)
     return pa_fail(PA_ERR_INVALID_ARGUMENT, "pa_check_metadata: bad sizes");
+  if (common_prefix_len > 0 && (!block_tables || !context_lens))
+    return pa_fail(PA_ERR_INVALID_ARGUMENT,
+                   "pa_check_metadata: the shared-prefix check needs block_tables and context_lens");
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "pa_check_metadata: synchronize");
   char msg[200];
+  auto bad = [&](const char* fmt, auto... a) {
+    std::snprintf(msg, sizeof msg, fmt, a...);
+    return pa_fail(PA_ERR_METADATA, msg);
+  };
   std::vector<int32_t> lens;
   if (context_lens && num_seqs) {
     lens.resize(num_seqs);
     e = hipMemcpy(lens.data(), context_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "pa_check_metadata: copy context_lens");
+    const int64_t cap = block_tables ? (int64_t)max_blocks_per_seq * block_size : INT64_MAX;
     for (int32_t s = 0; s < num_seqs; ++s) {
-      if (lens[s] < 0 || (int64_t)lens[s] > (int64_t)max_blocks_per_seq * block_size) {
-        std::snprintf(msg, sizeof msg, "context_lens[%d] = %d outside [0, %lld]", s, lens[s],
-                      (long long)max_blocks_per_seq * block_size);
-        return pa_fail(PA_ERR_METADATA, msg);
-      }
+      if (lens[s] < 0 || lens[s] > max_context_len)
+        return bad("context_lens[%d] = %d outside [0, max_context_len = %d]", s, lens[s],
+                   max_context_len);
+      if (lens[s] > cap)
+        return bad("context_lens[%d] = %d exceeds the table's %lld slots", s, lens[s],
+                   (long long)cap);
+      if (lens[s] < common_prefix_len)
+        return bad("context_lens[%d] = %d is shorter than common_prefix_len = %d", s, lens[s],
+                   common_prefix_len);
     }
   }
+  if (common_prefix_len % block_size != 0)
+    return bad("common_prefix_len = %d is not a multiple of block_size = %d", common_prefix_len,
+               block_size);
   if (block_tables && num_seqs && max_blocks_per_seq) {
     std::vector<int32_t> bt((size_t)num_seqs * max_blocks_per_seq);
     e = hipMemcpy(bt.data(), block_tables, sizeof(int32_t) * bt.size(), hipMemcpyDeviceToHost);
@@ -783,13 +800,16 @@ extern "C" pa_status pa_check_metadata(const int32_t* block_tables, const int32_
                                         : ((int64_t)lens[s] + block_size - 1) / block_size;
       for (int64_t i = 0; i < used; ++i) {
         const int32_t b = bt[(size_t)s * max_blocks_per_seq + i];
-        if (b < 0 || b >= num_blocks) {
-          std::snprintf(msg, sizeof msg, "block_tables[%d][%lld] = %d outside [0, %d)", s,
-                        (long long)i, b, num_blocks);
-          return pa_fail(PA_ERR_METADATA, msg);
-        }
+        if (b < 0 || b >= num_blocks)
+          return bad("block_tables[%d][%lld] = %d outside [0, %d)", s, (long long)i, b, num_blocks);
       }
     }
+    const int32_t nbc = common_prefix_len / block_size;  // <= every row's used entries
+    for (int32_t s = 1; s < num_seqs; ++s)
+      for (int32_t i = 0; i < nbc; ++i)
+        if (bt[(size_t)s * max_blocks_per_seq + i] != bt[i])
+          return bad("block_tables[%d][%d] = %d differs from row 0's shared block %d", s, i,
+                     bt[(size_t)s * max_blocks_per_seq + i], bt[i]);
   }
   if (slot_mapping && num_tokens) {
     std::vector<int64_t> sl(num_tokens);
@@ -799,11 +819,10 @@ extern "C" pa_status pa_check_metadata(const int32_t* block_tables, const int32_
     std::vector<char> seen((size_t)nslots, 0);
     for (int32_t i = 0; i < num_tokens; ++i) {
       if (sl[i] < 0) continue;
-      if (sl[i] >= nslots || seen[sl[i]]) {
-        std::snprintf(msg, sizeof msg, "slot_mapping[%d] = %lld %s", i, (long long)sl[i],
-                      sl[i] >= nslots ? "out of range" : "repeats an earlier slot");
-        return pa_fail(PA_ERR_METADATA, msg);
-      }
+      if (sl[i] >= nslots) return bad("slot_mapping[%d] = %lld out of range [0, %lld)", i,
+                                      (long long)sl[i], (long long)nslots);
+      if (seen[sl[i]]) return bad("slot_mapping[%d] = %lld repeats an earlier slot", i,
+                                  (long long)sl[i]);
       seen[sl[i]] = 1;
     }
   }

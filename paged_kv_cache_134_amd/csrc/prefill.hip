@@ -30,13 +30,24 @@
 //     probabilities, with the key order permuted consistently in A and B),
 //     so the online-softmax statistics and the output rescaling stay
 //     in-lane;
-//   * scores stay unscaled until exp2(fma(z, scale*log2e, -m)); the running
-//     max moves only past a 2^8 headroom (a ballot decides); probabilities
-//     are rounded to f16 for PV (relative error at most 2^-10 per weight; V
-//     is converted exactly from bf16 and must lie in f16 range) and the
-//     normaliser sums the rounded values with v_dot2, so the weights that
-//     multiply V are exactly the ones that are divided out; QK^T uses the
-//     stored type with fp32 accumulation;
+//   * scores stay unscaled until exp2(fma(z, scale*log2e, 7 - m)); the
+//     running max moves only past a 2^8 headroom (a ballot decides), so a
+//     weight is at most 2^15; each weight is split into two f16 terms, hi =
+//     f16(p) and lo = f16(p - hi), and PV takes both products on the same V
+//     operand, so the weights carry about 22 significant bits (relative
+//     error below 2^-20, plus 2^-24 absolute in the scaled units for weights
+//     below 2^-10 of the reference); the normaliser sums hi + lo with v_dot2,
+//     so the weights that multiply V are exactly the ones that are divided
+//     out, and the 2^7 cancels (prefix partials are written without it);
+//     QK^T uses the stored type with fp32 accumulation;
+//   * V is staged as f16: exactly for f16 and FP8 caches, and for bf16
+//     values below 2^16 in magnitude.  A bf16 tile holding a finite |v| of
+//     2^16 or more (found while it is staged) sends the workgroup back to
+//     its first tile with V stored as v * 2^-vsh, vsh chosen from that
+//     magnitude so the largest value seen stays below 2^15 (exact but for
+//     values under 2^-24 of the scaled range, which become f16 subnormals);
+//     the output is multiplied by 2^vsh.  Infinities and NaN pass through
+//     as themselves;
 //   * a wave whose rows are all padding, or that sees none of a tile's keys,
 //     skips that tile's products; the wave index goes through readfirstlane
 //     so these tests, and the causal mask (applied only to tiles that reach
@@ -48,6 +59,8 @@
 //     normalisation.  Their staging registers are half as many, so outside
 //     the prefix pass they run 3 waves per SIMD (the others 2).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kernel_common.h"
 #include "pa_internal.h"
@@ -61,6 +74,7 @@ constexpr int kQW = 32;                         // query rows per wave
 constexpr int kBM = kPrefillWaves * kQW;        // query rows per workgroup
 constexpr int kBN = 64;                         // keys per tile
 constexpr float kLazyRescaleP = 8.f;            // log2 headroom of the running max
+constexpr float kWeightLog2 = 7.f;              // weights carry 2^7 (largest 2^15, within f16)
 constexpr int kBtWinP = 256;                    // block-table entries staged in LDS at a time
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -156,6 +170,9 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
   __shared__ __attribute__((aligned(16))) char sK[kBN * KROW];
   __shared__ __attribute__((aligned(16))) char sV[D * VROW];
   __shared__ int32_t s_bt[kBtWinP];  // block-table window
+  // per tile parity: largest finite |v| (bf16 bits) beyond the current V range, 0 = none
+  __shared__ int32_t sVwide[2];
+  constexpr bool kWideCheck = !FP8 && DT == PA_BF16;
 
   // XCD-aware order: consecutive workgroup ids go round-robin to the 8 XCDs
   // (each with its own L2).  Pairs are numbered head-major (pair = head *
@@ -217,11 +234,7 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
   }
 
   f32x16_t o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m, l;
 
   const int32_t* bt = p.block_tables + (PREFIX ? 0 : (int64_t)s * p.max_blocks_per_seq);
   const int lbs = p.log2_bs;
@@ -246,8 +259,6 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
   auto stage_bt = [&]() {
     for (int i = tid; i < kBtWinP; i += kPrefillThreads) s_bt[i] = bt[min(wb0 + i, e_last)];
   };
-  stage_bt();
-  __syncthreads();
 
   // Global -> registers for one key tile.  Keys past kend are clamped to the
   // last visible key (finite data the tile reads anyway); the causal mask
@@ -303,8 +314,81 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
   const float c = p.scale_log2e;
   const uint32_t ones = pk_f16(1.f, 1.f);
 
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  m = -INFINITY;
+  l = 0.f;
+  stage_bt();
+  if (kWideCheck && tid == 0) sVwide[0] = sVwide[1] = 0;
+  __syncthreads();
+  int vsh = 0;  // V is held in the tile as v * 2^-vsh (grows only for bf16 caches)
+  int ti = 0;   // tile count (its parity selects the V-range flag)
   TileRegs tr = fetch(k_lo);
-  for (int k0 = k_lo; k0 < kend; k0 += kBN) {
+  // V of tile registers -> LDS, transposed to [d][key] in f16 (times
+  // 2^-vsh).  CHECK (bf16 caches): also flag, in sVwide, a finite value too
+  // large for the current shift.
+  auto stage_v = [&](auto check_tag) {
+    constexpr bool CHECK = decltype(check_tag)::value;
+    const uint32_t wide_bits = (uint32_t)min(143 + vsh, 255) << 7;  // |v| >= 2^(16 + vsh)
+    const float vmul = __builtin_ldexpf(1.f, -vsh);
+    if (VITEMS == kPrefillThreads || tid < VITEMS) {  // head size 64: half the threads stage no V
+      // key group v_kq (keys 4 v_kq .. +3) goes to group slot (v_kq & ~3) +
+      // 2 (v_kq & 1) + ((v_kq >> 1) & 1) of the row: in every 16-key slice
+      // the groups are stored in the order 0, 2, 1, 3, so the 8 keys one
+      // half-wave contracts per product (groups hf and hf + 2) are 16
+      // contiguous bytes
+      const int v_slot = ((v_kq & ~3) + 2 * (v_kq & 1) + ((v_kq >> 1) & 1)) * 8;
+      float vmax = 0.f;  // bf16 caches: largest |v| staged (fmaxf skips NaN)
+      float fv[4][8];  // FP8: the 8 columns of each of the 4 keys
+      if constexpr (FP8) {
+  #pragma unroll
+        for (int k = 0; k < 4; ++k) fp8x8_to_f32(tr.v[k], fv[k]);
+      }
+  #pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        // columns e, e+1 of keys v_kq*4 .. +3
+        float f0[4], f1[4];
+  #pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f0[k] = FP8 ? fv[k][e] : chunk_elem<DT>(tr.v[k], e);
+          f1[k] = FP8 ? fv[k][e + 1] : chunk_elem<DT>(tr.v[k], e + 1);
+          if (kWideCheck && vsh != 0) {  // exact power-of-two scaling
+            f0[k] *= vmul;
+            f1[k] *= vmul;
+          }
+        }
+        const uint2 w0 = make_uint2(pk_f16(f0[0], f0[1]), pk_f16(f0[2], f0[3]));
+        const uint2 w1 = make_uint2(pk_f16(f1[0], f1[1]), pk_f16(f1[2], f1[3]));
+        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e) * VROW + v_slot) = w0;
+        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e + 1) * VROW + v_slot) = w1;
+        if constexpr (CHECK) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) vmax = fmaxf(vmax, fmaxf(fabsf(f0[k]), fabsf(f1[k])));
+        }
+      }
+      // The staged (scaled) values must stay below 2^16 in magnitude (f16's
+      // largest finite is 65504; no bf16 value lies in [65504, 65536)).  Only
+      // past that -- or for an infinity, which passes through as itself --
+      // are the thread's raw values looked at one by one for the largest
+      // finite magnitude beyond the range.
+      if (CHECK && vmax >= 65536.f) {
+        uint32_t big = 0;
+        uint32_t raw[16] = {tr.v[0].x, tr.v[0].y, tr.v[0].z, tr.v[0].w, tr.v[1].x, tr.v[1].y,
+                            tr.v[1].z, tr.v[1].w, tr.v[2].x, tr.v[2].y, tr.v[2].z, tr.v[2].w,
+                            tr.v[3].x, tr.v[3].y, tr.v[3].z, tr.v[3].w};
+  #pragma unroll
+        for (int q = 0; q < 32; ++q) {
+          const uint32_t b = (raw[q / 2] >> (16 * (q & 1))) & 0x7FFFu;
+          if (b >= wide_bits && b < 0x7F80u) big = max(big, b);
+        }
+        if (big) atomicMax(&sVwide[ti & 1], (int32_t)big);
+      }
+    }
+  };
+
+  for (int k0 = k_lo; k0 < kend; k0 += kBN, ++ti) {
     // ---- registers -> LDS: K row-major, V transposed to [d][key] in f16
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -317,33 +401,7 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
         store16(sK + k_row * KROW + k_chunk(i) * 16, tr.k[i]);
       }
     }
-    if (VITEMS == kPrefillThreads || tid < VITEMS) {  // head size 64: half the threads stage no V
-      // key group v_kq (keys 4 v_kq .. +3) goes to group slot (v_kq & ~3) +
-      // 2 (v_kq & 1) + ((v_kq >> 1) & 1) of the row: in every 16-key slice
-      // the groups are stored in the order 0, 2, 1, 3, so the 8 keys one
-      // half-wave contracts per product (groups hf and hf + 2) are 16
-      // contiguous bytes
-      const int v_slot = ((v_kq & ~3) + 2 * (v_kq & 1) + ((v_kq >> 1) & 1)) * 8;
-      float fv[4][8];  // FP8: the 8 columns of each of the 4 keys
-      if constexpr (FP8) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) fp8x8_to_f32(tr.v[k], fv[k]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        // columns e, e+1 of keys v_kq*4 .. +3
-        float f0[4], f1[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f0[k] = FP8 ? fv[k][e] : chunk_elem<DT>(tr.v[k], e);
-          f1[k] = FP8 ? fv[k][e + 1] : chunk_elem<DT>(tr.v[k], e + 1);
-        }
-        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e) * VROW + v_slot) =
-            make_uint2(pk_f16(f0[0], f0[1]), pk_f16(f0[2], f0[3]));
-        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e + 1) * VROW + v_slot) =
-            make_uint2(pk_f16(f1[0], f1[1]), pk_f16(f1[2], f1[3]));
-      }
-    }
+    stage_v(std::integral_constant<bool, kWideCheck>{});
     {
       // the next tile's entries must be in the window; every read of it
       // ended with the previous fetch, which the loop's last barrier orders
@@ -356,6 +414,20 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
       }
     }
     __syncthreads();
+    if constexpr (kWideCheck) {
+      const int wv = __builtin_amdgcn_readfirstlane(sVwide[ti & 1]);
+      if (tid == 0) sVwide[(ti + 1) & 1] = 0;  // its last reader was the previous tile
+      if (wv != 0) {  // uniform and rare: a larger shift from this tile on
+        // the largest finite |v| seen (2^e <= |v| < 2^(e+1)) lands below 2^15
+        const int nv = ((wv >> 7) - 127) - 14;
+        const float a = __builtin_ldexpf(1.f, vsh - nv);  // exact rescale of the fp32 sums
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= a;
+        vsh = nv;
+        if (VITEMS == kPrefillThreads || tid < VITEMS) stage_v(std::false_type{});  // this tile again
+        __syncthreads();
+      }
+    }
     tr = fetch(k0 + kBN);  // next tile in flight (clamped past the end: never a wait on a branch)
     if (wave_rows && k0 <= lim_max) {  // wave-uniform
 
@@ -403,19 +475,25 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= a;
     }
-    // p = 2^(c z - m), rounded to f16 (the first key of the range is visible
-    // to every query, so m is finite here and masked scores give exp2(-inf)
-    // = 0); the normaliser sums the rounded values
-    const float nm = -m;
-    uint32_t pp[2][8];
+    // p = 2^(c z - m + 7) (the first key of the range is visible to every
+    // query, so m is finite here and masked scores give exp2(-inf) = 0),
+    // split into f16 hi = f16(p) and lo = f16(p - hi); the normaliser sums
+    // hi + lo
+    const float nm = kWeightLog2 - m;
+    uint32_t ph[2][8], pl[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const uint32_t w2 = pk_f16(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], c, nm)),
-                                   __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, nm)));
-        pp[kb][i / 2] = w2;
-        l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w2), __builtin_bit_cast(f16x2_t, ones),
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], c, nm));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, nm));
+        const uint32_t h2 = pk_f16(e0, e1);
+        const f16x2_t hv = __builtin_bit_cast(f16x2_t, h2);
+        const uint32_t l2 = pk_f16(e0 - (float)hv.x, e1 - (float)hv.y);
+        ph[kb][i / 2] = h2;
+        pl[kb][i / 2] = l2;
+        l = __builtin_amdgcn_fdot2(hv, __builtin_bit_cast(f16x2_t, ones), l, false);
+        l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, l2), __builtin_bit_cast(f16x2_t, ones),
                                    l, false);
       }
 
@@ -427,13 +505,31 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kb = t / 2, jp = t % 2;
-      const f16x8_t pb = __builtin_bit_cast(
-          f16x8_t, make_uint4(pp[kb][4 * jp], pp[kb][4 * jp + 1], pp[kb][4 * jp + 2], pp[kb][4 * jp + 3]));
+      const f16x8_t pbh = __builtin_bit_cast(
+          f16x8_t, make_uint4(ph[kb][4 * jp], ph[kb][4 * jp + 1], ph[kb][4 * jp + 2], ph[kb][4 * jp + 3]));
+      const f16x8_t pbl = __builtin_bit_cast(
+          f16x8_t, make_uint4(pl[kb][4 * jp], pl[kb][4 * jp + 1], pl[kb][4 * jp + 2], pl[kb][4 * jp + 3]));
       const int col = (kb * 32 + jp * 16) * 2 + hf * 16;
+      if constexpr (kPrefillMinWaves<PREFIX, FP8> == 2) {
+        // every block's hi product before the lo products, so no product
+        // waits on the one just issued into the same accumulator (the
+        // 3-wave FP8 kernel has no registers for the A operands meanwhile)
+        f16x8_t a[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f16x8_t a = __builtin_bit_cast(f16x8_t, load16(sV + (db * 32 + lq) * VROW + col));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb, o[db], 0, 0, 0);
+        for (int db = 0; db < DB; ++db) {
+          a[db] = __builtin_bit_cast(f16x8_t, load16(sV + (db * 32 + lq) * VROW + col));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[db], pbh, o[db], 0, 0, 0);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[db], pbl, o[db], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const f16x8_t a = __builtin_bit_cast(f16x8_t, load16(sV + (db * 32 + lq) * VROW + col));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pbh, o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pbl, o[db], 0, 0, 0);
+        }
       }
     }
     }  // wave has visible keys in this tile
@@ -443,11 +539,12 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
   // ---- normalise and store: lane holds O[query lq][d = 32 db + 8 g + 4 hf + i]
   const float lt = l + __shfl_xor(l, 32);
   if constexpr (PREFIX) {
-    // partial of (row j, head h, key partition s)
+    // partial of (row j, head h, key partition s), without the weights'
+    // factor 2^7 and with V's 2^vsh
     if (j < n) {
       const int64_t pi = ((int64_t)j * p.num_heads + h) * p.max_partitions + s;
       float* po = p.part_out + pi * D;
-      const float vsc = p.v_scale;
+      const float vsc = p.v_scale * __builtin_ldexpf(1.f, vsh - (int)kWeightLog2);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -457,13 +554,13 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
                              __float_as_uint(o[db][4 * g + 2] * vsc), __float_as_uint(o[db][4 * g + 3] * vsc)));
       if (hf == 0) {
         p.part_ml[2 * pi] = m;
-        p.part_ml[2 * pi + 1] = lt;
+        p.part_ml[2 * pi + 1] = lt * __builtin_ldexpf(1.f, -(int)kWeightLog2);
       }
     }
     return;
   }
   if (j < n) {
-    const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
+    const float inv = lt > 0.f ? p.v_scale * __builtin_ldexpf(1.f, vsh) / lt : 0.f;
     const int64_t row = ((int64_t)(q_begin + j) * p.num_heads + h) * D;
     // four consecutive columns per group g
 #pragma unroll

@@ -1,7 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-bench times (HND pools, split-K decode with the automatic partition size),
-on sampled outputs the oracle computes one by one, plus properties that hold
-at any size (every output finite, sampled pool slots bit-exact).
+bench times (HND pools; split-K decode at the workload's own partition size
+where it names one, and at the library's choice), on whole outputs where the
+oracle finishes in seconds and on every head of sampled sequences / rows
+otherwise, plus properties that hold at any size (every output finite,
+sampled pool slots bit-exact).
 
 The oracle side derives its own slots (allocator model) and computes each
 sampled output as the plain definition over the sequence's logical K/V.
@@ -53,17 +55,48 @@ def _check_pool_samples(dw, st, seqs):
             assert np.array_equal(vg, raw(np.stack(v_log)[:, kvh])), (s, kvh)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, "5a"])
-def test_decode_full_size_sampled(cfg):
+def _oracle_heads(w, s, qf, heads, rows=None):
+    """The plain definition for sequence s at the given query heads: decode
+    (rows None) or the prefill rows given as packed row indices.  K/V are the
+    sequence's logical values, upcast one kv head at a time."""
+    K, V = w.kv(s)
+    out = {}
+    by_g = {}
+    for h in heads:
+        by_g.setdefault(h // w.G, []).append(h)
+    n, L = (int(w.query_lens[s]), int(w.context_lens[s])) if rows is not None else (0, 0)
+    for g, hs in by_g.items():
+        Kf, Vf = A.bits_to_f64(K[:, g], w.dtype), A.bits_to_f64(V[:, g], w.dtype)
+        for h in hs:
+            if rows is None:
+                out[h], _ = A.attention_dense(qf[s, h], Kf, Vf, w.scale)
+            else:
+                q0 = int(w.query_start_loc[s])
+                for r in rows:
+                    a = L - n + (r - q0)  # absolute position of the row's token
+                    out[(r, h)], _ = A.attention_dense(qf[r, h], Kf[:a + 1], Vf[:a + 1], w.scale)
+    return out
+
+
+# (workload, partition size: None = the library's choice, else the workload's own)
+DECODE_FULL = [(2, None), (3, None), (4, 512), (4, None), ("5a", None)]
+
+
+@pytest.mark.parametrize("cfg,part", DECODE_FULL)
+def test_decode_full_size(cfg, part):
+    """Full-size decode in the bench's launch configuration.  The 7B-like and
+    70B-like workloads are compared whole (every sequence and head); the
+    long-context (at its 512-token partitions and at the library's choice)
+    and shared-prefix workloads on every head of sampled sequences."""
     need_gpu()
     w = workloads.make(cfg)
-    announce("full-size decode", w.name)
+    ps = part if part is not None else P.pa_decode_auto_partition(
+        w.S, w.H, w.Hkv, P.KV_DTYPE[w.dtype], w.max_context_len, int(w.context_lens.sum()))
+    assert ps > 0
+    announce("full-size decode", w.name, "partition", ps)
     dw = M.setup(w, layout=P.HND, write_step=True)
     st = build_state(w)
     assert np.array_equal(dw.block_tables_host, st.block_tables)
-    ps = P.pa_decode_auto_partition(w.S, w.H, w.Hkv, P.KV_DTYPE[w.dtype], dw.max_context_len,
-                                   int(w.context_lens.sum()))
-    assert ps > 0
     ws = torch.empty(P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, ps),
                      dtype=torch.uint8, device="cuda")
     out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
@@ -72,25 +105,29 @@ def test_decode_full_size_sampled(cfg):
     P.pa_decode_reduce(out, dw.context_lens, dw.max_context_len, w.Hkv, ps, ws)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    assert np.all(np.isfinite(got))
     lens = w.context_lens
-    seqs = sorted({0, w.S // 2, w.S - 1, int(np.argmax(lens)), int(np.argmin(lens))})
-    _check_pool_samples(dw, st, seqs)
+    whole = cfg in (2, 3)
+    seqs = range(w.S) if whole else sorted({0, w.S // 2, w.S - 1, int(np.argmax(lens)),
+                                            int(np.argmin(lens))})
+    _check_pool_samples(dw, st, sorted({0, w.S // 2, w.S - 1, int(np.argmax(lens))}))
+    del dw
+    assert np.all(np.isfinite(got))
     qf = A.bits_to_f64(w.query, w.dtype)
     worst = 0.0
     for s in seqs:
-        K, V = w.kv(s)
-        for h in sorted({0, w.G - 1, w.H // 2, w.H - 1}):
-            g = h // w.G
-            ref, _ = A.attention_dense(qf[s, h], A.bits_to_f64(K[:, g], w.dtype),
-                                       A.bits_to_f64(V[:, g], w.dtype), w.scale)
-            worst = max(worst, float(np.max(np.abs(got[s, h] - ref))))
-    announce("max-abs", worst)
+        ref = _oracle_heads(w, s, qf, range(w.H))
+        for h in range(w.H):
+            worst = max(worst, float(np.max(np.abs(got[s, h] - ref[h]))))
+    announce("max-abs", worst, "over", len(seqs), "sequences x", w.H, "heads")
     assert worst <= TOL[w.dtype]
 
 
 @pytest.mark.parametrize("cfg", ["5b", "5c"])
-def test_prefill_full_size_sampled(cfg):
+def test_prefill_full_size(cfg):
+    """Full-size prefill.  The packed prefill of the printed lengths is
+    compared whole (all 460 rows, every head); the prefix-cached suffix
+    prefill on every head of sampled rows (first, second, middle, last) of
+    sampled sequences."""
     need_gpu()
     w = workloads.make(cfg)
     announce("full-size prefill", w.name)
@@ -103,22 +140,18 @@ def test_prefill_full_size_sampled(cfg):
                  layout=dw.layout)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
+    seqs = range(w.S) if cfg == "5b" else sorted({0, w.S // 2, w.S - 1})
+    _check_pool_samples(dw, st, sorted({0, w.S // 2, w.S - 1}))
+    del dw
     assert np.all(np.isfinite(got))
-    seqs = sorted({0, w.S // 2, w.S - 1})
-    _check_pool_samples(dw, st, seqs)
     qf = A.bits_to_f64(w.query, w.dtype)
     worst = 0.0
     for s in seqs:
-        K, V = w.kv(s)
-        n, L = int(w.query_lens[s]), int(w.context_lens[s])
-        for h in sorted({0, w.H - 1}):
-            g = h // w.G
-            Kf, Vf = A.bits_to_f64(K[:, g], w.dtype), A.bits_to_f64(V[:, g], w.dtype)
-            for j in sorted({0, 1, n // 2, n - 1}):
-                a = L - n + j
-                r = int(w.query_start_loc[s]) + j
-                ref, _ = A.attention_dense(qf[r, h], Kf[:a + 1], Vf[:a + 1], w.scale)
-                worst = max(worst, float(np.max(np.abs(got[r, h] - ref))))
+        n, q0 = int(w.query_lens[s]), int(w.query_start_loc[s])
+        rows = range(q0, q0 + n) if cfg == "5b" else [q0 + j for j in sorted({0, 1, n // 2, n - 1})]
+        ref = _oracle_heads(w, s, qf, range(w.H), rows=rows)
+        for (r, h), o in ref.items():
+            worst = max(worst, float(np.max(np.abs(got[r, h] - o))))
     announce("max-abs", worst)
     assert worst <= TOL[w.dtype]
 
@@ -145,12 +178,9 @@ def test_cascade_decode_full_size_sampled():
     qf = A.bits_to_f64(w.query, w.dtype)
     worst = 0.0
     for s in sorted({0, w.S // 2, w.S - 1}):
-        K, V = w.kv(s)
-        for h in sorted({0, w.H // 2, w.H - 1}):
-            g = h // w.G
-            ref, _ = A.attention_dense(qf[s, h], A.bits_to_f64(K[:, g], w.dtype),
-                                       A.bits_to_f64(V[:, g], w.dtype), w.scale)
-            worst = max(worst, float(np.max(np.abs(got[s, h] - ref))))
+        ref = _oracle_heads(w, s, qf, range(w.H))
+        for h in range(w.H):
+            worst = max(worst, float(np.max(np.abs(got[s, h] - ref[h]))))
     announce("max-abs", worst)
     assert worst <= TOL[w.dtype]
 

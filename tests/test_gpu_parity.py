@@ -78,24 +78,41 @@ def test_write_and_decode_small(name, layout):
         assert err <= TOL[w.dtype], f"{name} part={part} err={err} at {where}"
 
 
-@pytest.mark.parametrize("G", [1, 8])
-def test_empty_contexts_give_zero_rows(G):
-    """Contexts of length 0 (set on the device after the pool is written)
-    give zero rows in every mode: single pass, explicit partitions and the
-    automatic split; the other rows match the oracle."""
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("G", [1, 4, 8, 16])
+def test_empty_contexts_give_zero_rows(G, kv):
+    """Contexts of length 0 (set on the device after the pool is written,
+    sequence 0 among them) give zero rows in every mode: single pass,
+    explicit partitions and the automatic split; the other rows match the
+    oracle.  Every kernel family (per-head, grouped 16-bit, grouped FP8) in
+    single pass must return before reading the empty row's block table."""
     need_gpu()
     w = workloads.make(3, S=9, H=4 * G, Hkv=4, len_median=600, len_cap=2500)
-    announce("empty contexts", "G", G)
-    dw = M.setup(w, write_step=True)
+    announce("empty contexts", "G", G, kv)
+    fp8 = kv == "e4m3"
+    kw = dict(kv_dtype="e4m3", k_scale=KS, v_scale=VS) if fp8 else {}
+    dw = M.setup(w, write_step=True, **kw)
     st = build_state(w)
-    kc, vc = build_pool(w, st, include_step=True)
+    kc, vc = build_pool(w, st, include_step=True, **kw)
     lens = w.context_lens.astype(np.int64).copy()
     lens[[0, 4, 8]] = 0
     dw.context_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
     ref = A.decode_ref(w.query, kc, vc, st.block_tables, np.maximum(lens, 1), w.scale, w.bs,
-                       w.dtype)
+                       w.dtype, **kw)
     for part in (0, 64, 512, -1):
-        got = _decode(dw, part)
+        if fp8:
+            out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+            ws = None
+            if part != 0:
+                nbytes = P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, part)
+                ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+            P.pa_decode_fp8(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                            dw.context_lens, dw.max_context_len, w.scale, KS, VS,
+                            partition_size=part, workspace=ws)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+        else:
+            got = _decode(dw, part)
         assert np.all(got[lens == 0] == 0.0), part
         err, where = max_abs(got[lens > 0], ref[lens > 0])
         announce("partition", part, "max-abs", err)
@@ -204,17 +221,25 @@ def test_gqa_equals_mha_with_repeated_kv():
     assert np.max(np.abs(out_m.cpu().numpy() - out_g)) <= TOL["bf16"]
 
 
-def test_bf16_output_within_one_ulp():
+@pytest.mark.parametrize("G", [1, 8])
+def test_bf16_output_within_one_ulp(G):
+    """bf16 output mode: every element within one bf16 ulp of the oracle's
+    value rounded to bf16 (nearest even); per-head (G = 1) and grouped
+    (G = 8) kernels, single pass and split-K."""
     need_gpu()
-    w = workloads.make(2, S=4, H=4, Hkv=4, len_lo=100, len_hi=900, n_pad=0)
-    announce("bf16 out")
+    from tests.gpu_util import bf16_rne, bf16_ulp
+    w = workloads.make(2, S=4, H=4 * G, Hkv=4, len_lo=100, len_hi=900, n_pad=0)
+    announce("bf16 out", "G", G)
     dw = M.setup(w, write_step=True)
     st = build_state(w)
     kc, vc = build_pool(w, st, include_step=True)
-    ref = A.decode_ref(w.query, kc, vc, st.block_tables, w.context_lens, w.scale, w.bs, "bf16")
-    got = _decode(dw, 512, out_dtype=torch.bfloat16)
-    ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
-    assert np.all(np.abs(got - ref) <= ulp + 2e-3)
+    ref = bf16_rne(A.decode_ref(w.query, kc, vc, st.block_tables, w.context_lens, w.scale, w.bs,
+                                "bf16"))
+    for part in (0, 512):
+        got = _decode(dw, part, out_dtype=torch.bfloat16)
+        excess = np.abs(got - ref) / bf16_ulp(ref)
+        announce("partition", part, "max error in ulps", float(excess.max()))
+        assert np.all(excess <= 1.0), (part, np.unravel_index(np.argmax(excess), excess.shape))
 
 
 @pytest.mark.parametrize("G", [1, 8])

@@ -41,8 +41,10 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return (r >> np.uint32(16)).astype(np.uint16)
 
 
-def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+def _normal(rng: np.random.Generator, shape, dtype: str, std: float = 1.0) -> np.ndarray:
     x = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x = x * np.float32(std)
     return x if dtype == F32 else f32_to_bf16_bits(x)
 
 
@@ -84,6 +86,7 @@ class Workload:
     query_start_loc: Optional[np.ndarray] = None  # int32 [S+1] packed offsets (prefill)
     prefix_len: int = 0       # shared prefix length (all sequences share it), 0 = none
     partition_size: int = 0   # split-K partition size named by the workload (0 = none)
+    v_std: float = 1.0        # V drawn from N(0, v_std^2) (a power of two keeps bf16 exact)
     notes: Dict[str, object] = field(default_factory=dict)
     _query: Optional[np.ndarray] = field(default=None, repr=False)
 
@@ -125,7 +128,8 @@ class Workload:
             a, b = c * CHUNK, (c + 1) * CHUNK
             shape = (CHUNK, self.Hkv, self.D)
             k = _normal(np.random.default_rng([self.seed, _TAG_K, idx, c]), shape, self.dtype)
-            v = _normal(np.random.default_rng([self.seed, _TAG_V, idx, c]), shape, self.dtype)
+            v = _normal(np.random.default_rng([self.seed, _TAG_V, idx, c]), shape, self.dtype,
+                        self.v_std)
             x0, x1 = max(a, lo), min(b, hi)
             K[x0 - lo:x1 - lo] = k[x0 - a:x1 - a]
             V[x0 - lo:x1 - lo] = v[x0 - a:x1 - a]
@@ -249,7 +253,8 @@ def _build_decode(cfg, seed, sp) -> Workload:
                     S=S, H=sp["H"], Hkv=sp["Hkv"], D=sp["D"], bs=sp["bs"], NB=NB,
                     context_lens=lens, free_order=free_order, query_shape=(S, sp["H"], sp["D"]),
                     row_seq=row_seq, row_pos=row_pos, pad_k=pad_k, pad_v=pad_v,
-                    partition_size=int(sp.get("partition_size", 0)))
+                    partition_size=int(sp.get("partition_size", 0)),
+                    v_std=float(sp.get("v_std", 1.0)))
 
 
 def _build_shared(cfg, seed, sp) -> Workload:
@@ -301,7 +306,7 @@ def _build_shared(cfg, seed, sp) -> Workload:
                     S=S, H=H, Hkv=Hkv, D=D, bs=bs, NB=NB, context_lens=lens,
                     free_order=free_order, query_shape=qshape, row_seq=row_seq, row_pos=row_pos,
                     pad_k=empty, pad_v=empty, query_start_loc=q_start, prefix_len=prefix,
-                    notes={"suffix_lens": qlens})
+                    notes={"suffix_lens": qlens}, v_std=float(sp.get("v_std", 1.0)))
 
 
 def _lens_fixed(rng, S, sp):
