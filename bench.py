@@ -7,19 +7,27 @@ One step = one pass of the whole path over one batch of the workload:
                      attention (split-K partitions + reduce, or one pass);
   prefill workloads: the cache write of the packed new rows, then causal
                      packed prefill over the paged cache.
-Default workload: the 7B-like MHA decode layer (64 sequences, 32 heads,
-head size 128, bf16, block size 16, context lengths U[200, 2048], 71 write
-rows of which 7 are padding) over head-major (HND) pools.  Inputs are seeded synthetic data already
-resident in device memory when the timed region starts.
+Default workload: long-context split-K decode (8 sequences of 131,072 tokens,
+64 query / 8 kv heads, head size 128, bf16, block size 16) in partitions of
+512 tokens reduced by max/sum rescaling, over head-major (HND) pools.  Inputs
+are seeded synthetic data already resident in device memory when the timed
+region starts.
+
+Timing: every timed step is preceded, outside its events, by a 512 MiB write
+to a scratch buffer, so no K/V line of the previous step is still in the
+GPU's memory-side cache; HIP events recorded on the stream the kernels run on
+bracket each kernel.  ms_per_step is the mean event-timed step (write +
+attention, flush excluded); medians, minima and 90th percentiles are listed
+per kernel.
 
 --kv fp8 runs a workload over FP8 (E4M3) pools: the cache write quantises,
 decode and prefill read one byte per element.
 
 Prints ONE JSON line.  `value` = algorithmic KV bytes read per step / step
 time (GB/s) for decode, algorithmic flops / step time (TFLOP/s) for prefill.
-`roofline` covers the dominant kernel, timed with HIP events recorded on the
-stream the kernels run on.  `cpu_baseline` is the fp64 oracle timed on a
-bounded sample of the same workload on the host.
+`roofline` covers the dominant kernel (also against the streaming-read
+ceiling measured in the same run); `cpu_baseline` is the fp64 oracle timed on
+a bounded sample of the same workload over a pool of host processes.
 """
 from __future__ import annotations
 
@@ -48,6 +56,8 @@ KERNEL_SOURCES = {
     "decode_group_fp8": ["decode_group_fp8.hip", "decode_common.h", "kernel_common.h"],
     "prefill": ["prefill.hip", "kernel_common.h"],
 }
+FLUSH_BYTES = 512 << 20      # > the 256 MB memory-side cache (MALL)
+PROBE_BYTES = 4 << 30        # streaming-read ceiling buffer
 
 
 def decode_kernel_kind(w, fp8: bool = False) -> str:
@@ -70,7 +80,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=-1,
                     help="untimed warm-up steps; -1 (default): as many as fill 0.3 s (at least 5), "
                          "so clocks have settled before the timed steps")
-    ap.add_argument("--config", default="2", help="workload: 1, 2, 3, 4, 5a, 5b, 5c")
+    ap.add_argument("--config", default="4", help="workload: 1, 2, 3, 4, 5a, 5b, 5c (default 4)")
     ap.add_argument("--layout", choices=["nhd", "hnd"], default="hnd",
                     help="pool layout: hnd (head-major, default: a kv head's block is one "
                          "contiguous run) or nhd")
@@ -80,10 +90,17 @@ def parse():
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
                     help="keep the workload's cache type, or FP8 (E4M3) pools written by the "
                          "quantising cache write")
-    ap.add_argument("--partition", type=int, default=-1,
-                    help="decode partition size (-1 auto, 0 single pass)")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="decode partition size: the workload's own when it names one (512 for "
+                         "the long-context workload), else -1 = the library's choice; 0 = single pass")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the 512 MiB scratch write before each timed step")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="CPU work budget of the oracle baseline sample")
+                    help="wall-time budget of the oracle baseline sample")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle baseline processes (0: the host cores this process may use, at "
+                         "most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -119,6 +136,14 @@ def traffic_from_profile(workload: str, kind: str):
     return float(val.group(1))
 
 
+def stats_us(xs_ms):
+    """mean / median / min / p90 of a list of millisecond timings, in us."""
+    import numpy as np
+    a = np.asarray(xs_ms, np.float64) * 1e3
+    return {"mean": round(float(a.mean()), 3), "median": round(float(np.median(a)), 3),
+            "min": round(float(a.min()), 3), "p90": round(float(np.percentile(a, 90)), 3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,19 +152,33 @@ def main():
         sys.exit(2)
 
     import numpy as np
-    import torch
 
     import workloads
-    import paged_kv_cache_134_amd as P
-    from paged_kv_cache_134_amd import metadata as M
 
     cfg = args.config if not args.config.isdigit() else int(args.config)
     w = workloads.make(cfg)
-    layout = P.NHD if args.layout == "nhd" else P.HND
     fp8 = args.kv == "fp8"
     if fp8 and w.dtype == "f32":
         raise SystemExit("--kv fp8 needs a bf16 workload")
     ks, vs = workloads.FP8_K_SCALE, workloads.FP8_V_SCALE
+    unit = "GB/s" if w.kind == "decode" else "TFLOP/s"
+
+    # The oracle baseline runs first, in worker processes forked before this
+    # process touches the GPU (the workers use NumPy only).
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(w, args.cpu_seconds, unit, (ks, vs) if fp8 else None,
+                           args.cpu_workers)
+        log(f"[bench] oracle baseline took {time.time() - t0:.1f}s: {cpu['value']} {unit} "
+            f"on {cpu['cores']} processes")
+
+    import torch
+
+    import paged_kv_cache_134_amd as P
+    from paged_kv_cache_134_amd import metadata as M
+
+    layout = P.NHD if args.layout == "nhd" else P.HND
     torch.cuda.set_device(0)
     t0 = time.time()
     dw = (M.setup(w, layout=layout, kv_dtype="e4m3", k_scale=ks, v_scale=vs) if fp8
@@ -153,43 +192,14 @@ def main():
     lens = w.context_lens.astype(np.int64)
     kv_bytes = int(lens.sum()) * Hkv * D * 2 * eb
     out = torch.empty(w.query_shape, dtype=torch.float32, device="cuda")
-    kinds = []
+    kv_code = P.PA_FP8_E4M3 if fp8 else P.KV_DTYPE[w.dtype]
+    ps_requested = args.partition if args.partition is not None else (
+        w.partition_size if w.partition_size > 0 else -1)
 
-    cascade = None
-    if args.cascade:
-        if w.kind != "decode" or w.prefix_len < w.bs:
-            raise SystemExit("--cascade needs a decode workload with a shared prefix (5a)")
-        common = (w.prefix_len // w.bs) * w.bs  # the fully shared blocks
-        # unique bytes the method must read: the common blocks once, then each
-        # sequence's own tokens
-        unique = (common + int((lens - common).sum())) * Hkv * D * 2 * eb
-        cascade = {"common_prefix_len": common, "unique_kv_bytes_per_step": unique}
-        ps = args.partition if args.partition >= 0 else -1
-        ws = torch.empty(P.pa_decode_cascade_workspace_size(S, H, D, dw.max_context_len, common, ps),
-                         dtype=torch.uint8, device="cuda")
-
-        def step(ev):
-            ev[0].record(stream)
-            M.write_step_rows(dw)
-            ev[1].record(stream)
-            if fp8:
-                P.pa_decode_cascade_fp8(out, dw.query, dw.key_cache, dw.value_cache,
-                                        dw.block_tables, dw.context_lens, dw.max_context_len,
-                                        common, w.scale, ks, vs, ws, layout=layout,
-                                        partition_size=ps)
-            else:
-                P.pa_decode_cascade(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
-                                    dw.context_lens, dw.max_context_len, common, w.scale, ws,
-                                    layout=layout, partition_size=ps)
-            ev[2].record(stream)
-            ev[3].record(stream)
-        kinds = ["reshape_and_cache", "decode_cascade", None]
-        dominant = 1
-        work_units = S
-    elif w.kind == "decode":
-        ps = args.partition if args.partition >= 0 else P.pa_decode_auto_partition(
-            S, H, Hkv, P.PA_FP8_E4M3 if fp8 else P.KV_DTYPE[w.dtype],
-            dw.max_context_len, int(lens.sum()))
+    def decode_step_fn(ps):
+        """One decode step at partition size ps (> 0 split-K, 0 single pass):
+        the cache write, the partition kernel (or single pass), the reduce;
+        events between the kernels."""
         ws = None
         if ps > 0:
             ws = torch.empty(P.pa_decode_workspace_size(S, H, D, dw.max_context_len, ps),
@@ -222,6 +232,45 @@ def main():
                             partition_size=0)
                 ev[2].record(stream)
             ev[3].record(stream)
+        return step
+
+    def auto_ps():
+        return P.pa_decode_auto_partition(S, H, Hkv, kv_code, dw.max_context_len, int(lens.sum()))
+
+    cascade = None
+    if args.cascade:
+        if w.kind != "decode" or w.prefix_len < w.bs:
+            raise SystemExit("--cascade needs a decode workload with a shared prefix (5a)")
+        common = (w.prefix_len // w.bs) * w.bs  # the fully shared blocks
+        # unique bytes the method must read: the common blocks once, then each
+        # sequence's own tokens
+        unique = (common + int((lens - common).sum())) * Hkv * D * 2 * eb
+        cascade = {"common_prefix_len": common, "unique_kv_bytes_per_step": unique}
+        ps = ps_requested
+        ws = torch.empty(P.pa_decode_cascade_workspace_size(S, H, D, dw.max_context_len, common, ps),
+                         dtype=torch.uint8, device="cuda")
+
+        def step(ev):
+            ev[0].record(stream)
+            M.write_step_rows(dw)
+            ev[1].record(stream)
+            if fp8:
+                P.pa_decode_cascade_fp8(out, dw.query, dw.key_cache, dw.value_cache,
+                                        dw.block_tables, dw.context_lens, dw.max_context_len,
+                                        common, w.scale, ks, vs, ws, layout=layout,
+                                        partition_size=ps)
+            else:
+                P.pa_decode_cascade(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                    dw.context_lens, dw.max_context_len, common, w.scale, ws,
+                                    layout=layout, partition_size=ps)
+            ev[2].record(stream)
+            ev[3].record(stream)
+        kinds = ["reshape_and_cache", "decode_cascade", None]
+        dominant = 1
+        work_units = S
+    elif w.kind == "decode":
+        ps = ps_requested if ps_requested >= 0 else auto_ps()
+        step = decode_step_fn(ps)
         kinds = ["reshape_and_cache", "decode_partitions" if ps > 0 else "decode_single_pass",
                  "decode_reduce"]
         dominant = 1
@@ -253,30 +302,73 @@ def main():
         dominant = 1
         work_units = int(qlens.sum())
 
+    flush_buf = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
-    if args.warmup >= 0:
-        for _ in range(args.warmup):
-            step(events())
-        torch.cuda.synchronize()
-    else:
-        args.warmup, t_w = 0, time.perf_counter()
-        while args.warmup < 5 or time.perf_counter() - t_w < 0.3:
-            for _ in range(5):
-                step(events())
+    def timed(step_fn, steps, warmup):
+        """warmup untimed steps (-1: enough to fill 0.3 s, at least 5), then
+        `steps` steps, each after a flush of the memory-side cache outside
+        its events; returns (event lists, wall seconds, warmup steps run)."""
+        if warmup >= 0:
+            for _ in range(warmup):
+                step_fn(events())
             torch.cuda.synchronize()
-            args.warmup += 5
-    evs = [events() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for e in evs:
-        step(e)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_per_step = wall * 1e3 / max(args.steps, 1)
-    kern_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
-    kernels_us = {k: round(t * 1e3, 3) for k, t in zip(kinds, kern_ms) if k}
+        else:
+            warmup, t_w = 0, time.perf_counter()
+            while warmup < 5 or time.perf_counter() - t_w < 0.3:
+                for _ in range(5):
+                    step_fn(events())
+                torch.cuda.synchronize()
+                warmup += 5
+        evs = [events() for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i, e in enumerate(evs):
+            if flush_buf is not None:
+                flush_buf.fill_(i & 0xFF)
+            step_fn(e)
+        torch.cuda.synchronize()
+        return evs, time.perf_counter() - t_start, warmup
+
+    evs, wall, args.warmup = timed(step, args.steps, args.warmup)
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    ms_per_step = float(np.mean(step_ms))
+    kern = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(3)]
+    kern_ms = [float(np.mean(k)) for k in kern]
+    kernels_us = {k: stats_us(t) for k, t in zip(kinds, kern) if k}
+
+    # secondary: the library's own partition choice for the same decode step
+    auto_line = None
+    if w.kind == "decode" and not cascade and ps_requested > 0 and auto_ps() != ps_requested:
+        pa_auto = auto_ps()
+        ev2, _, _ = timed(decode_step_fn(pa_auto), 20, 10)
+        t2 = float(np.mean([e[0].elapsed_time(e[3]) for e in ev2]))
+        auto_line = {"partition_size": pa_auto, "ms_per_step": round(t2, 5),
+                     "value": round(kv_bytes / (t2 * 1e-3) / 1e9, 3),
+                     "decode_partitions_us": stats_us([e[1].elapsed_time(e[2]) for e in ev2])}
+
+    # streaming-read ceiling: 4 GiB read once per launch with the decode kernels' loads
+    ceiling = None
+    if not args.no_probe and w.kind == "decode":
+        buf = torch.empty(PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        buf.fill_(1)
+        sink = torch.empty(P.pa_stream_read_probe_sink_words(), dtype=torch.int32, device="cuda")
+        pev = []
+        for i in range(13):
+            if flush_buf is not None:
+                flush_buf.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            P.pa_stream_read_probe(buf, sink)
+            b.record(stream)
+            pev.append((a, b))
+        torch.cuda.synchronize()
+        pt = [a.elapsed_time(b) for a, b in pev[3:]]
+        ceiling = {"gbps": round(PROBE_BYTES / (float(np.median(pt)) * 1e-3) / 1e9, 1),
+                   "bytes": PROBE_BYTES, "runs": len(pt), "us": stats_us(pt)}
+        del buf
 
     # sampled parity of the last step's output against the oracle's plain definition
     # (FP8 pools: the oracle's codes of the same rows, read back times the scales)
@@ -285,17 +377,19 @@ def main():
     got = out.cpu().numpy()
     errs = []
     sample_seqs = sorted({0, S // 2, S - 1}) if w.kind == "decode" else sorted({0, S - 1})
+    sample_heads = sorted({0, H - 1})
+    qf = A.bits_to_f64(w.query, w.dtype)
     for s in sample_seqs:
         K, V = w.kv(s)
-        if fp8:
-            Kf = F8.dequantize(F8.quantize(K, w.dtype, ks), ks)
-            Vf = F8.dequantize(F8.quantize(V, w.dtype, vs), vs)
-        else:
-            Kf, Vf = A.bits_to_f64(K, w.dtype), A.bits_to_f64(V, w.dtype)
-        qf = A.bits_to_f64(w.query, w.dtype)
-        for h in sorted({0, H - 1}):
+        for h in sample_heads:
+            g = h // w.G
+            if fp8:
+                Kf = F8.dequantize(F8.quantize(K[:, g], w.dtype, ks), ks)
+                Vf = F8.dequantize(F8.quantize(V[:, g], w.dtype, vs), vs)
+            else:
+                Kf, Vf = A.bits_to_f64(K[:, g], w.dtype), A.bits_to_f64(V[:, g], w.dtype)
             if w.kind == "decode":
-                ref, _ = A.attention_dense(qf[s, h], Kf[:, h // w.G], Vf[:, h // w.G], w.scale)
+                ref, _ = A.attention_dense(qf[s, h], Kf, Vf, w.scale)
                 errs.append(float(np.max(np.abs(got[s, h] - ref))))
             else:
                 n = int(w.query_lens[s])
@@ -303,28 +397,27 @@ def main():
                 for j in sorted({0, n // 2, n - 1}):
                     a = L - n + j
                     r = int(w.query_start_loc[s]) + j
-                    ref, _ = A.attention_dense(qf[r, h], Kf[:a + 1, h // w.G], Vf[:a + 1, h // w.G],
-                                               w.scale)
+                    ref, _ = A.attention_dense(qf[r, h], Kf[:a + 1], Vf[:a + 1], w.scale)
                     errs.append(float(np.max(np.abs(got[r, h] - ref))))
     tol = 1e-5 if w.dtype == "f32" else 2e-3
     parity = {"max_abs": max(errs), "tolerance": tol, "ok": max(errs) <= tol,
-              "sampled": f"sequences {sample_seqs}, heads {sorted({0, H - 1})}"}
+              "sampled": f"sequences {sample_seqs}, heads {sample_heads}"}
 
+    dom_ms = kern_ms[dominant]
     if w.kind == "decode":
         value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        dom_ms = kern_ms[dominant]
         # the cascade's roofline counts the bytes it must read (common blocks
         # once); the value keeps the logical KV bytes of the plain method
         achieved = (cascade["unique_kv_bytes_per_step"] if cascade else kv_bytes) / (dom_ms * 1e-3) / 1e9
         kind_src = decode_kernel_kind(w, fp8)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        if ceiling:
+            roof["stream_ceiling_gbps"] = ceiling["gbps"]
+            roof["frac_stream_ceiling"] = round(achieved / ceiling["gbps"], 4)
         alg = {"kv_bytes_per_step": kv_bytes}
     else:
         value = flops / (ms_per_step * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        dom_ms = kern_ms[dominant]
         achieved = flops / (dom_ms * 1e-3) / 1e12
         kind_src = "prefill"
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
@@ -332,11 +425,11 @@ def main():
         alg = {"flops_per_step": flops, "causal_pairs_per_head": pairs}
     roof["kernel"] = kinds[dominant]
     prof_name = w.name + ("-e4m3" if fp8 else "")
+    if w.kind == "decode" and not cascade and ps and ps != w.partition_size and w.partition_size:
+        prof_name += f"-p{ps}"
     roof["traffic"] = traffic_from_profile(prof_name, kind_src)
     roof["kernel_source_sha"] = source_sha(kind_src)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds, unit,
-                                                         (ks, vs) if fp8 else None)
     pcache = prefix_cache_probe(w, P) if w.prefix_len >= w.bs else None
 
     line = {
@@ -352,8 +445,13 @@ def main():
                    **({"path": "cascade", **cascade} if cascade else {})},
         "tokens_per_s": round(work_units / (ms_per_step * 1e-3), 1),
         "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4) if unit == "GB/s" else None,
+        "step_us": stats_us(step_ms),
+        "wall_ms_per_step_with_flush": round(wall * 1e3 / max(args.steps, 1), 5),
+        "mall_flush_bytes": 0 if flush_buf is None else FLUSH_BYTES,
         "kernels_us": kernels_us,
         **alg,
+        **({"auto_partition": auto_line} if auto_line else {}),
+        **({"stream_read_ceiling": ceiling} if ceiling else {}),
         "parity": parity,
         **({"prefix_cache": pcache} if pcache else {}),
         "roofline": roof,
@@ -381,64 +479,100 @@ def prefix_cache_probe(w, P):
             "host_us_per_sequence": round(us, 2)}
 
 
-def cpu_baseline(w, budget_s: float, unit: str, fp8_scales=None):
-    """The fp64 oracle on a bounded sample of the workload, one host thread.
+# ------------------------------------------------------------ oracle baseline
+# State shared with the forked workers (set before the pool is created).
+_CPU = {}
 
-    The oracle's pool is built untimed.  Timed: the oracle cache write of the
-    step's rows (charged pro rata to the sampled sequences) plus the oracle
-    decode / prefill of whole sequences taken in order until the CPU budget
-    is spent.  Reported in the metric's unit over the sample's own work.
-    fp8_scales (k_scale, v_scale): FP8 pools, quantising write."""
+
+def _cpu_item(s, g):
+    """The oracle on one (sequence, kv head) of the workload: decode of the G
+    query heads that share kv head g, or prefill of the sequence's rows for
+    them; returns the item's algorithmic work (KV bytes, or flops)."""
     import numpy as np
+    from oracle import attention as A
+    c = _CPU
+    w, st, kc, vc = c["w"], c["st"], c["kc"], c["vc"]
+    G, L = w.G, int(w.context_lens[s])
+    kw = dict(kv_dtype=c["kv"], k_scale=c["ks"], v_scale=c["vs"])
+    kcg, vcg = kc[:, :, g:g + 1], vc[:, :, g:g + 1]  # NHD pools: kv head g alone
+    if w.kind == "decode":
+        A.decode_ref(w.query[s:s + 1, g * G:(g + 1) * G], kcg, vcg, st.block_tables[s:s + 1],
+                     w.context_lens[s:s + 1], w.scale, w.bs, w.dtype, **kw)
+        return float(L) * w.D * 2 * c["eb"]
+    a, b = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+    A.prefill_ref(w.query[a:b, g * G:(g + 1) * G], kcg, vcg, st.block_tables[s:s + 1],
+                  np.array([0, b - a]), w.context_lens[s:s + 1], w.scale, w.bs, w.dtype, **kw)
+    n = b - a
+    return 4.0 * w.D * G * (n * (L - n) + n * (n + 1) / 2)
+
+
+def _cpu_worker(k):
+    """Worker k takes items k, k + W, k + 2W, ... of the item list (passing
+    over it again while its budget lasts); returns (work, items, seconds)."""
     from threadpoolctl import threadpool_limits
+    c = _CPU
+    items, W, budget = c["items"], c["workers"], c["budget"]
+    work, n, t0 = 0.0, 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        i = k
+        while time.perf_counter() - t0 < budget and i < 64 * len(items):
+            work += _cpu_item(*items[i % len(items)])
+            n += 1
+            i += W
+    return work, n, time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s: float, unit: str, fp8_scales=None, workers: int = 0):
+    """The fp64 oracle on a bounded sample of the workload over a pool of
+    host processes (forked, one BLAS thread each).
+
+    Untimed: the oracle's block tables and its pool after set-up.  Timed: the
+    oracle cache write of the step's rows (one process; charged pro rata to
+    the sample) plus, in parallel, the oracle decode / prefill of (sequence,
+    kv head) items taken sequence by sequence, round-robin over the
+    processes, until each has spent the budget.  Reported in the metric's
+    unit: the sample's algorithmic work over the pool's wall time."""
+    import multiprocessing as mp
+
+    import numpy as np
 
     from oracle import attention as A
     from oracle.state import build_pool, build_state
 
+    cores = len(os.sched_getaffinity(0))
+    W = workers if workers > 0 else min(cores, 16)
     st = build_state(w)
     ks, vs = fp8_scales or (1.0, 1.0)
     kv = "e4m3" if fp8_scales else None
     kc, vc = build_pool(w, st, kv_dtype=kv, k_scale=ks, v_scale=vs)
     K, V = w.new_rows()
-    lens = w.context_lens.astype(np.int64)
-    eb = 1 if fp8_scales else w.elem_bytes
-    done, secs, work = [], 0.0, 0.0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        if fp8_scales:
-            kc, vc = A.write_ref_fp8(kc, vc, K, V, st.step_slots, w.bs, w.dtype, ks, vs)
-        else:
-            kc, vc = A.write_ref(kc, vc, K, V, st.step_slots, w.bs)
-        t_write = time.perf_counter() - t0
-        # whole sequences in order, passing over the batch again while the
-        # budget lasts (a short workload is timed over several passes)
-        order = [s for _ in range(1000) for s in range(w.S)]
-        for s in order:
-            t0 = time.perf_counter()
-            if w.kind == "decode":
-                A.decode_ref(w.query[s:s + 1], kc, vc, st.block_tables[s:s + 1], lens[s:s + 1],
-                             w.scale, w.bs, w.dtype, kv_dtype=kv, k_scale=ks, v_scale=vs)
-                work += float(lens[s]) * w.Hkv * w.D * 2 * eb
-            else:
-                a, b = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
-                A.prefill_ref(w.query[a:b], kc, vc, st.block_tables[s:s + 1],
-                              np.array([0, b - a]), lens[s:s + 1], w.scale, w.bs, w.dtype,
-                              kv_dtype=kv, k_scale=ks, v_scale=vs)
-                n, L = b - a, int(lens[s])
-                work += 4.0 * w.D * w.H * (n * (L - n) + n * (n + 1) / 2)
-            secs += time.perf_counter() - t0
-            done.append(s)
-            if secs >= budget_s:
-                break
-    secs += t_write * len(done) / w.S
+    t0 = time.perf_counter()
+    if fp8_scales:
+        kc, vc = A.write_ref_fp8(kc, vc, K, V, st.step_slots, w.bs, w.dtype, ks, vs)
+    else:
+        kc, vc = A.write_ref(kc, vc, K, V, st.step_slots, w.bs)
+    t_write = time.perf_counter() - t0
+    items = [(s, g) for s in range(w.S) for g in range(w.Hkv)]
+    _CPU.update(w=w, st=st, kc=kc, vc=vc, kv=kv, ks=ks, vs=vs,
+                eb=1 if fp8_scales else w.elem_bytes, items=items, workers=W, budget=budget_s)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(W) as pool:
+        res = pool.map(_cpu_worker, range(W))
+    wall = time.perf_counter() - t0
+    _CPU.clear()
+    work = sum(r[0] for r in res)
+    done = sum(r[1] for r in res)
+    # the step's write, charged for the fraction of the batch the sample covers
+    frac = done / len(items)
+    secs = wall + t_write * frac
     value = work / secs / (1e9 if unit == "GB/s" else 1e12)
-    passes = len(done) / w.S
-    what = (f"{len(done)} of {w.S} sequences" if len(done) < w.S
-            else f"{passes:.2f} passes over the {w.S} sequences")
-    return {"value": round(value, 6), "unit": unit, "cores": 1, "kind": "oracle",
-            "seconds": round(secs, 2),
-            "sample": f"{what} of {w.name} (all heads): oracle {w.kind} of those sequences + "
-                      f"their share of the oracle write of the step rows; pool built untimed"}
+    what = (f"{done} of {len(items)} (sequence, kv head) items" if done < len(items)
+            else f"{frac:.2f} passes over the {len(items)} (sequence, kv head) items")
+    return {"value": round(value, 6), "unit": unit, "cores": W, "kind": "oracle",
+            "host_cpus_visible": cores, "seconds": round(secs, 2),
+            "sample": f"{what} of {w.name}: oracle {w.kind} of each kv head's query heads over "
+                      f"the paged pool, {W} processes with one BLAS thread each, plus the oracle "
+                      f"write of the step rows pro rata; pool built untimed"}
 
 
 if __name__ == "__main__":
