@@ -222,6 +222,33 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_static_scratch -- pa_decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  No workspace argument: split-K
+ * partials, their (max, sum) records and the dispatch list live in a
+ * library-owned array of PA_STATIC_SCRATCH_BYTES (96 MiB) on each GPU, held
+ * from when the library's code is loaded on that GPU until the process
+ * ends; the call allocates nothing.  Arguments, result, partition policy
+ * and errors are those of pa_decode (16-bit and fp32 caches); additionally,
+ * a shape whose split-K workspace at the resolved partition size
+ * (pa_decode_workspace_size) exceeds PA_STATIC_SCRATCH_BYTES returns
+ * PA_ERR_WORKSPACE_TOO_SMALL before any device call.  Every call on one GPU
+ * uses that GPU's one array: calls ordered on one stream are safe, calls
+ * that overlap in time on one GPU (other streams, other threads) race and
+ * give undefined results.  Nothing needs clearing between calls: every byte
+ * a call reads from the array it has written first.
+ */
+#define PA_STATIC_SCRATCH_BYTES (96u << 20)
+pa_status pa_decode_static_scratch(void* out, pa_dtype out_dtype, const void* query,
+                                   const void* key_cache, const void* value_cache,
+                                   pa_dtype kv_dtype, pa_layout layout,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t max_context_len,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                   float scale, int32_t partition_size, void* stream);
+
+/*
  * pa_decode_fp8 -- pa_decode over FP8 (E4M3) pools written by
  * pa_reshape_and_cache_fp8: the cached key t reads back as K_t = value(code)
  * * k_scale and the value as V_t = value(code) * v_scale ([vllm] §6.3), so

@@ -49,7 +49,7 @@ EXPORTED = [
     "pa_check_metadata", "pa_pool_create", "pa_pool_destroy", "pa_pool_add_seq", "pa_pool_fork",
     "pa_pool_append", "pa_pool_free_seq", "pa_pool_block_table", "pa_pool_seq_len",
     "pa_pool_num_free", "pa_pool_refcount", "pa_pool_add_seq_cached", "pa_pool_num_cached",
-    "pa_stream_read_probe_sink_words", "pa_stream_read_probe",
+    "pa_stream_read_probe_sink_words", "pa_stream_read_probe", "pa_decode_static_scratch",
 ]
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -102,7 +102,10 @@ _sig = {
     "pa_pool_refcount": (_i32, [_vp, _i32]),
     "pa_stream_read_probe_sink_words": (_i32, []),
     "pa_stream_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
+    "pa_decode_static_scratch": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
 }
+PA_STATIC_SCRATCH_BYTES = 96 << 20  # the static split-K workspace of pa_decode_static_scratch
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
     _fn.restype = _res
@@ -281,6 +284,29 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, ma
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, H, hkv, d, bs,
         nb, float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_decode_static_scratch(out, query, key_cache, value_cache, block_tables, context_lens,
+                             max_context_len: int, scale: float, layout: int = NHD,
+                             partition_size: int = -1, stream=None) -> None:
+    """pa_decode without a workspace argument (for callers that cannot
+    allocate): the split-K workspace is the library's static per-GPU array
+    of PA_STATIC_SCRATCH_BYTES; calls overlapping on one GPU race."""
+    torch = _torch()
+    nb, bs, hkv, d = _geom(key_cache, layout)
+    S, H, D = query.shape
+    if D != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_seqs, num_heads, head_size]")
+    if query.dtype != key_cache.dtype:
+        raise TypeError("query dtype must equal the cache dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables [S, max_blocks] and context_lens [S] required")
+    _check("pa_decode_static_scratch", _lib.pa_decode_static_scratch(
+        _dev(out, "out"), _dtype_code(out), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dtype_code(key_cache), layout,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, H, hkv, d, bs,
+        nb, float(scale), int(partition_size), _stream(stream)))
 
 
 def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens,
