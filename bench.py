@@ -13,10 +13,12 @@ Default workload: long-context split-K decode (8 sequences of 131,072 tokens,
 are seeded synthetic data already resident in device memory when the timed
 region starts.
 
-Timing: every timed step is preceded, outside its events, by a 512 MiB write
-to a scratch buffer, so no K/V line of the previous step is still in the
-GPU's memory-side cache; HIP events recorded on the stream the kernels run on
-bracket each kernel.  ms_per_step is the mean event-timed step (write +
+Timing: every timed step is preceded, outside its events, by a read of a
+512 MiB scratch buffer, so no K/V line of the previous step is still in the
+GPU's 256 MB memory-side cache (a read, not a write: a written buffer would
+leave dirty lines whose write-back then lands inside the next step -- about
+20 us on the long-context step); HIP events recorded on the stream the
+kernels run on bracket each kernel.  ms_per_step is the mean event-timed step (write +
 attention, flush excluded); medians, minima and 90th percentiles are listed
 per kernel.
 
@@ -93,8 +95,9 @@ def parse():
     ap.add_argument("--partition", type=int, default=None,
                     help="decode partition size: the workload's own when it names one (512 for "
                          "the long-context workload), else -1 = the library's choice; 0 = single pass")
-    ap.add_argument("--no-flush", action="store_true",
-                    help="skip the 512 MiB scratch write before each timed step")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="before each timed step, outside its events: write (or read) a 512 MiB "
+                         "scratch buffer, or nothing")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle baseline sample")
@@ -302,7 +305,17 @@ def main():
         dominant = 1
         work_units = int(qlens.sum())
 
-    flush_buf = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flush_buf = None
+    if args.flush != "none":
+        flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+
+    def flush(i):
+        if flush_buf is None:
+            return
+        if args.flush == "write":
+            flush_buf.fill_(i & 0xFF)
+        else:
+            flush_buf.sum()
 
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -326,8 +339,7 @@ def main():
         torch.cuda.synchronize()
         t_start = time.perf_counter()
         for i, e in enumerate(evs):
-            if flush_buf is not None:
-                flush_buf.fill_(i & 0xFF)
+            flush(i)
             step_fn(e)
         torch.cuda.synchronize()
         return evs, time.perf_counter() - t_start, warmup
@@ -358,8 +370,7 @@ def main():
         sink = torch.empty(P.pa_stream_read_probe_sink_words(), dtype=torch.int32, device="cuda")
         pev = []
         for i in range(13):
-            if flush_buf is not None:
-                flush_buf.fill_(i & 0xFF)
+            flush(i)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             P.pa_stream_read_probe(buf, sink)
@@ -448,6 +459,7 @@ def main():
         "step_us": stats_us(step_ms),
         "wall_ms_per_step_with_flush": round(wall * 1e3 / max(args.steps, 1), 5),
         "mall_flush_bytes": 0 if flush_buf is None else FLUSH_BYTES,
+        "mall_flush": args.flush,
         "kernels_us": kernels_us,
         **alg,
         **({"auto_partition": auto_line} if auto_line else {}),

@@ -56,8 +56,11 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   }
   if (single_partition(p, L)) return;
   const int np = p.part_base + (L > p.key_begin ? (L - p.key_begin + p.partition_size - 1) / p.partition_size : 0);
-  const float* ml = p.part_ml + sh * p.max_partitions * 2;
-  const float* po = p.part_out + sh * p.max_partitions * D + lane * CPL;
+  // partial k of this row: record (s, k, h), num_heads records after k - 1
+  const int64_t r0 = part_record(p, s, 0, (int)(sh - (int64_t)s * p.num_heads));
+  const float* ml = p.part_ml + 2 * r0;
+  const float* po = p.part_out + r0 * D + lane * CPL;
+  const int64_t mls = 2 * (int64_t)p.num_heads, pos = (int64_t)p.num_heads * D;
 
   float o[CPL], lsum = 0.f;
 #pragma unroll
@@ -69,10 +72,10 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int kk = min(k, np - 1);  // (repeats of the last partial are not used)
-      mv[k] = ml[2 * kk];
-      lv[k] = ml[2 * kk + 1];
+      mv[k] = ml[kk * mls];
+      lv[k] = ml[kk * mls + 1];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) ov[k][c] = po[(int64_t)kk * D + c];
+      for (int c = 0; c < CPL; ++c) ov[k][c] = po[kk * pos + c];
     }
     float M = mv[0];
 #pragma unroll
@@ -93,17 +96,17 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   }
 
   float M = -INFINITY;
-  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[2 * i]);
+  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[i * mls]);
   M = wave_max(M);
   int i = 0;
   for (; i + 8 <= np; i += 8) {
     float mv[8], lv[8], ov[8][CPL];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      mv[k] = ml[2 * (i + k)];
-      lv[k] = ml[2 * (i + k) + 1];
+      mv[k] = ml[(i + k) * mls];
+      lv[k] = ml[(i + k) * mls + 1];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) ov[k][c] = po[(int64_t)(i + k) * D + c];
+      for (int c = 0; c < CPL; ++c) ov[k][c] = po[(i + k) * pos + c];
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -114,10 +117,10 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
     }
   }
   for (; i < np; ++i) {
-    const float a = exp2_diff(ml[2 * i], M);
-    lsum += a * ml[2 * i + 1];
+    const float a = exp2_diff(ml[i * mls], M);
+    lsum += a * ml[i * mls + 1];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) o[c] += a * po[(int64_t)i * D + c];
+    for (int c = 0; c < CPL; ++c) o[c] += a * po[i * pos + c];
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
@@ -149,11 +152,13 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_wide_kernel(cons
   }
   if (single_partition(p, L)) return;
   const int np = p.part_base + (L > p.key_begin ? (L - p.key_begin + p.partition_size - 1) / p.partition_size : 0);
-  const float* ml = p.part_ml + sh * p.max_partitions * 2;
-  const float* po = p.part_out + sh * p.max_partitions * D + lane * CPL;
+  const int64_t r0 = part_record(p, s, 0, (int)(sh - (int64_t)s * p.num_heads));
+  const float* ml = p.part_ml + 2 * r0;
+  const float* po = p.part_out + r0 * D + lane * CPL;
+  const int64_t mls = 2 * (int64_t)p.num_heads, pos = (int64_t)p.num_heads * D;
 
   float M = -INFINITY;
-  for (int i = threadIdx.x; i < np; i += kReduceThreads) M = fmaxf(M, ml[2 * i]);
+  for (int i = threadIdx.x; i < np; i += kReduceThreads) M = fmaxf(M, ml[i * mls]);
   M = wave_max(M);
   if (lane == 0) sMax[wave] = M;
   __syncthreads();
@@ -169,10 +174,10 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_wide_kernel(cons
 #pragma unroll
     for (int k = 0; k < kWideBatch; ++k) {
       const int i = min(i0 + NW * k, np - 1);  // repeats past the end are not used
-      mv[k] = ml[2 * i];
-      lv[k] = ml[2 * i + 1];
+      mv[k] = ml[i * mls];
+      lv[k] = ml[i * mls + 1];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) ov[k][c] = po[(int64_t)i * D + c];
+      for (int c = 0; c < CPL; ++c) ov[k][c] = po[i * pos + c];
     }
 #pragma unroll
     for (int k = 0; k < kWideBatch; ++k) {
@@ -308,7 +313,6 @@ DecodeParams make_params(const DecodeArgs& a) {
   p.num_kv_heads = g.num_kv_heads;
   p.log2_bs = g.block_size > 0 ? __builtin_ctz((unsigned)g.block_size) : 0;
   p.partition_size = a.partition_size;
-  p.run = 1;
   p.max_partitions = a.max_partitions;
   p.key_begin = a.key_begin;
   p.part_base = a.part_base;
@@ -359,25 +363,6 @@ hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
   } else {
     p.items = nullptr;
     p.item_count = nullptr;
-    // Grouped kernels over the grid: a workgroup walks a run of partitions
-    // (whole 64-token chunks each) so that the grid has about as many
-    // workgroups as the library's own partition choice would give; the
-    // partials stay per partition.  On the long-context batch at 512-token
-    // partitions, one workgroup per partition pays its start-up (lengths,
-    // table window, first loads) 8 times as often.
-    // (16-bit grouped kernel: its partition merge defers the partials' stores
-    // behind the chunk in flight; the FP8 kernel, two tiles in flight per
-    // wave, measured slower with runs than with a workgroup per partition)
-    if (group && a.kv_dtype != PA_FP8_E4M3 && a.partition_size > 0 &&
-        a.partition_size % 64 == 0) {
-      const int32_t span = a.max_context_len - a.key_begin;
-      const int32_t want = pa_decode_auto_partition(a.num_seqs, a.num_heads, g.num_kv_heads,
-                                                    a.kv_dtype, span, 0);
-      if (want > a.partition_size) {
-        p.run = want / a.partition_size;
-        grid.y = (grid.y + p.run - 1) / p.run;
-      }
-    }
   }
   if (a.kv_dtype == PA_FP8_E4M3)
     return group ? dec::launch_group_fp8(p, a.q_dtype, g.head_size, G, grid, stream)

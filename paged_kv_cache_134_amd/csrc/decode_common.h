@@ -38,7 +38,6 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t log2_bs;
   int32_t partition_size;  // 0 = single pass
-  int32_t run;             // split-K: consecutive partitions per workgroup (16-bit grouped kernel; else 1)
   int32_t max_partitions;  // workspace partitions per (sequence, head)
   int32_t key_begin;       // partitions cover keys [key_begin, L) (0 outside cascades)
   int32_t part_base;       // workspace index of partition 0 (earlier slots hold prefix partials)
@@ -57,8 +56,7 @@ struct DecodeParams {
 // The (sequence, kv head, partition) of this workgroup: from the dispatch
 // list when there is one, else from the (pairs, partitions) grid, partitions
 // taken last-first when last_first (only long contexts have high
-// partitions, so their workgroups start early).  With runs (p.run > 1) the
-// grid's second index counts runs of p.run partitions.  False: nothing to do.
+// partitions, so their workgroups start early).  False: nothing to do.
 __device__ __forceinline__ bool decode_item(const DecodeParams& p, bool last_first, int& s, int& kvh,
                                             int& part) {
   if (p.items) {
@@ -96,20 +94,36 @@ __device__ __forceinline__ bool single_partition(const DecodeParams& p, int L) {
   return !p.all_partial && L <= p.partition_size;
 }
 
-// Writes one (max, sum, unnormalised output) partial, or the final output
-// when the whole context is one partition (the reduce skips those heads).
-__device__ __forceinline__ void emit(const DecodeParams& p, int64_t head, int part, int d, int D,
+// Split-K partials are partition-major: record (s, k, h) -- sequence s,
+// workspace partition k, head h of the sequence -- is row
+// (s * max_partitions + k) * num_heads + h of part_out (D floats) and of
+// part_ml ((max, sum)).  The workgroups of one (sequence, partition) -- the
+// kv heads, dispatched side by side -- thus write one contiguous stretch.
+// (Head-major rows, 512-token partitions apart, wrote the same bytes at
+// large power-of-two strides; on the long-context batch the partition
+// kernel took 807 us with them, 771 us partition-major, 756 us with the
+// stores also non-temporal.)
+__device__ __forceinline__ int64_t part_record(const DecodeParams& p, int s, int k, int h) {
+  return ((int64_t)s * p.max_partitions + k) * p.num_heads + h;
+}
+
+// Writes one (max, sum, unnormalised output) partial of sequence s, head h
+// of the sequence, or the final output when the whole context is one
+// partition (the reduce skips those heads).  The partials are stored
+// non-temporally: the reduce reads them once, after this kernel.
+__device__ __forceinline__ void emit(const DecodeParams& p, int s, int h, int part, int d, int D,
                                      float M, float lsum, float o, bool single) {
   o *= p.v_scale;
   if (p.partition_size > 0 && !single) {
-    const int64_t pi = head * p.max_partitions + p.part_base + part;
-    p.part_out[pi * D + d] = o;
+    const int64_t r = part_record(p, s, p.part_base + part, h);
+    __builtin_nontemporal_store(o, p.part_out + r * D + d);
     if (d == 0) {
-      p.part_ml[2 * pi] = M;
-      p.part_ml[2 * pi + 1] = lsum;
+      p.part_ml[2 * r] = M;
+      p.part_ml[2 * r + 1] = lsum;
     }
   } else {
-    store_out(p.out, head * D + d, lsum > 0.f ? o / lsum : 0.f, p.out_dtype);
+    store_out(p.out, ((int64_t)s * p.num_heads + h) * D + d, lsum > 0.f ? o / lsum : 0.f,
+              p.out_dtype);
   }
 }
 

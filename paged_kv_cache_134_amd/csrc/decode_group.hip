@@ -58,29 +58,24 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
   __shared__ int32_t sResc[kDecodeWaves];          // wave w moved a running max this chunk
   __shared__ float sM[G], sL[G];
   __shared__ int32_t s_bt[kBtWin];                 // block-table window
-  // merged values of a finished partition awaiting their store (slot k *
-  // 256 + tid holds thread tid's k-th value; only that thread reads it)
-  constexpr int NPT = (G * D + kDecodeThreads - 1) / kDecodeThreads;
-  __shared__ float sPend[NPT * kDecodeThreads];
   uint4* sK = sKV;
   uint4* sV = sKV + kChunk * KSTR;
 
-  int s, kvh, item;
-  if (!decode_item(p, true, s, kvh, item)) return;
+  int s, kvh, part;
+  if (!decode_item(p, true, s, kvh, part)) return;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
-  // Tokens [t0, t1): partitions part0 .. part0 + run - 1 (split-K) or the
-  // whole context (single pass).
+  // Tokens [t0, t1): the partition (split-K) or the whole context (single
+  // pass).
   const int L = p.context_lens[s];
   const int P = p.partition_size;
-  int t0 = 0, t1 = L, part0 = 0;
+  int t0 = 0, t1 = L;
   if (P > 0) {
-    part0 = item * p.run;
-    t0 = p.key_begin + part0 * P;
+    t0 = p.key_begin + part * P;
     if (t0 >= L) return;
-    t1 = min(L, t0 + p.run * P);
+    t1 = min(L, t0 + P);
   }
   const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
   if (t1 <= t0) {  // single pass over an empty context (split-K returned above)
@@ -118,15 +113,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
                         (2 * (wave * (kChunk / kDecodeWaves / 2) + half) * RC) * 16 + dl * DPL * 2;
   const char* pp_base = reinterpret_cast<const char*>(&sP[wave * (kChunk / kDecodeWaves / 2) + half][0][0]);
 
-  // A run's partitions are walked starting from a different one in every
-  // workgroup (rotation by the workgroup's grid position) and wrapping
-  // around: workgroups with equal work would otherwise reach their partition
-  // boundaries, where the waves merge and no new loads are issued, all at
-  // the same moment, leaving HBM idle chip-wide each time.
-  const int nparts = P > 0 && p.run > 1 ? (t1 - t0 + P - 1) / P : 1;
-  const int rot = nparts > 1 ? (int)((blockIdx.x + blockIdx.y) % (unsigned)nparts) : 0;
-  const int c_first = t0 + rot * P;  // first chunk walked
-  int wb0 = c_first >> lbs;  // the window holds entries wb0 .. wb0 + kBtWin - 1 (clamped to e_last)
+  int wb0 = t0 >> lbs;  // the window holds entries wb0 .. wb0 + kBtWin - 1 (clamped to e_last)
   auto stage_bt = [&]() {
     for (int i = tid; i < kBtWin; i += kDecodeThreads) s_bt[i] = bt[min(wb0 + i, e_last)];
   };
@@ -153,108 +140,35 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
     }
   };
 
-  // Softmax state of the current partition: reference max and lane sums of
-  // this wave's QK heads, and the lane's PV accumulators (its tokens, all
-  // heads, its columns).
+  // Softmax state: reference max and lane sums of this wave's QK heads, and
+  // the lane's PV accumulators (its tokens, all heads, its columns).
   float m_ref[HPW], l_lane[HPW];
   float acc[G][DPL];
-  auto reset = [&]() {
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      m_ref[hh] = -INFINITY;
-      l_lane[hh] = 0.f;
-    }
+  for (int hh = 0; hh < HPW; ++hh) {
+    m_ref[hh] = -INFINITY;
+    l_lane[hh] = 0.f;
+  }
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-  };
-  // Merge of the partition's state -- halves, then waves (the statistics come
-  // from the QK waves) -- written as partition `part`'s partial, or as the
-  // final rows when the context is a single partition.  The chunk tiles'
-  // LDS holds the waves' accumulators meanwhile; the next chunk's loads
-  // stay in flight in registers.
-  // A boundary inside a run parks its merged values in sPend and writes them
-  // once the chunk already in flight has been staged, just before the next
-  // chunk's loads (write_pending): vector memory operations complete in
-  // order, so stores issued while a chunk is in flight would make that
-  // chunk's staging wait for them too, whereas stores issued ahead of the
-  // loads are done by the time those loads are.
-  int pend_part = -1;  // partition of the values in sPend (-1: none)
-  auto write_pending = [&]() {
-    if (pend_part < 0) return;  // uniform
-    // always a partial (a single-partition context has no boundary)
-#pragma unroll 1
-    for (int k = 0; k < NPT; ++k) {
-      const int i = tid + k * kDecodeThreads;
-      if (i < G * D) {
-        const int h = i / D, d = i % D;
-        const int64_t pi = (head0 + h) * p.max_partitions + p.part_base + pend_part;
-        p.part_out[pi * D + d] = sPend[k * kDecodeThreads + tid] * p.v_scale;
-        if (d == 0) {
-          p.part_ml[2 * pi] = sM[h];
-          p.part_ml[2 * pi + 1] = sL[h];
-        }
-      }
-    }
-    pend_part = -1;
-  };
-  auto flush = [&](int part, bool defer) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const float lt = wave_sum(l_lane[hh]);
-      if (lane == 0) {
-        sM[wave * HPW + hh] = m_ref[hh];
-        sL[wave * HPW + hh] = lt;
-      }
-    }
-    __syncthreads();  // the chunk's last PV reads are done: the tiles are free
-    float* sAcc = reinterpret_cast<float*>(sKV);  // [waves][G][D]
-    if (half == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) sAcc[(wave * G + h) * D + dl * DPL + e] = acc[h][e];
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int k = 0; k < NPT; ++k) {
-      const int i = tid + k * kDecodeThreads;
-      if (i < G * D) {
-        const int h = i / D, d = i % D;
-        float o = 0.f;
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) o += sAcc[(w * G + h) * D + d];
-        if (defer)
-          sPend[k * kDecodeThreads + tid] = o;
-        else
-          emit(p, head0 + h, part, d, D, sM[h], sL[h], o, single);
-      }
-    }
-    if (defer) pend_part = part;
-    reset();
-  };
+    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
 
   // One chunk in flight in registers while the previous one is consumed
   // from LDS.
-  // cn: the chunk walked after c0 (valid when more).
-  auto step = [&](int c0, int cn, bool more, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
-    __syncthreads();  // previous chunk (or merge) fully consumed, window reads included
+  auto step = [&](int c0, bool more, uint4 (&kr)[PPT], uint4 (&vr)[PPT]) {
+    const int cn = c0 + kChunk;
+    __syncthreads();  // previous chunk fully consumed, window reads included
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {  // piece tid + 256 r: row prow + RSTEP r, column pcol
       sK[(prow + RSTEP * r) * KSTR + pcol] = kr[r];
       sV[tid + kDecodeThreads * r] = vr[r];
     }
-    if (more && ((cn >> lbs) < wb0 || (min(cn + kChunk - 1, t1 - 1) >> lbs) - wb0 >= kBtWin)) {  // uniform
+    if (more && (min(cn + kChunk - 1, t1 - 1) >> lbs) - wb0 >= kBtWin) {  // uniform
       wb0 = cn >> lbs;
       stage_bt();
     }
     __syncthreads();
-    write_pending();              // a finished partition's partial, ahead of the next loads
     if (more) fetch(cn, kr, vr);  // next chunk in flight
 
     // ---- QK: lane = token row, this wave's HPW heads
@@ -360,29 +274,42 @@ __global__ __launch_bounds__(kDecodeThreads, (kLdsMinWaves<G, D>)) void decode_l
     }
   };
 
-  reset();
   stage_bt();
   __syncthreads();  // window staged
   uint4 kr[PPT], vr[PPT];
-  fetch(c_first, kr, vr);
-  // chunks from c_first to the end of the range, then from t0 (whole
-  // chunks: partitions are whole chunks when a run has several)
-  const int n_first = (t1 - c_first + kChunk - 1) / kChunk;  // chunks from c_first on
-  const int nchunks = n_first + (c_first - t0) / kChunk;
-  auto chunk_at = [&](int k) { return k < n_first ? c_first + k * kChunk : t0 + (k - n_first) * kChunk; };
-  int part = part0 + rot;
-  for (int k = 0; k < nchunks; ++k) {  // uniform
-    const int c0 = chunk_at(k);
-    if (nparts > 1) {
-      const int pc = part0 + (c0 - t0) / P;
-      if (pc != part) {
-        flush(part, true);
-        part = pc;
-      }
+  fetch(t0, kr, vr);
+  for (int c0 = t0; c0 < t1; c0 += kChunk) step(c0, c0 + kChunk < t1, kr, vr);  // uniform
+
+  // ---- merge of the halves, then of the waves (the statistics come from
+  // the QK waves); the chunk tiles' LDS holds the waves' accumulators
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const float lt = wave_sum(l_lane[hh]);
+    if (lane == 0) {
+      sM[wave * HPW + hh] = m_ref[hh];
+      sL[wave * HPW + hh] = lt;
     }
-    step(c0, chunk_at(k + 1), k + 1 < nchunks, kr, vr);
   }
-  flush(part, false);
+  __syncthreads();  // the last chunk's PV reads are done: the tiles are free
+  float* sAcc = reinterpret_cast<float*>(sKV);  // [waves][G][D]
+  if (half == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sAcc[(wave * G + h) * D + dl * DPL + e] = acc[h][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kDecodeThreads) {
+    const int h = i / D, d = i % D;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) o += sAcc[(w * G + h) * D + d];
+    emit(p, s, kvh * G + h, part, d, D, sM[h], sL[h], o, single);
+  }
 }
 
 template <pa_dtype DT, int D, bool OFF32>

@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
         lsum += a * sL[w][h];
         ov += a * sAcc[(w * G + h) * D + d];
       }
-      emit(p, head0 + h, part, d, D, M, lsum, ov, single);
+      emit(p, s, kvh * G + h, part, d, D, M, lsum, ov, single);
     }
   };
 

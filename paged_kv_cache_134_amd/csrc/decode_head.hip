@@ -217,7 +217,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
   }
   __syncthreads();
 
-  const int64_t head0 = (int64_t)s * p.num_heads + (int64_t)kvh * G;
   for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) {
     const int g = i / D;
     const int d = i % D;
@@ -231,7 +230,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reg_kernel(const Decode
       lsum += a * sm_l[w][g];
       o += a * sm_acc[w][g][d];
     }
-    emit(p, head0 + g, part, d, D, M, lsum, o, single_partition(p, L));
+    emit(p, s, kvh * G + g, part, d, D, M, lsum, o, single_partition(p, L));
   }
 }
 

@@ -62,8 +62,8 @@ struct DecodeArgs {
   float scale;
   int32_t partition_size;  // 0 = single pass, > 0 = split-K
   int32_t max_partitions;  // ceil(max_context_len / partition_size) when split
-  float* part_out;         // [num_seqs, num_heads, max_partitions, head_size]
-  float* part_ml;          // [num_seqs, num_heads, max_partitions, 2] (max, sum)
+  float* part_out;         // [num_seqs, max_partitions, num_heads, head_size]
+  float* part_ml;          // [num_seqs, max_partitions, num_heads, 2] (max, sum)
   int32_t key_begin = 0;   // cascade: partitions cover [key_begin, L) ...
   int32_t part_base = 0;   // ... and start at this workspace partition
   bool all_partial = false;  // cascade: prefix partials exist, never finish a head early

@@ -130,6 +130,22 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
+// e - (the low / high f16 half of h, widened): one mixed-precision FMA each
+// (v_fma_mix_f32 reads an f16 source exactly; the compiler keeps a
+// conversion and a subtraction for the same expression).  Register-only.
+__device__ __forceinline__ float sub_f16_lo(float e, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(e));
+  return r;
+}
+__device__ __forceinline__ float sub_f16_hi(float e, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(e));
+  return r;
+}
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
 // 8 E4M3 codes as floats.
 __device__ __forceinline__ void fp8x8_to_f32(const uint4& v, float* out) {
   const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, false);
@@ -327,12 +343,11 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
   int ti = 0;   // tile count (its parity selects the V-range flag)
   TileRegs tr = fetch(k_lo);
   // V of tile registers -> LDS, transposed to [d][key] in f16 (times
-  // 2^-vsh).  CHECK (bf16 caches): also flag, in sVwide, a finite value too
-  // large for the current shift.
+  // 2^-vsh once a shift is in force: a uniform branch, so the common path
+  // converts only).  CHECK (bf16 caches): also flag, in sVwide, a finite
+  // value too large for the current shift.
   auto stage_v = [&](auto check_tag) {
     constexpr bool CHECK = decltype(check_tag)::value;
-    const uint32_t wide_bits = (uint32_t)min(143 + vsh, 255) << 7;  // |v| >= 2^(16 + vsh)
-    const float vmul = __builtin_ldexpf(1.f, -vsh);
     if (VITEMS == kPrefillThreads || tid < VITEMS) {  // head size 64: half the threads stage no V
       // key group v_kq (keys 4 v_kq .. +3) goes to group slot (v_kq & ~3) +
       // 2 (v_kq & 1) + ((v_kq >> 1) & 1) of the row: in every 16-key slice
@@ -340,50 +355,63 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
       // half-wave contracts per product (groups hf and hf + 2) are 16
       // contiguous bytes
       const int v_slot = ((v_kq & ~3) + 2 * (v_kq & 1) + ((v_kq >> 1) & 1)) * 8;
-      float vmax = 0.f;  // bf16 caches: largest |v| staged (fmaxf skips NaN)
-      float fv[4][8];  // FP8: the 8 columns of each of the 4 keys
-      if constexpr (FP8) {
-  #pragma unroll
-        for (int k = 0; k < 4; ++k) fp8x8_to_f32(tr.v[k], fv[k]);
-      }
-  #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        // columns e, e+1 of keys v_kq*4 .. +3
-        float f0[4], f1[4];
-  #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f0[k] = FP8 ? fv[k][e] : chunk_elem<DT>(tr.v[k], e);
-          f1[k] = FP8 ? fv[k][e + 1] : chunk_elem<DT>(tr.v[k], e + 1);
-          if (kWideCheck && vsh != 0) {  // exact power-of-two scaling
-            f0[k] *= vmul;
-            f1[k] *= vmul;
-          }
-        }
-        const uint2 w0 = make_uint2(pk_f16(f0[0], f0[1]), pk_f16(f0[2], f0[3]));
-        const uint2 w1 = make_uint2(pk_f16(f1[0], f1[1]), pk_f16(f1[2], f1[3]));
-        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e) * VROW + v_slot) = w0;
-        *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e + 1) * VROW + v_slot) = w1;
-        if constexpr (CHECK) {
+      auto put = [&](auto scaled_tag) {
+        constexpr bool SCALED = decltype(scaled_tag)::value;
+        const float vmul = SCALED ? __builtin_ldexpf(1.f, -vsh) : 1.f;
+        float fv[4][8];  // FP8: the 8 columns of each of the 4 keys
+        if constexpr (FP8) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) vmax = fmaxf(vmax, fmaxf(fabsf(f0[k]), fabsf(f1[k])));
+          for (int k = 0; k < 4; ++k) fp8x8_to_f32(tr.v[k], fv[k]);
         }
-      }
-      // The staged (scaled) values must stay below 2^16 in magnitude (f16's
-      // largest finite is 65504; no bf16 value lies in [65504, 65536)).  Only
-      // past that -- or for an infinity, which passes through as itself --
-      // are the thread's raw values looked at one by one for the largest
-      // finite magnitude beyond the range.
-      if (CHECK && vmax >= 65536.f) {
-        uint32_t big = 0;
-        uint32_t raw[16] = {tr.v[0].x, tr.v[0].y, tr.v[0].z, tr.v[0].w, tr.v[1].x, tr.v[1].y,
-                            tr.v[1].z, tr.v[1].w, tr.v[2].x, tr.v[2].y, tr.v[2].z, tr.v[2].w,
-                            tr.v[3].x, tr.v[3].y, tr.v[3].z, tr.v[3].w};
-  #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-          const uint32_t b = (raw[q / 2] >> (16 * (q & 1))) & 0x7FFFu;
-          if (b >= wide_bits && b < 0x7F80u) big = max(big, b);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          // columns e, e+1 of keys v_kq*4 .. +3
+          float f0[4], f1[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            f0[k] = FP8 ? fv[k][e] : chunk_elem<DT>(tr.v[k], e);
+            f1[k] = FP8 ? fv[k][e + 1] : chunk_elem<DT>(tr.v[k], e + 1);
+            if constexpr (SCALED) {  // exact power-of-two scaling
+              f0[k] *= vmul;
+              f1[k] *= vmul;
+            }
+          }
+          const uint2 w0 = make_uint2(pk_f16(f0[0], f0[1]), pk_f16(f0[2], f0[3]));
+          const uint2 w1 = make_uint2(pk_f16(f1[0], f1[1]), pk_f16(f1[2], f1[3]));
+          *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e) * VROW + v_slot) = w0;
+          *reinterpret_cast<uint2*>(sV + (v_dq * 8 + e + 1) * VROW + v_slot) = w1;
         }
-        if (big) atomicMax(&sVwide[ti & 1], (int32_t)big);
+      };
+      if (kWideCheck && vsh != 0)  // uniform
+        put(std::true_type{});
+      else
+        put(std::false_type{});
+      if constexpr (CHECK) {
+        // The staged (scaled) values must stay below 2^16 in magnitude
+        // (f16's largest finite is 65504; no bf16 value lies in [65504,
+        // 65536)), i.e. raw bf16 magnitudes below 2^(16 + vsh).  Magnitudes
+        // order as their bf16 bits with the sign cleared (infinities and
+        // NaN above every finite value), so packed 16-bit maxima of the raw
+        // words find the largest; only past the bound -- or for an infinity
+        // or NaN, which pass through as themselves -- are the thread's
+        // values looked at one by one for the largest finite one.
+        const uint32_t wide_bits = (uint32_t)min(143 + vsh, 255) << 7;  // |v| >= 2^(16 + vsh)
+        const uint32_t raw[16] = {tr.v[0].x, tr.v[0].y, tr.v[0].z, tr.v[0].w, tr.v[1].x, tr.v[1].y,
+                                  tr.v[1].z, tr.v[1].w, tr.v[2].x, tr.v[2].y, tr.v[2].z, tr.v[2].w,
+                                  tr.v[3].x, tr.v[3].y, tr.v[3].z, tr.v[3].w};
+        u16x2_t mx = __builtin_bit_cast(u16x2_t, raw[0] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int q = 1; q < 16; ++q)
+          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, raw[q] & 0x7FFF7FFFu));
+        if (max((uint32_t)mx.x, (uint32_t)mx.y) >= wide_bits) {
+          uint32_t big = 0;
+#pragma unroll
+          for (int q = 0; q < 32; ++q) {
+            const uint32_t b = (raw[q / 2] >> (16 * (q & 1))) & 0x7FFFu;
+            if (b >= wide_bits && b < 0x7F80u) big = max(big, b);
+          }
+          if (big) atomicMax(&sVwide[ti & 1], (int32_t)big);
+        }
       }
     }
   };
@@ -489,7 +517,7 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, nm));
         const uint32_t h2 = pk_f16(e0, e1);
         const f16x2_t hv = __builtin_bit_cast(f16x2_t, h2);
-        const uint32_t l2 = pk_f16(e0 - (float)hv.x, e1 - (float)hv.y);
+        const uint32_t l2 = pk_f16(sub_f16_lo(e0, h2), sub_f16_hi(e1, h2));
         ph[kb][i / 2] = h2;
         pl[kb][i / 2] = l2;
         l = __builtin_amdgcn_fdot2(hv, __builtin_bit_cast(f16x2_t, ones), l, false);
@@ -542,7 +570,7 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
     // partial of (row j, head h, key partition s), without the weights'
     // factor 2^7 and with V's 2^vsh
     if (j < n) {
-      const int64_t pi = ((int64_t)j * p.num_heads + h) * p.max_partitions + s;
+      const int64_t pi = ((int64_t)j * p.max_partitions + s) * p.num_heads + h;  // partition-major
       float* po = p.part_out + pi * D;
       const float vsc = p.v_scale * __builtin_ldexpf(1.f, vsh - (int)kWeightLog2);
 #pragma unroll
