@@ -99,6 +99,9 @@ def parse():
                     help="before each timed step, outside its events: write (or read) a 512 MiB "
                          "scratch buffer, or nothing")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling probe")
+    ap.add_argument("--no-auto-line", action="store_true",
+                    help="skip the secondary run at the library's own partition size (profiles: "
+                         "every dispatch of the kernel is then the timed configuration's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle baseline sample")
     ap.add_argument("--cpu-workers", type=int, default=0,
@@ -307,13 +310,15 @@ def main():
 
     flush_buf = None
     if args.flush != "none":
-        flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        # float32: its sum is one reduction that reads the buffer (an integer
+        # sum would first widen it to int64, a 1 GiB write)
+        flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
 
     def flush(i):
         if flush_buf is None:
             return
         if args.flush == "write":
-            flush_buf.fill_(i & 0xFF)
+            flush_buf.fill_(float(i & 0xFF))
         else:
             flush_buf.sum()
 
@@ -354,7 +359,8 @@ def main():
 
     # secondary: the library's own partition choice for the same decode step
     auto_line = None
-    if w.kind == "decode" and not cascade and ps_requested > 0 and auto_ps() != ps_requested:
+    if (w.kind == "decode" and not cascade and ps_requested > 0 and auto_ps() != ps_requested
+            and not args.no_auto_line):
         pa_auto = auto_ps()
         ev2, _, _ = timed(decode_step_fn(pa_auto), 20, 10)
         t2 = float(np.mean([e[0].elapsed_time(e[3]) for e in ev2]))
