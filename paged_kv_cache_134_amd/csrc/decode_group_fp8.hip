@@ -49,6 +49,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef __fp16 lds_f16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+// gfx950 transposing LDS read: in each group of 16 lanes, lane 4 r + c
+// addresses 4 consecutive 16-bit values of row r (columns 4 c .. 4 c + 3)
+// of a 4 x 16 block, and lane l receives column l of the block (rows 0..3).
+__device__ __forceinline__ f16x4_t lds_read_tr16(const _Float16* p) {
+  return __builtin_bit_cast(
+      f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) lds_f16x4_t*)(p)));
+}
 
 template <pa_dtype DT>
 __device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
@@ -143,9 +152,12 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   const int64_t lane_off = (int64_t)kvh * p.head_stride + q4 * 16;  // bytes
 
   uint4* sV = reinterpret_cast<uint4*>(smem) + wave * kWaveV;
-  // PV A operand: V^T[d = 16 b + tl][token 4 q4 + j], j = 0..3, read from the
-  // wave's f16 rows (row stride VSTR pieces)
-  const _Float16* vh = reinterpret_cast<const _Float16*>(sV) + (4 * q4) * (VSTR * 8) + tl;
+  // PV A operand: V^T[d = 16 b + tl][token 4 q4 + j], j = 0..3, from the
+  // wave's f16 rows (row stride VSTR pieces) by one transposing read per
+  // block: lane tl of quarter q4 addresses row 4 q4 + tl / 4, columns
+  // 16 b + 4 (tl % 4) .. +3
+  const _Float16* vh =
+      reinterpret_cast<const _Float16*>(sV) + (4 * q4 + tl / 4) * (VSTR * 8) + 4 * (tl % 4);
 
   auto block_of = [&](int ts) -> int32_t { return bt[min(ts + tl, t1 - 1) >> lbs]; };
   // K and V pieces of the lane's token in tile ts (rows past the end are
@@ -243,8 +255,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
     f16x4_t a[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a[b][j] = vh[j * (VSTR * 8) + 16 * b];
+      a[b] = lds_read_tr16(vh + 16 * b);
       o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(a[b], pbh, o[b], 0, 0, 0);
     }
 #pragma unroll
