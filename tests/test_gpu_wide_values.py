@@ -158,3 +158,49 @@ def test_prefill_bf16_values_beyond_f16_range(shift):
                 err = float(np.max(np.abs(got[q0 + jrow, h] - ref)))
                 assert err <= tol, (s, h, jrow, err, tol)
     announce("ok")
+
+
+@pytest.mark.parametrize("shift", [17, 40])
+def test_cascade_bf16_values_beyond_f16_range_in_shared_prefix(shift):
+    """A block of the shared prefix holding bf16 V of magnitude 2^shift (past
+    f16's range): the cascade's prefix pass -- the prefill kernel over the
+    common blocks -- switches to V scaled by a power of two, and cascade
+    decode still equals the plain definition over each whole context, to
+    2e-3 relative to the output's magnitude, at every partition mode."""
+    need_gpu()
+    w = workloads.make("5a", S=6, H=16, Hkv=2, prefix=700, suffix_lo=1, suffix_hi=300)
+    announce("cascade V beyond f16 range in the shared prefix", "2^", shift)
+    dw = M.setup(w, layout=P.HND, write_step=True)
+    st = build_state(w)
+    common = (w.prefix_len // w.bs) * w.bs
+    # positions 320..335 lie in the common blocks, which every sequence's
+    # table shares (row 0's slots are every row's there)
+    big = np.arange(320, 336)
+    assert big[-1] < common
+    slots = torch.from_numpy(st.seq_slots[0][big].astype(np.int64)).cuda()
+    blk, off = slots // w.bs, slots % w.bs
+    dw.value_cache[blk, :, off] *= 2.0 ** shift  # exact: exponent shift (HND pool)
+    qf = A.bits_to_f64(w.query, w.dtype)
+    refs = {}
+    for s in range(w.S):
+        K, V = w.kv(s)
+        for h in range(w.H):
+            g = h // w.G
+            Kf, Vf = A.bits_to_f64(K[:, g], w.dtype), A.bits_to_f64(V[:, g], w.dtype)
+            Vf[big] *= 2.0 ** shift
+            refs[s, h], _ = A.attention_dense(qf[s, h], Kf, Vf, w.scale)
+    for part in (-1, 0, 64):
+        out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+        nbytes = P.pa_decode_cascade_workspace_size(w.S, w.H, w.D, dw.max_context_len, common, part)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        P.pa_decode_cascade(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                            dw.context_lens, dw.max_context_len, common, w.scale, ws,
+                            layout=P.HND, partition_size=part)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.all(np.isfinite(got))
+        for (s, h), ref in refs.items():
+            tol = TOL[w.dtype] * max(1.0, float(np.max(np.abs(ref))))
+            err = float(np.max(np.abs(got[s, h] - ref)))
+            assert err <= tol, (part, s, h, err, tol)
+        announce("partition", part, "ok")
