@@ -375,7 +375,11 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0 || a.partition_size <= 0) return hipSuccess;
   const dec::DecodeParams p = dec::make_params(a);
   const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
-  if (a.max_partitions > 8) {  // many partials per row: a workgroup per (sequence, head)
+  // Many partials per row: a workgroup per (sequence, head).  Up to 64 the
+  // one-wave-per-row kernel is faster (shared-prefix cascade, 16 partials:
+  // 161 -> 153 us step; long context at 32 partials); at 256 the row's
+  // batches in one wave would run one after another.
+  if (a.max_partitions > 64) {
     if (pairs > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (a.geom.head_size == 64)
       hipLaunchKernelGGL(dec::decode_reduce_wide_kernel<64>, dim3((unsigned)pairs),
