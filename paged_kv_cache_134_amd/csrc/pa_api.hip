@@ -51,8 +51,8 @@ int64_t partitions_for(int32_t max_context_len, int32_t partition_size) {
 
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Split-K workspace: partial outputs [S, H, parts, D] fp32, partial (max,
-// sum) [S, H, parts, 2] fp32, then the dispatch list of the partition
+// Split-K workspace: partial outputs [S, parts, H, D] fp32, partial (max,
+// sum) [S, parts, H, 2] fp32 (partition-major), then the dispatch list of the partition
 // kernel: a 256-byte header (item count) and one 16-byte item per (sequence,
 // kv head, partition), num_heads bounding num_kv_heads.  Each part starts on
 // a 256-byte boundary.
