@@ -199,8 +199,10 @@ def test_fp8_decode_full_size_sampled(cfg, layout):
     announce("full-size fp8 decode", w.name, layout)
     dw = M.setup(w, layout=lay, write_step=True, kv_dtype="e4m3", k_scale=ks, v_scale=vs)
     st = build_state(w)
-    ps = P.pa_decode_auto_partition(w.S, w.H, w.Hkv, P.PA_FP8_E4M3, dw.max_context_len,
-                                   int(w.context_lens.sum()))
+    # the bench's partition: the workload's own (512 for the long context), else the library's
+    ps = w.partition_size or P.pa_decode_auto_partition(w.S, w.H, w.Hkv, P.PA_FP8_E4M3,
+                                                        dw.max_context_len, int(w.context_lens.sum()))
+    announce("partition", ps)
     ws = torch.empty(max(16, P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, ps)),
                      dtype=torch.uint8, device="cuda")
     out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
