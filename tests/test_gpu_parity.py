@@ -119,6 +119,49 @@ def test_empty_contexts_give_zero_rows(G, kv):
         assert err <= TOL[w.dtype], (part, err, where)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("G", [1, 8])
+def test_many_partials_per_row(G, kv):
+    """16-token partitions over contexts of up to 2,500 tokens: rows with more
+    than 64 partials take the workgroup-per-row reduce, shorter rows the
+    one-wave-per-row one (max_partitions decides for the whole call), so
+    rows of every length meet the wide kernel: empty, exactly one partition
+    (16 tokens), one token past it (17), and long lognormal ones."""
+    need_gpu()
+    w = workloads.make(3, S=9, H=4 * G, Hkv=4, len_median=1500, len_cap=2500)
+    fp8 = kv == "e4m3"
+    kw = dict(kv_dtype="e4m3", k_scale=KS, v_scale=VS) if fp8 else {}
+    dw = M.setup(w, write_step=True, **kw)
+    st = build_state(w)
+    kc, vc = build_pool(w, st, include_step=True, **kw)
+    lens = w.context_lens.astype(np.int64).copy()
+    lens[0] = 0
+    lens[3] = min(lens[3], 16)
+    lens[5] = min(lens[5], 17)
+    dw.context_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    part = 16
+    parts = -(-int(dw.max_context_len) // part)
+    announce("many partials", "G", G, kv, "max partitions", parts, "lens", lens.tolist())
+    assert parts > 64
+    ref = A.decode_ref(w.query, kc, vc, st.block_tables, np.maximum(lens, 1), w.scale, w.bs,
+                       w.dtype, **kw)
+    if fp8:
+        out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
+        nbytes = P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, part)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        P.pa_decode_fp8(out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                        dw.context_lens, dw.max_context_len, w.scale, KS, VS,
+                        partition_size=part, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+    else:
+        got = _decode(dw, part)
+    assert np.all(got[lens == 0] == 0.0)
+    err, where = max_abs(got[lens > 0], ref[lens > 0])
+    announce("max-abs", err)
+    assert err <= TOL[w.dtype], (err, where)
+
+
 @pytest.mark.parametrize("S,Hkv,G,D,kv", [
     (128, 4, 4, 64, "bf16"),   # 512 pairs: the one-pass list (<= 256 sequences)
     (300, 2, 8, 64, "bf16"),   # 600 pairs, 300 sequences: the batched list
