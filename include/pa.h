@@ -336,7 +336,7 @@ pa_status pa_decode_reduce(void* out, pa_dtype out_dtype,
  *                      every context_lens[s]; block_tables[s][0 ..
  *                      common_prefix_len / block_size - 1] must be the same
  *                      blocks for every s (row 0's are read; not checked on
- *                      the device)
+ *                      the device -- pa_check_metadata checks it on request)
  *   partition_size     split of each sequence's own tokens [common_prefix_len,
  *                      L): > 0 (a multiple of 16), 0 = one partition for the
  *                      longest, -1 = chosen by the library
@@ -397,8 +397,12 @@ pa_status pa_decode_cascade_fp8(void* out, pa_dtype out_dtype, const void* query
  *                   non-decreasing, query_start_loc[num_seqs] = num_tokens
  *   max_query_len   >= every n (host value)
  * out, query and both caches must be 16-byte aligned (PA_ERR_INVALID_ARGUMENT
- * otherwise).  Probabilities are rounded to f16 for the P.V product and the
- * normaliser sums the rounded values; V must lie in f16 range.
+ * otherwise).  Each probability enters the P.V product as two f16 terms
+ * (hi = f16(p), lo = f16(p - hi): about 22 significant bits) and the
+ * normaliser sums those same terms; V of any finite bf16 magnitude is
+ * handled (values of 2^16 and more switch the workgroup to V scaled by a
+ * power of two, its earlier sums rescaled exactly), infinities and NaN
+ * propagate as in the plain definition.
  * Supported: kv_dtype PA_BF16 or PA_F16 (matrix cores), head_size 64 or 128,
  * num_heads / num_kv_heads in {1,2,4,8,16}, block_size a power of two.
  */
