@@ -331,7 +331,9 @@ pa_status pa_decode_reduce(void* out, pa_dtype out_dtype,
  * mask, each sequence's own tokens separately, and the parts are merged with
  * the online-softmax rule of §7.3).
  *
- * Same result as pa_decode (same arguments and output).  Additionally:
+ * Same result as pa_decode up to the order of fp32 sums (same arguments and
+ * output; both equal the plain definition within the same bound, at any V
+ * magnitude).  Additionally:
  *   common_prefix_len  tokens, a positive multiple of block_size, at most
  *                      every context_lens[s]; block_tables[s][0 ..
  *                      common_prefix_len / block_size - 1] must be the same
