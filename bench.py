@@ -57,6 +57,7 @@ KERNEL_SOURCES = {
     "decode_group": ["decode_group.hip", "decode_common.h", "kernel_common.h"],
     "decode_group_fp8": ["decode_group_fp8.hip", "decode_common.h", "kernel_common.h"],
     "prefill": ["prefill.hip", "kernel_common.h"],
+    "copy_blocks": ["cache_ops.hip", "kernel_common.h"],
 }
 FLUSH_BYTES = 512 << 20      # > the 256 MB memory-side cache (MALL)
 PROBE_BYTES = 4 << 30        # streaming-read ceiling buffer
@@ -108,6 +109,9 @@ def parse():
                     help="oracle baseline processes (0: the host cores this process may use, at "
                          "most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-blocks", action="store_true",
+                    help="time the batched copy-on-write block copy (pa_copy_blocks) of a "
+                         "shared-prefix workload's set-up instead of an attention step")
     return ap.parse_args()
 
 
@@ -150,12 +154,142 @@ def stats_us(xs_ms):
             "min": round(float(a.min()), 3), "p90": round(float(np.percentile(a, 90)), 3)}
 
 
+def copy_blocks_bench(args):
+    """--copy-blocks: the batched copy-on-write copy of a shared-prefix
+    workload (its set-up copies the shared partial block once per sequence
+    that appends into it), timed alone.  One step = one pa_copy_blocks call
+    over every pair, K and V pools.  value = bytes the copies move per step
+    (each pair's block read and written) / mean step time; the roofline
+    counts the HBM bytes the step must move (every destination written, each
+    distinct source read once: one shared source here) against the HBM peak;
+    parity: every destination block equals its source bit for bit; the
+    baseline copies the same number of blocks of the same size between host
+    arrays with NumPy (the plain definition of the copy), one process."""
+    import numpy as np
+
+    import workloads
+
+    cfg = args.config if not args.config.isdigit() else int(args.config)
+    w = workloads.make(cfg)
+    if w.prefix_len == 0 or args.kv != "native":
+        raise SystemExit("--copy-blocks needs a shared-prefix workload (5a or 5c) with its own cache type")
+    block_bytes = w.bs * w.Hkv * w.D * w.elem_bytes
+
+    import torch
+
+    import paged_kv_cache_134_amd as P
+    from paged_kv_cache_134_amd import metadata as M
+
+    layout = P.NHD if args.layout == "nhd" else P.HND
+    torch.cuda.set_device(0)
+    dw = M.setup(w, layout=layout)
+    torch.cuda.synchronize()
+    if not dw.copies:
+        raise SystemExit(f"{w.name} makes no copy-on-write copies")
+    pairs_np = np.asarray(dw.copies, np.int32).reshape(-1, 2)
+    pairs = torch.from_numpy(pairs_np).cuda()
+    n = len(pairs_np)
+    moved = 2 * 2 * n * block_bytes  # K and V; each block read and written once
+    stream = torch.cuda.current_stream()
+    flush_buf = None if args.flush == "none" else torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32,
+                                                              device="cuda")
+
+    def step():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        P.pa_copy_blocks(dw.key_cache, dw.value_cache, pairs, layout)
+        b.record(stream)
+        return a, b
+
+    for _ in range(max(args.warmup, 5)):
+        step()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.sum() if args.flush == "read" else flush_buf.fill_(float(i & 0xFF))
+        evs.append(step())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in evs]
+    mean_ms = float(np.mean(ms))
+    src, dst = pairs[:, 0].long(), pairs[:, 1].long()
+
+    def bits(t):  # bit patterns: unwritten slots hold NaN, which == would reject
+        return t.contiguous().view(torch.uint8)
+
+    ok = bool(torch.equal(bits(dw.key_cache[dst]), bits(dw.key_cache[src])) and
+              torch.equal(bits(dw.value_cache[dst]), bits(dw.value_cache[src])))
+    # HBM bytes the copy must move: every destination written, each distinct
+    # source read once (the set-ups copy one shared block to many sequences)
+    unique = 2 * (n + len(set(pairs_np[:, 0].tolist()))) * block_bytes
+
+    # write ceiling: torch's fill of as many bytes as the copies write, timed
+    # the same way (the copy's reads are one shared block, cache-resident)
+    fill_buf = torch.empty(2 * n * block_bytes // 4, dtype=torch.int32, device="cuda")
+    fill_ev = []
+    for i in range(max(args.warmup, 5) + args.steps):
+        if flush_buf is not None:
+            flush_buf.sum() if args.flush == "read" else flush_buf.fill_(float(i & 0xFF))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fill_buf.fill_(i)
+        b.record(stream)
+        fill_ev.append((a, b))
+    torch.cuda.synchronize()
+    fill_ms = float(np.mean([a.elapsed_time(b) for a, b in fill_ev[max(args.warmup, 5):]]))
+    write_ceiling = 2 * n * block_bytes / (fill_ms * 1e-3) / 1e9
+    del fill_buf
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        elems = block_bytes // 2
+        host_src = np.random.default_rng(0).integers(0, 2**16, (2 * n, elems), dtype=np.uint16)
+        host_dst = np.empty_like(host_src)
+        reps, t_c = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t_c < min(args.cpu_seconds, 5.0):
+            for r in range(2 * n):
+                host_dst[r] = host_src[r]
+            reps += 1
+        sec = (time.perf_counter() - t_c) / reps
+        cpu = {"value": round(moved / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} passes of {2 * n} block copies of {block_bytes} bytes between "
+                         f"host arrays (NumPy, one process)"}
+
+    value = moved / (mean_ms * 1e-3) / 1e9
+    achieved = unique / (mean_ms * 1e-3) / 1e9
+    line = {
+        "metric": "batched copy-on-write block copy GB/s (bytes read + written)",
+        "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": max(args.warmup, 5), "ms_per_step": round(mean_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} copy-on-write copies", "pairs": n,
+                   "block_bytes": block_bytes, "layout": args.layout.upper()},
+        "step_us": stats_us(ms), "wall_ms_per_step_with_flush": round(wall * 1e3 / args.steps, 5),
+        "bytes_moved_per_step": moved, "unique_hbm_bytes_per_step": unique,
+        "parity": {"bit_exact": ok, "checked": "every destination block against its source"},
+        "write_ceiling_GBps": round(write_ceiling, 1),
+        "frac_write_ceiling": round(achieved / write_ceiling, 4),
+        "kernels_us": {"copy_blocks": stats_us(ms)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "kernel": "copy_blocks", "kernel_source_sha": source_sha("copy_blocks"),
+                     "traffic": traffic_from_profile(w.name, "copy_blocks")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every step of this "
               "path runs on a single MI355X and no multi-GPU figure is produced.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_blocks:
+        return copy_blocks_bench(args)
 
     import numpy as np
 

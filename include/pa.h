@@ -128,7 +128,9 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, pa_dtype 
  * copy-on-write step 2, [atb] copy-on-write section).
  *   block_pairs (device) int32 [num_pairs][2] = (source block, destination block)
  * Every destination must be distinct and no destination may be a source
- * (not checked on the device).  num_pairs == 0 is a no-op.
+ * (not checked on the device).  A pair naming a block outside
+ * [0, num_blocks) is skipped (the kernel checks each pair before touching
+ * either pool).  num_pairs == 0 is a no-op.
  */
 pa_status pa_copy_blocks(void* key_cache, void* value_cache,
                          const int32_t* block_pairs, int32_t num_pairs,

@@ -167,7 +167,7 @@ extern "C" pa_status pa_copy_blocks(void* key_cache, void* value_cache, const in
   if (block_bytes % 16 || !aligned16(key_cache) || !aligned16(value_cache))
     return pa_fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: blocks must be 16-byte multiples and aligned");
   hipError_t e = pa::launch_copy_blocks(key_cache, value_cache, block_pairs, num_pairs, block_bytes,
-                                        (hipStream_t)stream);
+                                        num_blocks, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_copy_blocks");
 }
 

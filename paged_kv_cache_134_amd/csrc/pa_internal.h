@@ -40,7 +40,8 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, pa_d
                                         hipStream_t stream);
 
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
-                              int32_t num_pairs, int64_t block_bytes, hipStream_t stream);
+                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
+                              hipStream_t stream);
 
 struct DecodeArgs {
   void* out;

@@ -493,3 +493,41 @@ def test_swap_blocks_out_and_back(kv):
         assert np.array_equal(bk[d_], kd[s_]) and np.array_equal(bv[d_], vd[s_])
     rest = sorted(set(range(nb)) - set(in_pairs[:, 1].tolist()))
     assert not bk[rest].any() and not bv[rest].any()
+
+
+@pytest.mark.parametrize("bs,hkv,d,dtype,layout", [
+    (16, 3, 64, "bfloat16", "NHD"),     # 6 KB block: one partial 16 KB piece
+    (48, 3, 128, "bfloat16", "HND"),    # 36 KB: two whole pieces and a 4 KB tail
+    (256, 8, 128, "bfloat16", "HND"),   # 512 KB: 32 pieces
+    (32, 2, 64, "float32", "NHD"),      # 16 KB: exactly one piece
+])
+def test_copy_blocks_bit_exact_and_out_of_range_pairs_skipped(bs, hkv, d, dtype, layout):
+    """pa_copy_blocks against its definition (each destination block becomes a
+    bit copy of its source; nothing else changes), over the whole pool: one
+    source shared by several pairs (the copy-on-write case), other sources
+    once each, and pairs naming a block outside the pool, which are skipped
+    with their valid side untouched."""
+    need_gpu()
+    announce("copy blocks", bs, hkv, d, dtype, layout)
+    nb = 40
+    lay = P.NHD if layout == "NHD" else P.HND
+    shape = (nb, bs, hkv, d) if layout == "NHD" else (nb, hkv, bs, d)
+    tdt = getattr(torch, dtype)
+    gen = torch.Generator().manual_seed(bs * 1000 + hkv * 10 + d)
+    words = torch.randint(-2**15, 2**15, shape + (torch.finfo(tdt).bits // 16,),
+                          dtype=torch.int16, generator=gen)
+    k0 = words.view(tdt).reshape(shape)
+    v0 = torch.randint(-2**15, 2**15, words.shape, dtype=torch.int16,
+                       generator=gen).view(tdt).reshape(shape)
+    valid = [(3, 10), (3, 11), (3, 12), (3, 13), (5, 20), (7, 21), (0, 39), (38, 1)]
+    skipped = [(-1, 30), (nb, 31), (8, nb), (9, -5), (2**31 - 1, 32), (33, -2**31)]
+    pairs_np = np.asarray(valid[:4] + skipped[:3] + valid[4:] + skipped[3:], np.int32)
+    kc, vc = k0.cuda(), v0.cuda()
+    P.pa_copy_blocks(kc, vc, torch.from_numpy(pairs_np).cuda(), lay)
+    torch.cuda.synchronize()
+    raw = lambda t: t.cpu().contiguous().view(torch.uint8).numpy()  # noqa: E731
+    ek, ev = raw(k0).copy(), raw(v0).copy()
+    for s_, d_ in valid:
+        ek[d_], ev[d_] = ek[s_], ev[s_]
+    gk, gv = raw(kc), raw(vc)
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
