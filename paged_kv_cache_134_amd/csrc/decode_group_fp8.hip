@@ -6,13 +6,20 @@
 // is walked in rounds of 64 tokens; wave w takes tokens 16 w .. 16 w + 15 of
 // each round and keeps its own softmax state, so the waves never wait for
 // one another until the final merge.  Per 16-token tile:
+//   loads    each 16-byte load instruction covers whole cache rows (8 rows
+//            of 128 bytes at head size 128), non-temporally; K rows go to
+//            the wave's LDS region as they are, V rows as f16 (exact for
+//            every E4M3 value).  (Lanes loading the quarters their MFMA
+//            operands need read half of each 128-byte line per instruction;
+//            that measured 3-10% slower, and another 10-15% slower with
+//            non-temporal loads, whose lines are gone before the other half
+//            is read.)
 //   QK       S[16 tokens x 16 heads] = K Q^T on v_mfma_f32_16x16x32 (bf16 or
-//            f16 by the query's type).  The A operand comes straight from
-//            the cache into registers (lane = token l % 16 and quarter l / 16
-//            of the row; each load instruction reads 64 contiguous bytes of
-//            every row) and converts exactly from E4M3 to the query's type;
-//            the B operand is the group's query vectors, held in registers
-//            for the whole partition (heads past G are zero).
+//            f16 by the query's type).  The A operand is read back from LDS
+//            (lane = token l % 16 and quarter l / 16 of the row) and
+//            converts exactly from E4M3 to the query's type; the B operand
+//            is the group's query vectors, held in registers for the whole
+//            partition (heads past G are zero).
 //   softmax  a lane holds 4 tokens of head l % 16.  The running maximum
 //            moves only when some score exceeds it by more than 2^8; the
 //            probabilities are rounded to f16 once and the normaliser sums
@@ -22,12 +29,14 @@
 //            four probabilities: the QK product left tokens 4 q4 .. +3 of
 //            head l % 16 in exactly the B layout, so P never leaves the
 //            registers.  The A operand (16 columns x 16 tokens) is read
-//            transposed from the tile's V rows, which pass through the wave's
-//            own LDS region as f16 (exact for every E4M3 value); a lane then
+//            transposed from the tile's f16 V rows in LDS; a lane then
 //            holds O[head l % 16][16 b + 4 q4 .. +3] for every block b.
 // Each wave keeps two tiles of K/V in flight (the next two rounds) and reads
 // the block ids it needs from the table two rounds ahead of the rows they
-// locate.  The probabilities enter PV as two f16 terms, hi = f16(p) and lo =
+// locate; the tiles past the end of the partition are loaded too (clamped
+// to its last row, which is cached) so that no load sits on a branch: a
+// conditional refill made the compiler copy the just-loaded registers at
+// the loop's end, waiting for the loads it meant to keep in flight.  The probabilities enter PV as two f16 terms, hi = f16(p) and lo =
 // f16(p - hi) (two products on the same V operand), so the weights carry
 // about 22 significant bits; the normaliser sums hi + lo.  The waves' (max, sum, output) states are merged at the end by the
 // log-sum-exp rule.  Heads past G are zero in the query operand, so their
@@ -87,12 +96,16 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   static_assert(DT == PA_BF16 || DT == PA_F16, "queries are bf16 or f16");
   static_assert(G == 4 || G == 8 || G == 16, "group size 4, 8 or 16");
   constexpr int KB = D / 32;            // MFMA k-blocks of 32 elements
-  constexpr int NLD = D / 64;           // 16-byte loads per lane per row (a quarter row)
-  constexpr int RC = D / 8;             // 16-byte LDS pieces per V row
+  constexpr int PPR = D / 16;           // 16-byte pieces per cache row (one byte per element)
+  constexpr int RPI = kWave / PPR;      // rows one load instruction covers (whole rows)
+  constexpr int NLD = kTile / RPI;      // load instructions per tensor per tile
+  constexpr int KSTR = PPR + 1;         // padded LDS row stride of the raw K rows, in pieces
+  constexpr int RC = D / 8;             // 16-byte LDS pieces per f16 V row
   constexpr int VSTR = RC + 1;          // padded LDS row stride in pieces
   constexpr int DB = D / 16;            // PV: 16-column blocks of O^T
+  constexpr int kWaveK = kTile * KSTR;                 // pieces of one wave's K region
   constexpr int kWaveV = kTile * VSTR;                 // pieces of one wave's V region
-  constexpr int kLdsMain = (kDecodeWaves * kWaveV) * 16;
+  constexpr int kLdsMain = (kDecodeWaves * (kWaveK + kWaveV)) * 16;
   constexpr int kLdsMerge = kDecodeWaves * G * D * 4;
   constexpr int kLds = kLdsMain > kLdsMerge ? kLdsMain : kLdsMerge;
   __shared__ __align__(16) char smem[kLds];
@@ -130,7 +143,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   const int q4 = lane / kTile;  // quarter of the row this lane loads
 
   // Element d held in slot e of MFMA k-block j by lanes of quarter q4: a
-  // lane's 16-byte loads are pieces q4, q4 + 4, ... of the row (16 elements
+  // lane reads pieces q4, q4 + 4, ... of its K row from LDS (16 elements
   // each), piece i feeding blocks 2 i and 2 i + 1.  The query operand uses
   // the same map.
   auto dmap = [&](int j) -> int { return 16 * (q4 + 4 * (j >> 1)) + 8 * (j & 1); };
@@ -149,9 +162,15 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
 
   const uint32_t blk_b = (uint32_t)p.blk_stride;  // one byte per element
   const uint32_t tok_b = (uint32_t)p.tok_stride;
-  const int64_t lane_off = (int64_t)kvh * p.head_stride + q4 * 16;  // bytes
+  const int64_t head_off = (int64_t)kvh * p.head_stride;  // bytes
+  // Loads cover whole rows: in load instruction i the lane reads piece lp of
+  // row RPI i + lr of the tile (every 128-byte line is read by one
+  // instruction, non-temporally; half-line reads measured slower).  Rows
+  // reach LDS as they are, and the MFMA lanes read back their quarters.
+  const int lr = lane / PPR, lp = lane % PPR;
 
-  uint4* sV = reinterpret_cast<uint4*>(smem) + wave * kWaveV;
+  uint4* sK = reinterpret_cast<uint4*>(smem) + wave * (kWaveK + kWaveV);  // raw E4M3 rows
+  uint4* sV = sK + kWaveK;                                                // f16 rows
   // PV A operand: V^T[d = 16 b + tl][token 4 q4 + j], j = 0..3, from the
   // wave's f16 rows (row stride VSTR pieces) by one transposing read per
   // block: lane tl of quarter q4 addresses row 4 q4 + tl / 4, columns
@@ -159,23 +178,27 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   const _Float16* vh =
       reinterpret_cast<const _Float16*>(sV) + (4 * q4 + tl / 4) * (VSTR * 8) + 4 * (tl % 4);
 
+  // block id of token ts + tl (lane tl of every quarter holds it)
   auto block_of = [&](int ts) -> int32_t { return bt[min(ts + tl, t1 - 1) >> lbs]; };
-  // K and V pieces of the lane's token in tile ts (rows past the end are
-  // clamped to the last row: valid, finite, masked where used)
+  // K and V pieces of tile ts (rows past the end are clamped to the last
+  // row: valid, finite, masked where used); blk = block_of(ts), whose value
+  // for row r sits in lane r
   auto fetch = [&](int ts, int32_t blk, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
-    const int t = min(ts + tl, t1 - 1);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
+      const int r = RPI * i + lr;
+      const int32_t b = __shfl(blk, r);
+      const int t = min(ts + r, t1 - 1);
       if constexpr (OFF32) {
         const uint32_t off =
-            (uint32_t)blk * blk_b + (uint32_t)(t & bs_mask) * tok_b + (uint32_t)lane_off + 64 * i;
-        kr[i] = load16(p.key_cache + off);
-        vr[i] = load16(p.value_cache + off);
+            (uint32_t)b * blk_b + (uint32_t)(t & bs_mask) * tok_b + (uint32_t)head_off + 16 * lp;
+        kr[i] = load_nt(p.key_cache + off);
+        vr[i] = load_nt(p.value_cache + off);
       } else {
-        const int64_t off = (int64_t)blk * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride +
-                            lane_off + 64 * i;
-        kr[i] = load16(p.key_cache + off);
-        vr[i] = load16(p.value_cache + off);
+        const int64_t off =
+            (int64_t)b * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride + head_off + 16 * lp;
+        kr[i] = load_nt(p.key_cache + off);
+        vr[i] = load_nt(p.value_cache + off);
       }
     }
   };
@@ -194,20 +217,25 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   // Consumes tile ts from (kr, vr), then refills them with the tile two
   // rounds ahead (its block ids were read two rounds ago).
   auto tile = [&](int ts, uint4 (&kr)[NLD], uint4 (&vr)[NLD], int32_t& blk_ahead) {
-    // ---- K as MFMA A operands (exact E4M3 -> query type), V into LDS as f16
-    uint4 ka[KB];
+    // ---- K rows into LDS as they are, V rows as f16
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      fp8x16_to_pairs<DT>(kr[i], ka[2 * i], ka[2 * i + 1]);
+      const int r = RPI * i + lr;
+      sK[r * KSTR + lp] = kr[i];
       uint4 v0, v1;
       fp8x16_to_pairs<PA_F16>(vr[i], v0, v1);
-      sV[tl * VSTR + 2 * (q4 + 4 * i)] = v0;
-      sV[tl * VSTR + 2 * (q4 + 4 * i) + 1] = v1;
+      sV[r * VSTR + 2 * lp] = v0;
+      sV[r * VSTR + 2 * lp + 1] = v1;
     }
-    if (ts + 2 * kRound - kTile * wave < t1) {
-      fetch(ts + 2 * kRound, blk_ahead, kr, vr);
-      blk_ahead = block_of(ts + 4 * kRound);
-    }
+    fetch(ts + 2 * kRound, blk_ahead, kr, vr);
+    blk_ahead = block_of(ts + 4 * kRound);
+    wave_lds_sync();  // the tile's K and V rows are visible to the whole wave
+
+    // ---- K as MFMA A operands: pieces q4, q4 + 4, ... of row tl (exact
+    // E4M3 -> query type)
+    uint4 ka[KB];
+#pragma unroll
+    for (int i = 0; i < KB / 2; ++i) fp8x16_to_pairs<DT>(sK[tl * KSTR + q4 + 4 * i], ka[2 * i], ka[2 * i + 1]);
 
     // ---- QK on matrix cores: the lane holds tokens 4 q4 + r of head tl
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -241,7 +269,6 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
       pl[r] = (_Float16)(e - (float)ph[r]);
       l_lane += (float)ph[r] + (float)pl[r];
     }
-    wave_lds_sync();  // the tile's V rows are visible to the whole wave
 
     // ---- PV on matrix cores: O^T[16 d x 16 heads] += V^T[16 d x 16 tokens]
     // P^T[16 tokens x 16 heads] per block of 16 columns
@@ -260,7 +287,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b) o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(a[b], pbl, o[b], 0, 0, 0);
-    wave_lds_sync();  // this tile's V is consumed before the next tile's stores
+    wave_lds_sync();  // this tile's K and V are consumed before the next tile's stores
   };
 
   // Merge of the waves' states (log-sum-exp rule) -- written as the
@@ -302,14 +329,18 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   };
 
   // Two tile buffers alternate, so two tiles per wave are always in flight.
+  // The block ids come first and the two tiles' loads in order (the
+  // scheduling barrier keeps them apart), so the first tile can be consumed
+  // while the second is still loading.
   const int ts0 = t0 + kTile * wave;
   uint4 ka_[NLD], va_[NLD], kb_[NLD], vb_[NLD];
-  fetch(ts0, block_of(ts0), ka_, va_);
-  if (ts0 + kRound - kTile * wave < t1) fetch(ts0 + kRound, block_of(ts0 + kRound), kb_, vb_);
+  const int32_t bid0 = block_of(ts0), bid1 = block_of(ts0 + kRound);
   int32_t bid_a = block_of(ts0 + 2 * kRound), bid_b = block_of(ts0 + 3 * kRound);
+  fetch(ts0, bid0, ka_, va_);
+  __builtin_amdgcn_sched_barrier(0);
+  fetch(ts0 + kRound, bid1, kb_, vb_);
   for (int ts = ts0; ts - kTile * wave < t1; ts += 2 * kRound) {
     tile(ts, ka_, va_, bid_a);
-    if (ts + kRound - kTile * wave >= t1) break;
     tile(ts + kRound, kb_, vb_, bid_b);
   }
   flush();
