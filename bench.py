@@ -54,8 +54,8 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16/fp16 MFMA, AMD published
 # retires the profile)
 KERNEL_SOURCES = {
     "decode_head": ["decode_head.hip", "decode_common.h", "kernel_common.h"],
-    "decode_group": ["decode_group.hip", "decode_common.h", "kernel_common.h"],
-    "decode_group_fp8": ["decode_group_fp8.hip", "decode_common.h", "kernel_common.h"],
+    "decode_group": ["decode_group_mfma.hip", "decode_common.h", "kernel_common.h"],
+    "decode_group_fp8": ["decode_group_mfma.hip", "decode_common.h", "kernel_common.h"],
     "prefill": ["prefill.hip", "kernel_common.h"],
     "copy_blocks": ["cache_ops.hip", "kernel_common.h"],
 }
@@ -65,8 +65,9 @@ PROBE_BYTES = 4 << 30        # streaming-read ceiling buffer
 
 def decode_kernel_kind(w, fp8: bool = False) -> str:
     """Which decode kernel the library dispatches for this workload: the
-    grouped kernels for group sizes 4, 8, 16 (LDS-staged for 16-bit caches,
-    matrix-core for FP8), the per-head kernel otherwise."""
+    matrix-core grouped kernel for group sizes 4, 8, 16 (named apart for
+    16-bit and FP8 caches: its two instantiations), the per-head kernel
+    otherwise."""
     if w.dtype == "f32" or w.G not in (4, 8, 16):
         return "decode_head"
     return "decode_group_fp8" if fp8 else "decode_group"

@@ -7,11 +7,10 @@
 // max/sum rescaling) and the block-wise online softmax of the "Paged
 // attention" post (k4i.top, attention over non-contiguous blocks).
 //
-// Three kernels share one contract; the dispatcher picks by GQA group size G
+// Two kernels share one contract; the dispatcher picks by GQA group size G
 // and element type: the per-head kernel (decode_head.hip) for G <= 2 and
-// every fp32 cache, the LDS-staged grouped kernel (decode_group.hip) for
-// 16-bit caches otherwise, and the matrix-core grouped kernel
-// (decode_group_fp8.hip) for FP8 caches otherwise.  All
+// every fp32 cache, the matrix-core grouped kernel (decode_group_mfma.hip)
+// for 16-bit and FP8 caches otherwise.  Both
 // use one workgroup of 4 waves per (sequence, kv head, partition), read each
 // kv head's K/V rows once for all G query heads of its group, never load a
 // token at or past the context length (so NaN in unused slots cannot reach
@@ -367,7 +366,7 @@ hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
   if (a.kv_dtype == PA_FP8_E4M3)
     return group ? dec::launch_group_fp8(p, a.q_dtype, g.head_size, G, grid, stream)
                  : dec::launch_head_fp8(p, a.q_dtype, g.head_size, G, grid, stream);
-  if (group) return dec::launch_group(p, a.kv_dtype, g.head_size, G, grid, stream);
+  if (group) return dec::launch_group_mfma(p, a.kv_dtype, g.head_size, G, grid, stream);
   return dec::launch_head(p, a.kv_dtype, g.head_size, G, grid, stream);
 }
 

@@ -138,11 +138,13 @@ __device__ __forceinline__ void emit_zero_rows(const DecodeParams& p, int64_t he
 // Kernel launches of one decode pass; grid = (num_seqs * num_kv_heads,
 // partitions or 1).
 hipError_t launch_head(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st);
-hipError_t launch_group(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st);
 // FP8 (E4M3) caches; qt = query type (bf16 or f16).  Group sizes 1 and 2 take
 // the per-head kernel, 4, 8 and 16 the matrix-core grouped kernel.
 hipError_t launch_head_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st);
 hipError_t launch_group_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st);
+// 16-bit caches on the matrix-core grouped kernel (dt = the cache's and the
+// query's type).
+hipError_t launch_group_mfma(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st);
 
 }  // namespace dec
 }  // namespace pa

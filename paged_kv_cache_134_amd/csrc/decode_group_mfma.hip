@@ -1,48 +1,55 @@
-// Paged decode over FP8 (E4M3) caches, grouped kernel (group size 4, 8 or
-// 16; bf16 or f16 queries) on matrix cores.
+// Paged decode, grouped kernel on matrix cores (group size 4, 8 or 16;
+// bf16 or f16 caches, and FP8 (E4M3) caches with bf16 or f16 queries).
 //
 // One workgroup of 4 waves per (sequence, kv head, partition), as in the
-// other decode kernels (contract and sources in decode.hip).  The partition
-// is walked in rounds of 64 tokens; wave w takes tokens 16 w .. 16 w + 15 of
+// per-head kernel (contract and sources in decode.hip).  The partition is
+// walked in rounds of 64 tokens; wave w takes tokens 16 w .. 16 w + 15 of
 // each round and keeps its own softmax state, so the waves never wait for
 // one another until the final merge.  Per 16-token tile:
-//   loads    each 16-byte load instruction covers whole cache rows (8 rows
-//            of 128 bytes at head size 128), non-temporally; K rows go to
-//            the wave's LDS region as they are, V rows as f16 (exact for
-//            every E4M3 value).  (Lanes loading the quarters their MFMA
-//            operands need read half of each 128-byte line per instruction;
-//            that measured 3-10% slower, and another 10-15% slower with
-//            non-temporal loads, whose lines are gone before the other half
-//            is read.)
+//   loads    each 16-byte load instruction covers whole cache rows (4 rows
+//            of 256 bytes for 16-bit caches at head size 128, 8 of 128
+//            bytes for FP8), non-temporally; K rows go to the wave's LDS
+//            region as they are, V rows as 16-bit values (FP8 codes as f16,
+//            exact for every E4M3 value).  (FP8 lanes loading the quarters
+//            their MFMA operands need read half of each 128-byte line per
+//            instruction; that measured 3-10% slower, and another 10-15%
+//            slower with non-temporal loads, whose lines are gone before
+//            the other half is read.)
 //   QK       S[16 tokens x 16 heads] = K Q^T on v_mfma_f32_16x16x32 (bf16 or
 //            f16 by the query's type).  The A operand is read back from LDS
-//            (lane = token l % 16 and quarter l / 16 of the row) and
-//            converts exactly from E4M3 to the query's type; the B operand
-//            is the group's query vectors, held in registers for the whole
+//            (lane = token l % 16 and quarter l / 16 of the row; FP8 codes
+//            convert exactly to the query's type); the B operand is the
+//            group's query vectors, held in registers for the whole
 //            partition (heads past G are zero).
 //   softmax  a lane holds 4 tokens of head l % 16.  The running maximum
-//            moves only when some score exceeds it by more than 2^8; the
-//            probabilities are rounded to f16 once and the normaliser sums
-//            the rounded values.
-//   PV       O^T[16 d x 16 heads] += V^T P^T on v_mfma_f32_16x16x16_f16,
-//            one product per 16 columns.  The B operand is the lane's own
-//            four probabilities: the QK product left tokens 4 q4 .. +3 of
-//            head l % 16 in exactly the B layout, so P never leaves the
-//            registers.  The A operand (16 columns x 16 tokens) is read
-//            transposed from the tile's f16 V rows in LDS; a lane then
+//            moves only when some score exceeds it by more than 2^8.
+//   PV       O^T[16 d x 16 heads] += V^T P^T on v_mfma_f32_16x16x16, one
+//            product per 16 columns and weight term.  The B operand is the
+//            lane's own four probabilities: the QK product left tokens
+//            4 q4 .. +3 of head l % 16 in exactly the B layout, so P never
+//            leaves the registers.  The A operand (16 columns x 16 tokens)
+//            is read transposed from the tile's V rows in LDS; a lane then
 //            holds O[head l % 16][16 b + 4 q4 .. +3] for every block b.
+// Precision: each weight enters PV as terms exact in V's type -- two f16
+// terms, hi = f16(p) and lo = f16(p - hi) (about 22 significant bits), for
+// f16 and FP8 caches; three bf16 terms (about 24 bits, fp32's precision)
+// for bf16 caches, whose V then enters the products exactly at any
+// magnitude, infinities and NaN included -- and the normaliser sums the
+// same terms.  QK products are exact with fp32 sums.
 // Each wave keeps two tiles of K/V in flight (the next two rounds) and reads
 // the block ids it needs from the table two rounds ahead of the rows they
 // locate; the tiles past the end of the partition are loaded too (clamped
 // to its last row, which is cached) so that no load sits on a branch: a
 // conditional refill made the compiler copy the just-loaded registers at
-// the loop's end, waiting for the loads it meant to keep in flight.  The probabilities enter PV as two f16 terms, hi = f16(p) and lo =
-// f16(p - hi) (two products on the same V operand), so the weights carry
-// about 22 significant bits; the normaliser sums hi + lo.  The waves' (max, sum, output) states are merged at the end by the
-// log-sum-exp rule.  Heads past G are zero in the query operand, so their
-// scores, probabilities and outputs are never used.  With 16-bit caches the
-// LDS-staged grouped kernel (decode_group.hip) is faster and is used
-// instead.
+// the loop's end, waiting for the loads it meant to keep in flight.  The
+// waves' (max, sum, output) states are merged at the end by the log-sum-exp
+// rule.  Heads past G are zero in the query operand, so their scores,
+// probabilities and outputs are never used.
+//
+// For 16-bit caches this replaced a kernel doing QK on v_dot2 and PV with
+// fp32 weights on fp32 FMAs, which was bound by its vector ALU (70% busy):
+// 762 -> 737 us on the long-context batch, 158 -> 151 us on the 70B-like
+// one, and at group size 16 228 -> 161 us.
 #include <hip/hip_runtime.h>
 
 #include "decode_common.h"
@@ -59,6 +66,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef __fp16 lds_f16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // gfx950 transposing LDS read: in each group of 16 lanes, lane 4 r + c
 // addresses 4 consecutive 16-bit values of row r (columns 4 c .. 4 c + 3)
@@ -87,20 +95,73 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int G, int D>
-constexpr int kMfmaMinWaves = (G >= 16 && D >= 128) ? 2 : 3;
+// Waves per SIMD the register budget is set for (3 = at most 168 VGPRs).
+// Group size 16 at head size 128 needs more and settles for 2, and so do
+// 16-bit caches at head size 128, whose loads in flight take twice the
+// registers: bf16 compiles to 170 registers there (168 under a 3-wave bound,
+// which measured 1% slower on the long-context batch and 0.3% faster on the
+// 70B-like one); f16 to 161, so it runs 3 waves all the same (its 3-wave
+// bound spilled).
+template <int G, int D, bool FP8, pa_dtype DT>
+constexpr int kMfmaMinWaves = (D >= 128 && (G >= 16 || !FP8)) ? 2 : 3;
 
-template <pa_dtype DT, int D, int G, bool OFF32>
-__global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_fp8_mfma_kernel(
+// PV on matrix cores, O^T[16 d x 16 heads] += V^T P^T over 16 tokens: a =
+// the lane's V^T operand (16-bit rows: f16, or bf16 bits), w = the lane's
+// four weights (p = the sum of the terms, each exact in the operand type).
+template <bool BF16V>
+struct PvWeights;
+template <>
+struct PvWeights<false> {  // f16 V: p = hi + lo, two f16 terms (~22 bits)
+  f16x4_t hi, lo;
+  __device__ __forceinline__ float set(int r, float w) {
+    hi[r] = (_Float16)w;
+    lo[r] = (_Float16)(w - (float)hi[r]);
+    return (float)hi[r] + (float)lo[r];
+  }
+  __device__ __forceinline__ void first(const f16x4_t& a, f32x4_t& o) const {
+    o = __builtin_amdgcn_mfma_f32_16x16x16f16(a, hi, o, 0, 0, 0);
+  }
+  __device__ __forceinline__ void rest(const f16x4_t& a, f32x4_t& o) const {
+    o = __builtin_amdgcn_mfma_f32_16x16x16f16(a, lo, o, 0, 0, 0);
+  }
+};
+template <>
+struct PvWeights<true> {  // bf16 V: p = t0 + t1 + t2, three bf16 terms (~24 bits)
+  __bf16 t[3][4];
+  __device__ __forceinline__ float set(int r, float w) {
+    t[0][r] = (__bf16)w;
+    const float r1 = w - (float)t[0][r];  // exact
+    t[1][r] = (__bf16)r1;
+    t[2][r] = (__bf16)(r1 - (float)t[1][r]);
+    return (float)t[0][r] + (float)t[1][r] + (float)t[2][r];
+  }
+  __device__ __forceinline__ i16x4_t term(int k) const {
+    return i16x4_t{__builtin_bit_cast(short, t[k][0]), __builtin_bit_cast(short, t[k][1]),
+                   __builtin_bit_cast(short, t[k][2]), __builtin_bit_cast(short, t[k][3])};
+  }
+  __device__ __forceinline__ void first(const f16x4_t& a, f32x4_t& o) const {
+    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), term(0), o, 0, 0, 0);
+  }
+  __device__ __forceinline__ void rest(const f16x4_t& a, f32x4_t& o) const {
+    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), term(1), o, 0, 0, 0);
+    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), term(2), o, 0, 0, 0);
+  }
+};
+
+// DT = the query's type (and the cache's, unless FP8).
+template <pa_dtype DT, int D, int G, bool OFF32, bool FP8>
+__global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D, FP8, DT>)) void decode_mfma_kernel(
     const DecodeParams p) {
   static_assert(DT == PA_BF16 || DT == PA_F16, "queries are bf16 or f16");
   static_assert(G == 4 || G == 8 || G == 16, "group size 4, 8 or 16");
+  constexpr int CB = FP8 ? 1 : 2;       // cache bytes per element
+  constexpr bool kBf16V = !FP8 && DT == PA_BF16;  // V rows in LDS are bf16 (else f16)
   constexpr int KB = D / 32;            // MFMA k-blocks of 32 elements
-  constexpr int PPR = D / 16;           // 16-byte pieces per cache row (one byte per element)
+  constexpr int PPR = D * CB / 16;      // 16-byte pieces per cache row
   constexpr int RPI = kWave / PPR;      // rows one load instruction covers (whole rows)
   constexpr int NLD = kTile / RPI;      // load instructions per tensor per tile
   constexpr int KSTR = PPR + 1;         // padded LDS row stride of the raw K rows, in pieces
-  constexpr int RC = D / 8;             // 16-byte LDS pieces per f16 V row
+  constexpr int RC = D / 8;             // 16-byte LDS pieces per 16-bit V row
   constexpr int VSTR = RC + 1;          // padded LDS row stride in pieces
   constexpr int DB = D / 16;            // PV: 16-column blocks of O^T
   constexpr int kWaveK = kTile * KSTR;                 // pieces of one wave's K region
@@ -143,10 +204,12 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   const int q4 = lane / kTile;  // quarter of the row this lane loads
 
   // Element d held in slot e of MFMA k-block j by lanes of quarter q4: a
-  // lane reads pieces q4, q4 + 4, ... of its K row from LDS (16 elements
-  // each), piece i feeding blocks 2 i and 2 i + 1.  The query operand uses
-  // the same map.
-  auto dmap = [&](int j) -> int { return 16 * (q4 + 4 * (j >> 1)) + 8 * (j & 1); };
+  // lane reads pieces q4, q4 + 4, ... of its K row from LDS -- FP8: 16
+  // elements each, piece i feeding blocks 2 i and 2 i + 1; 16-bit: 8
+  // elements, piece i = block i.  The query operand uses the same map.
+  auto dmap = [&](int j) -> int {
+    return FP8 ? 16 * (q4 + 4 * (j >> 1)) + 8 * (j & 1) : 8 * (q4 + 4 * j);
+  };
 
   // B operand: the query vector of head tl (zero past the group).
   uint4 qb[KB];
@@ -160,9 +223,9 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
     }
   }
 
-  const uint32_t blk_b = (uint32_t)p.blk_stride;  // one byte per element
-  const uint32_t tok_b = (uint32_t)p.tok_stride;
-  const int64_t head_off = (int64_t)kvh * p.head_stride;  // bytes
+  const uint32_t blk_b = (uint32_t)(p.blk_stride * CB);
+  const uint32_t tok_b = (uint32_t)(p.tok_stride * CB);
+  const int64_t head_off = (int64_t)kvh * p.head_stride * CB;  // bytes
   // Loads cover whole rows: in load instruction i the lane reads piece lp of
   // row RPI i + lr of the tile (every 128-byte line is read by one
   // instruction, non-temporally; half-line reads measured slower).  Rows
@@ -195,8 +258,8 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
         kr[i] = load_nt(p.key_cache + off);
         vr[i] = load_nt(p.value_cache + off);
       } else {
-        const int64_t off =
-            (int64_t)b * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride + head_off + 16 * lp;
+        const int64_t off = ((int64_t)b * p.blk_stride + (int64_t)(t & bs_mask) * p.tok_stride) * CB +
+                            head_off + 16 * lp;
         kr[i] = load_nt(p.key_cache + off);
         vr[i] = load_nt(p.value_cache + off);
       }
@@ -217,25 +280,34 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   // Consumes tile ts from (kr, vr), then refills them with the tile two
   // rounds ahead (its block ids were read two rounds ago).
   auto tile = [&](int ts, uint4 (&kr)[NLD], uint4 (&vr)[NLD], int32_t& blk_ahead) {
-    // ---- K rows into LDS as they are, V rows as f16
+    // ---- K rows into LDS as they are, V rows as 16-bit (FP8: f16)
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int r = RPI * i + lr;
       sK[r * KSTR + lp] = kr[i];
-      uint4 v0, v1;
-      fp8x16_to_pairs<PA_F16>(vr[i], v0, v1);
-      sV[r * VSTR + 2 * lp] = v0;
-      sV[r * VSTR + 2 * lp + 1] = v1;
+      if constexpr (FP8) {
+        uint4 v0, v1;
+        fp8x16_to_pairs<PA_F16>(vr[i], v0, v1);
+        sV[r * VSTR + 2 * lp] = v0;
+        sV[r * VSTR + 2 * lp + 1] = v1;
+      } else {
+        sV[r * VSTR + lp] = vr[i];
+      }
     }
     fetch(ts + 2 * kRound, blk_ahead, kr, vr);
     blk_ahead = block_of(ts + 4 * kRound);
     wave_lds_sync();  // the tile's K and V rows are visible to the whole wave
 
-    // ---- K as MFMA A operands: pieces q4, q4 + 4, ... of row tl (exact
-    // E4M3 -> query type)
+    // ---- K as MFMA A operands: pieces q4, q4 + 4, ... of row tl (FP8:
+    // exact E4M3 -> query type)
     uint4 ka[KB];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < KB / 2; ++i) fp8x16_to_pairs<DT>(sK[tl * KSTR + q4 + 4 * i], ka[2 * i], ka[2 * i + 1]);
+      for (int i = 0; i < KB / 2; ++i) fp8x16_to_pairs<DT>(sK[tl * KSTR + q4 + 4 * i], ka[2 * i], ka[2 * i + 1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KB; ++j) ka[j] = sK[tl * KSTR + q4 + 4 * j];
+    }
 
     // ---- QK on matrix cores: the lane holds tokens 4 q4 + r of head tl
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -261,32 +333,28 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
 #pragma unroll
       for (int b = 0; b < DB; ++b) o[b] *= alpha;  // the lane's own head
     }
-    _Float16 ph[4], pl[4];  // p = hi + lo, each f16
+    // weights split into terms exact in V's type; the normaliser sums the
+    // terms, so the weights that multiply V are the ones divided out
+    PvWeights<kBf16V> pw;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float e = z[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
-      ph[r] = (_Float16)e;
-      pl[r] = (_Float16)(e - (float)ph[r]);
-      l_lane += (float)ph[r] + (float)pl[r];
-    }
+    for (int r = 0; r < 4; ++r)
+      l_lane += pw.set(r, z[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref));
 
     // ---- PV on matrix cores: O^T[16 d x 16 heads] += V^T[16 d x 16 tokens]
     // P^T[16 tokens x 16 heads] per block of 16 columns
-    // (v_mfma_f32_16x16x16_f16).  The B operand is this lane's own four
-    // probabilities (tokens 4 q4 .. +3 of head tl, where the QK product put
-    // them; zero past the group and the context).
-    const f16x4_t pbh = {ph[0], ph[1], ph[2], ph[3]};
-    const f16x4_t pbl = {pl[0], pl[1], pl[2], pl[3]};
-    // (every block's hi product before the lo products: no product waits on
-    // the one just issued into the same accumulator)
+    // (v_mfma_f32_16x16x16, f16 or bf16 by V's type).  The B operand is this
+    // lane's own four probabilities (tokens 4 q4 .. +3 of head tl, where the
+    // QK product put them; zero past the group and the context).  Every
+    // block's first product comes before the other terms' products: no
+    // product waits on the one just issued into the same accumulator.
     f16x4_t a[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       a[b] = lds_read_tr16(vh + 16 * b);
-      o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(a[b], pbh, o[b], 0, 0, 0);
+      pw.first(a[b], o[b]);
     }
 #pragma unroll
-    for (int b = 0; b < DB; ++b) o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(a[b], pbl, o[b], 0, 0, 0);
+    for (int b = 0; b < DB; ++b) pw.rest(a[b], o[b]);
     wave_lds_sync();  // this tile's K and V are consumed before the next tile's stores
   };
 
@@ -346,22 +414,24 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D>)) void decode_
   flush();
 }
 
-template <pa_dtype DT, int D, bool OFF32>
+template <pa_dtype DT, int D, bool OFF32, bool FP8>
 hipError_t launch_g(const DecodeParams& p, int G, dim3 grid, hipStream_t st) {
   dim3 block(kDecodeThreads);
   switch (G) {
-    case 4: hipLaunchKernelGGL((decode_fp8_mfma_kernel<DT, D, 4, OFF32>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_fp8_mfma_kernel<DT, D, 8, OFF32>), grid, block, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((decode_fp8_mfma_kernel<DT, D, 16, OFF32>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 4, OFF32, FP8>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 8, OFF32, FP8>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 16, OFF32, FP8>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <pa_dtype DT>
+template <pa_dtype DT, bool FP8>
 hipError_t launch_d(const DecodeParams& p, int D, int G, dim3 grid, hipStream_t st) {
-  if (D == 64) return p.off32 ? launch_g<DT, 64, true>(p, G, grid, st) : launch_g<DT, 64, false>(p, G, grid, st);
-  if (D == 128) return p.off32 ? launch_g<DT, 128, true>(p, G, grid, st) : launch_g<DT, 128, false>(p, G, grid, st);
+  if (D == 64)
+    return p.off32 ? launch_g<DT, 64, true, FP8>(p, G, grid, st) : launch_g<DT, 64, false, FP8>(p, G, grid, st);
+  if (D == 128)
+    return p.off32 ? launch_g<DT, 128, true, FP8>(p, G, grid, st) : launch_g<DT, 128, false, FP8>(p, G, grid, st);
   return hipErrorInvalidValue;
 }
 
@@ -369,8 +439,16 @@ hipError_t launch_d(const DecodeParams& p, int D, int G, dim3 grid, hipStream_t 
 
 hipError_t launch_group_fp8(const DecodeParams& p, pa_dtype qt, int D, int G, dim3 grid, hipStream_t st) {
   switch (qt) {
-    case PA_BF16: return launch_d<PA_BF16>(p, D, G, grid, st);
-    case PA_F16: return launch_d<PA_F16>(p, D, G, grid, st);
+    case PA_BF16: return launch_d<PA_BF16, true>(p, D, G, grid, st);
+    case PA_F16: return launch_d<PA_F16, true>(p, D, G, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_group_mfma(const DecodeParams& p, pa_dtype dt, int D, int G, dim3 grid, hipStream_t st) {
+  switch (dt) {
+    case PA_BF16: return launch_d<PA_BF16, false>(p, D, G, grid, st);
+    case PA_F16: return launch_d<PA_F16, false>(p, D, G, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

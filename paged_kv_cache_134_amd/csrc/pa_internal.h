@@ -75,7 +75,7 @@ struct DecodeArgs {
 };
 
 // Single pass (partition_size == 0) or the split-K partition kernel.
-// Whether decode takes the grouped (LDS-staged) kernel for this element type
+// Whether decode takes the grouped (matrix-core) kernel for this element type
 // and group size G = num_heads / num_kv_heads.
 bool decode_uses_group_kernel(pa_dtype kv_dtype, int G);
 
