@@ -260,7 +260,8 @@ def test_gqa_equals_mha_with_repeated_kv():
                 dw.max_context_len, w.scale, partition_size=0)
     torch.cuda.synchronize()
     assert g[2] == 2
-    # the grouped kernel rounds probabilities to f16, the per-head one keeps fp32
+    # the grouped kernel splits each weight into bf16 terms, the per-head one
+    # keeps fp32
     assert np.max(np.abs(out_m.cpu().numpy() - out_g)) <= TOL["bf16"]
 
 
@@ -285,25 +286,39 @@ def test_bf16_output_within_one_ulp(G):
         assert np.all(excess <= 1.0), (part, np.unravel_index(np.argmax(excess), excess.shape))
 
 
-@pytest.mark.parametrize("G", [1, 8])
-def test_f16_decode(G):
-    """f16 caches: the bf16 workload's values converted to f16 (exact in range)."""
+@pytest.mark.parametrize("G,D,bs,layout,part", [
+    (1, 128, 16, P.NHD, 0),
+    (8, 128, 16, P.NHD, 0),
+    (4, 64, 8, P.HND, 512),
+    (8, 128, 32, P.HND, 512),
+    (16, 128, 16, P.NHD, 256),
+    (16, 64, 1, P.HND, 0),      # one token per block: every row has its own block id
+    (8, 128, 2, P.NHD, -1),
+])
+def test_f16_decode(G, D, bs, layout, part):
+    """f16 caches: the bf16 workload's values converted to f16 (exact in
+    range); per-head (G = 1) and grouped kernels (two f16 weight terms),
+    single pass and split-K, both layouts."""
     need_gpu()
-    w = workloads.make(2, S=3, H=4 * G, Hkv=4, len_lo=30, len_hi=600, n_pad=1)
-    announce("f16 decode", "G", G)
-    dw = M.setup(w, write_step=True)
+    w = workloads.make(2, S=3, H=4 * G, Hkv=4, D=D, bs=bs, len_lo=30, len_hi=600, n_pad=1)
+    announce("f16 decode", "G", G, "D", D, "bs", bs, "layout", layout, "partition", part)
+    dw = M.setup(w, layout=layout, write_step=True)
     kc16 = dw.key_cache.to(torch.float16)
     vc16 = dw.value_cache.to(torch.float16)
     q16 = dw.query.to(torch.float16)
     out = torch.empty(w.query_shape, dtype=torch.float32, device="cuda")
+    ws = None
+    if part != 0:
+        nbytes = P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, part)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     P.pa_decode(out, q16, kc16, vc16, dw.block_tables, dw.context_lens, dw.max_context_len,
-                w.scale, partition_size=0)
+                w.scale, layout=layout, partition_size=part, workspace=ws)
     torch.cuda.synchronize()
     st = build_state(w)
-    kc, vc = build_pool(w, st, include_step=True)
+    kc, vc = build_pool(w, st, layout=layout, include_step=True)
     f16 = lambda x: A.bits_to_f64(x, "bf16").astype(np.float16).view(np.uint16)  # noqa: E731
     ref = A.decode_ref(f16(w.query), f16(kc), f16(vc), st.block_tables, w.context_lens, w.scale,
-                       w.bs, "f16")
+                       w.bs, "f16", layout)
     err, where = max_abs(out.cpu().numpy(), ref)
     assert err <= TOL["f16"], (err, where)
 

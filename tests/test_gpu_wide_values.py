@@ -4,14 +4,15 @@ head and grouped kernels, single pass and split-K), causal packed prefill
 (fresh prompts and prefix + suffix) and cascade decode, each held to the
 same absolute tolerance as the N(0, 1) workloads: max-abs 2e-3 against the
 fp64 oracle with fp32 output.  The kernels' weights carry at least 22
-significant bits (fp32 in decode, two f16 terms in the prefill's PV
-products), so the error stays well below 2e-3 at these ranges.
+significant bits (fp32 in the per-head decode, three bf16 terms in the
+grouped decode, two f16 terms in the prefill's PV products), so the error
+stays well below 2e-3 at these ranges.
 
-Plus bf16 values past the f16 range in the prefill (2^17 and 2^40 times a
-block of one sequence's V, in a later key tile): from that tile on the
-prefill holds V scaled by a power of two (its fp32 sums rescaled exactly).
-There the bound is the one an fp32 kernel can keep, 2e-3 relative to the
-output's magnitude.
+Plus bf16 values past the f16 range (2^17 and 2^40 times a block of one
+sequence's V) in decode, in the prefill (in a later key tile: from that tile
+on the prefill holds V scaled by a power of two, its fp32 sums rescaled
+exactly) and in a cascade's shared prefix.  There the bound is the one an
+fp32 kernel can keep, 2e-3 relative to the output's magnitude.
 """
 import numpy as np
 import pytest
@@ -204,3 +205,43 @@ def test_cascade_bf16_values_beyond_f16_range_in_shared_prefix(shift):
             err = float(np.max(np.abs(got[s, h] - ref)))
             assert err <= tol, (part, s, h, err, tol)
         announce("partition", part, "ok")
+
+
+@pytest.mark.parametrize("shift", [17, 40])
+@pytest.mark.parametrize("G", [1, 8])
+def test_decode_bf16_values_beyond_f16_range(G, shift):
+    """bf16 V values of magnitude 2^shift in one block of a sequence (not its
+    first): the per-head kernel multiplies fp32 weights with V converted
+    exactly to fp32, the grouped kernel three bf16 weight terms with V as it
+    is, so no value range needs special handling; every row compared with the
+    plain definition relative to the output's size, single pass and
+    split-K."""
+    need_gpu()
+    w = workloads.make(3, S=5, H=4 * G, Hkv=4, len_median=400, len_cap=1200)
+    announce("decode V beyond f16 range", "G", G, "2^", shift)
+    dw = M.setup(w, layout=P.HND, write_step=True)
+    st = build_state(w)
+    s0 = int(np.argmax(w.context_lens))
+    assert int(w.context_lens[s0]) > 96
+    big = np.arange(64, 96)  # one block of 32 positions, past the first 64-token tile
+    slots = torch.from_numpy(st.seq_slots[s0][big].astype(np.int64)).cuda()
+    blk, off = slots // w.bs, slots % w.bs
+    dw.value_cache[blk, :, off] *= 2.0 ** shift  # exact: exponent shift (HND pool)
+    qf = A.bits_to_f64(w.query, w.dtype)
+    refs = {}
+    for s in range(w.S):
+        K, V = w.kv(s)
+        for h in range(w.H):
+            g = h // w.G
+            Kf, Vf = A.bits_to_f64(K[:, g], w.dtype), A.bits_to_f64(V[:, g], w.dtype)
+            if s == s0:
+                Vf[big] *= 2.0 ** shift
+            refs[s, h], _ = A.attention_dense(qf[s, h], Kf, Vf, w.scale)
+    for part in (0, 64, -1):
+        got = _decode(dw, part)
+        assert np.all(np.isfinite(got))
+        for (s, h), ref in refs.items():
+            tol = TOL[w.dtype] * max(1.0, float(np.max(np.abs(ref))))
+            err = float(np.max(np.abs(got[s, h] - ref)))
+            assert err <= tol, (part, s, h, err, tol)
+    announce("ok")
