@@ -102,7 +102,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // which measured 1% slower on the long-context batch and 0.3% faster on the
 // 70B-like one); f16 to 161, so it runs 3 waves all the same (its 3-wave
 // bound spilled).
-template <int G, int D, bool FP8, pa_dtype DT>
+template <int G, int D, bool FP8>
 constexpr int kMfmaMinWaves = (D >= 128 && (G >= 16 || !FP8)) ? 2 : 3;
 
 // PV on matrix cores, O^T[16 d x 16 heads] += V^T P^T over 16 tokens: a =
@@ -150,7 +150,7 @@ struct PvWeights<true> {  // bf16 V: p = t0 + t1 + t2, three bf16 terms (~24 bit
 
 // DT = the query's type (and the cache's, unless FP8).
 template <pa_dtype DT, int D, int G, bool OFF32, bool FP8>
-__global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D, FP8, DT>)) void decode_mfma_kernel(
+__global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D, FP8>)) void decode_mfma_kernel(
     const DecodeParams p) {
   static_assert(DT == PA_BF16 || DT == PA_F16, "queries are bf16 or f16");
   static_assert(G == 4 || G == 8 || G == 16, "group size 4, 8 or 16");
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D, FP8, DT>)) voi
   const int bs_mask = (1 << lbs) - 1;
 
   const int tl = lane % kTile;  // QK: token of the tile, and head of the B operand / scores
-  const int q4 = lane / kTile;  // quarter of the row this lane loads
+  const int q4 = lane / kTile;  // quarter of the K row this lane reads back (its MFMA k-slots)
 
   // Element d held in slot e of MFMA k-block j by lanes of quarter q4: a
   // lane reads pieces q4, q4 + 4, ... of its K row from LDS -- FP8: 16
@@ -232,10 +232,10 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D, FP8, DT>)) voi
   // reach LDS as they are, and the MFMA lanes read back their quarters.
   const int lr = lane / PPR, lp = lane % PPR;
 
-  uint4* sK = reinterpret_cast<uint4*>(smem) + wave * (kWaveK + kWaveV);  // raw E4M3 rows
-  uint4* sV = sK + kWaveK;                                                // f16 rows
+  uint4* sK = reinterpret_cast<uint4*>(smem) + wave * (kWaveK + kWaveV);  // K rows as stored
+  uint4* sV = sK + kWaveK;                                 // V rows, 16-bit (FP8: as f16)
   // PV A operand: V^T[d = 16 b + tl][token 4 q4 + j], j = 0..3, from the
-  // wave's f16 rows (row stride VSTR pieces) by one transposing read per
+  // wave's 16-bit V rows (row stride VSTR pieces) by one transposing read per
   // block: lane tl of quarter q4 addresses row 4 q4 + tl / 4, columns
   // 16 b + 4 (tl % 4) .. +3
   const _Float16* vh =
