@@ -20,7 +20,11 @@ leave dirty lines whose write-back then lands inside the next step -- about
 20 us on the long-context step); HIP events recorded on the stream the
 kernels run on bracket each kernel.  ms_per_step is the mean event-timed step (write +
 attention, flush excluded); medians, minima and 90th percentiles are listed
-per kernel.
+per kernel.  The events are created with hipEventDisableSystemFence, the
+flag HIP documents for events that only time work: a default event (torch's)
+ends its recording with a system-scope fence -- a write-back and invalidate
+of the caches between two kernels -- which added 4-5 us to a four-event
+decode step and is no part of the path.
 
 --kv fp8 runs a workload over FP8 (E4M3) pools: the cache write quantises,
 decode and prefill read one byte per element.
@@ -61,6 +65,51 @@ KERNEL_SOURCES = {
 }
 FLUSH_BYTES = 512 << 20      # > the 256 MB memory-side cache (MALL)
 PROBE_BYTES = 4 << 30        # streaming-read ceiling buffer
+
+
+_HIP = None
+
+
+class TimingEvent:
+    """A HIP timing event without the system-scope fence at its recording
+    (hipEventDisableSystemFence), recorded on a given stream; elapsed_time in
+    milliseconds, like torch's events.  The HIP runtime is the one torch
+    loaded (same soname), so torch's stream handles are valid here."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        global _HIP
+        import ctypes
+        if _HIP is None:
+            import torch  # noqa: F401  (loads the HIP runtime first)
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            _HIP = h
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        rc = _HIP.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = _HIP.hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        ms = self._ct.c_float()
+        rc = _HIP.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if _HIP is not None and self.h:
+            _HIP.hipEventDestroy(self.h)
 
 
 def decode_kernel_kind(w, fp8: bool = False) -> str:
@@ -196,7 +245,7 @@ def copy_blocks_bench(args):
                                                               device="cuda")
 
     def step():
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record(stream)
         P.pa_copy_blocks(dw.key_cache, dw.value_cache, pairs, layout)
         b.record(stream)
@@ -233,7 +282,7 @@ def copy_blocks_bench(args):
     for i in range(max(args.warmup, 5) + args.steps):
         if flush_buf is not None:
             flush_buf.sum() if args.flush == "read" else flush_buf.fill_(float(i & 0xFF))
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record(stream)
         fill_buf.fill_(i)
         b.record(stream)
@@ -458,7 +507,7 @@ def main():
             flush_buf.sum()
 
     def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        return [TimingEvent() for _ in range(4)]
 
     def timed(step_fn, steps, warmup):
         """warmup untimed steps (-1: enough to fill 0.3 s, at least 5), then
@@ -512,7 +561,7 @@ def main():
         pev = []
         for i in range(13):
             flush(i)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = TimingEvent(), TimingEvent()
             a.record(stream)
             P.pa_stream_read_probe(buf, sink)
             b.record(stream)

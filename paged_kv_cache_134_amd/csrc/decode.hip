@@ -232,23 +232,21 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_wide_kernel(cons
 // Split-K dispatch list, one workgroup.  Hardware dispatch starts workgroups
 // in id order, so the list orders the partitions largest first: every full
 // partition (partition_size tokens), sequence by sequence, then each
-// sequence's shorter last partition in kItemBuckets classes of decreasing
-// size (a class spans partition_size / kItemBuckets tokens; the order
+// sequence's shorter last partition in kItemClasses classes of decreasing
+// size (a class spans partition_size / kItemClasses tokens; the order
 // within a class is whatever the LDS atomics give).  Long work then starts
 // early and the shortest fills the end (longest-processing-time-first
 // scheduling), and no empty workgroup is dispatched before the last item:
 // the grid's unused tail is dispatched last and exits at once.  Only an
 // order: every partial and the reduce are those of the (pairs, partitions)
 // grid, so results do not depend on it.
-constexpr int kItemBuckets = 64;
-
 __global__ __launch_bounds__(kDecodeThreads) void decode_items_kernel(const DecodeParams p) {
   __shared__ int32_t red[kDecodeWaves];
-  __shared__ int32_t sCnt[kItemBuckets];  // shorter partitions per size class, then the class cursors
+  __shared__ int32_t sCnt[kItemClasses];  // shorter partitions per size class, then the class cursors
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int S = p.num_seqs, hkv = p.num_kv_heads, P = p.partition_size;
   int4* items = reinterpret_cast<int4*>(p.items);
-  auto bucket = [&](int r) { return (P - r) * kItemBuckets / P; };  // r in [1, P): 0 = longest
+  auto bucket = [&](int r) { return (int)((int64_t)(P - r) * kItemClasses / P); };  // r in [1, P): 0 = longest
   // exclusive prefix of x over the workgroup; total = the sum
   auto scan = [&](int x, int& total) -> int {
     int incl = x;
@@ -269,7 +267,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_items_kernel(const Deco
     __syncthreads();  // red is rewritten by the next scan
     return before + incl - x;
   };
-  if (tid < kItemBuckets) sCnt[tid] = 0;
+  if (tid < kItemClasses) sCnt[tid] = 0;
   __syncthreads();
   // full partitions in sequence order; shorter ones counted per class.  A
   // batch of at most kDecodeThreads sequences is read once (L0 is kept for
@@ -289,14 +287,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_items_kernel(const Deco
   }
   __syncthreads();
   if (wave == 0) {  // class cursors: after the full partitions, longest class first
-    const int c = lane < kItemBuckets ? sCnt[lane] : 0;
+    const int c = lane < kItemClasses ? sCnt[lane] : 0;
     int incl = c;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
       const int y = __shfl_up(incl, d);
       if (lane >= d) incl += y;
     }
-    if (lane < kItemBuckets) sCnt[lane] = full_base + incl - c;
+    if (lane < kItemClasses) sCnt[lane] = full_base + incl - c;
     rem_total = __shfl(incl, kWave - 1);
   }
   __syncthreads();
@@ -379,7 +377,19 @@ hipError_t launch_decode_main(const DecodeArgs& a, hipStream_t stream) {
   const bool listed = a.items && a.partition_size > 0 && a.key_begin == 0 && a.part_base == 0 &&
                       !a.all_partial && group && grid.x >= 2u * (unsigned)device_cus() &&
                       items <= 0x7FFFFFFF;
-  if (listed) {
+  if (listed && a.num_seqs <= dec::kDecodeThreads &&
+      (a.partition_size & (a.partition_size - 1)) == 0) {
+    // Up to kDecodeThreads sequences and a power-of-two partition size: each
+    // workgroup derives its item itself, and the list kernel's launch leaves
+    // the step (70B-like batch, same box, alternating builds: step 156.1-156.3
+    // -> 153.3-154.0 us; FP8 100.0-100.1 -> 98.6-99.5 us).  Larger batches
+    // would read more lengths per workgroup than the list costs.
+    p.items = nullptr;
+    p.item_count = nullptr;
+    p.inline_items = true;
+    p.log2_part = __builtin_ctz((unsigned)a.partition_size);
+    grid = dim3((unsigned)items);
+  } else if (listed) {
     hipLaunchKernelGGL(dec::decode_items_kernel, dim3(1), dim3(dec::kDecodeThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

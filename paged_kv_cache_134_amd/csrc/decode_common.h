@@ -51,6 +51,11 @@ struct DecodeParams {
   int32_t* item_count;
   int32_t* items;
   int32_t num_seqs;
+  // No list but the same order, derived by each workgroup from the context
+  // lengths (decode_item_inline): at most kDecodeThreads sequences and a
+  // power-of-two partition_size, 1 << log2_part.
+  bool inline_items;
+  int32_t log2_part;
 };
 
 // The (sequence, kv head, partition) of this workgroup: from the dispatch
@@ -70,6 +75,118 @@ __device__ __forceinline__ bool decode_item(const DecodeParams& p, bool last_fir
   kvh = blockIdx.x % p.num_kv_heads;
   s = blockIdx.x / p.num_kv_heads;
   part = last_first ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
+  return true;
+}
+
+// Sum over the 64 lanes of a wave, integers (every lane receives it).
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) x += __shfl_xor(x, d);
+  return x;
+}
+
+// Size classes of the shorter last partitions in the split-K dispatch order
+// (the list builder's and decode_item_inline's).
+constexpr int kItemClasses = 64;
+static_assert(kItemClasses == kWave, "one class per lane");
+
+// Size class of a last partition shorter than 1 << lp by `short_by` tokens
+// (1 .. 2^lp - 1): 0 = longest.
+__device__ __forceinline__ int item_class(int short_by, int lp) {
+  return (int)(((int64_t)short_by * kItemClasses) >> lp);
+}
+
+// The dispatch list's order without the list: workgroup b takes item b =
+// j * num_kv_heads + kv head, where j numbers every full partition, sequence
+// by sequence, then each sequence's shorter last partition by size class
+// (partition_size / kItemClasses tokens each), longest class first and by
+// sequence within a class.  Every workgroup derives it from the context
+// lengths of the (at most kDecodeThreads) sequences: an exclusive scan of
+// the full-partition counts for the first part, and for the second one
+// lane mask per (wave, class) -- a sequence's place is its class's start
+// plus the same-class sequences before it.  False past the last item (the
+// grid is an upper bound); L receives the sequence's context length.  Only
+// an order: the partials are those of the (pairs, partitions) grid.
+__device__ __forceinline__ bool decode_item_inline(const DecodeParams& p, int& s, int& kvh, int& part,
+                                                   int& L) {
+  static_assert(kDecodeWaves == 4, "one length per thread: kDecodeWaves x kWave sequences");
+  __shared__ int32_t sRed[kDecodeWaves];
+  __shared__ unsigned long long sMask[kDecodeWaves][kItemClasses];
+  __shared__ int32_t sCur[kItemClasses];
+  __shared__ int32_t sPick[3];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int S = p.num_seqs, lp = p.log2_part, P = 1 << lp;
+  const int j = blockIdx.x / p.num_kv_heads;
+  // Each wave reads every length (sequence lane + 64 k in Ls[k]) and counts
+  // the items itself, so a workgroup past the last item leaves before any
+  // barrier.
+  int Ls[kDecodeWaves];
+  int n = 0;
+#pragma unroll
+  for (int k = 0; k < kDecodeWaves; ++k) {
+    const int t = lane + kWave * k;
+    Ls[k] = t < S ? p.context_lens[t] : 0;
+    n += (Ls[k] >> lp) + ((Ls[k] & (P - 1)) != 0);
+  }
+  if (j >= wave_sum_int(n)) return false;
+  // this thread's sequence is tid
+  const int Lt = wave == 0 ? Ls[0] : wave == 1 ? Ls[1] : wave == 2 ? Ls[2] : Ls[3];
+  const int f = Lt >> lp, r = Lt & (P - 1);
+  const int c = r > 0 ? item_class(P - r, lp) : -1;
+  for (int i = tid; i < kDecodeWaves * kItemClasses; i += kDecodeThreads) (&sMask[0][0])[i] = 0ull;
+  int incl = f;  // inclusive scan of f within the wave
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == kWave - 1) sRed[wave] = incl;
+  __syncthreads();
+  if (c >= 0) atomicOr(&sMask[wave][c], 1ull << lane);
+  int before = 0, F = 0;
+#pragma unroll
+  for (int w = 0; w < kDecodeWaves; ++w) {
+    if (w < wave) before += sRed[w];
+    F += sRed[w];
+  }
+  __syncthreads();
+  if (j < F) {  // a full partition
+    const int fx = before + incl - f;
+    if (fx <= j && j < fx + f) {
+      sPick[0] = tid;
+      sPick[1] = j - fx;
+      sPick[2] = Lt;
+    }
+  } else {  // a shorter last partition (j is the same for the whole workgroup)
+    if (wave == 0) {  // lane = class: its start after the full partitions
+      int cnt = 0;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) cnt += __popcll(sMask[w][lane]);
+      int ci = cnt;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(ci, d);
+        if (lane >= d) ci += y;
+      }
+      sCur[lane] = F + ci - cnt;
+    }
+    __syncthreads();
+    if (c >= 0) {
+      int pos = sCur[c] + __popcll(sMask[wave][c] & ((1ull << lane) - 1ull));
+      for (int w = 0; w < wave; ++w) pos += __popcll(sMask[w][c]);
+      if (pos == j) {
+        sPick[0] = tid;
+        sPick[1] = f;
+        sPick[2] = Lt;
+      }
+    }
+  }
+  __syncthreads();
+  s = __builtin_amdgcn_readfirstlane(sPick[0]);
+  part = __builtin_amdgcn_readfirstlane(sPick[1]);
+  L = __builtin_amdgcn_readfirstlane(sPick[2]);
+  kvh = blockIdx.x % p.num_kv_heads;
   return true;
 }
 

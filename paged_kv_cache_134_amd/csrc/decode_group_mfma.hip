@@ -172,15 +172,19 @@ __global__ __launch_bounds__(kDecodeThreads, (kMfmaMinWaves<G, D, FP8>)) void de
   __shared__ __align__(16) char smem[kLds];
   __shared__ float sM[kDecodeWaves][G], sL[kDecodeWaves][G];
 
-  int s, kvh, item;
-  if (!decode_item(p, true, s, kvh, item)) return;
+  int s, kvh, item, L;
+  if (p.inline_items) {
+    if (!decode_item_inline(p, s, kvh, item, L)) return;
+  } else {
+    if (!decode_item(p, true, s, kvh, item)) return;
+    L = p.context_lens[s];
+  }
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
   // Tokens [t0, t1): one partition (split-K) or the whole context (single
   // pass).
-  const int L = p.context_lens[s];
   const int P = p.partition_size;
   const int part = item;
   int t0 = 0, t1 = L;

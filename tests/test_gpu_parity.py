@@ -163,15 +163,18 @@ def test_many_partials_per_row(G, kv):
 
 
 @pytest.mark.parametrize("S,Hkv,G,D,kv", [
-    (128, 4, 4, 64, "bf16"),   # 512 pairs: the one-pass list (<= 256 sequences)
-    (300, 2, 8, 64, "bf16"),   # 600 pairs, 300 sequences: the batched list
-    (130, 4, 4, 128, "e4m3"),  # the FP8 grouped kernel reads the same list
+    (128, 4, 4, 64, "bf16"),   # 512 pairs, <= 256 sequences: order derived in the kernel
+    (300, 2, 8, 64, "bf16"),   # 600 pairs, 300 sequences: the list kernel, batched
+    (130, 4, 4, 128, "e4m3"),  # the FP8 grouped kernel, same order
 ])
 def test_grouped_decode_dispatch_list(S, Hkv, G, D, kv):
     """Grouped split-K decode over at least 512 (sequence, kv head) pairs
-    runs its partitions from the largest-first dispatch list.  Lognormal
-    lengths, some contexts set to 0 and to exact multiples of the partition
-    size on the device; every row against the oracle, empty ones zero."""
+    runs its partitions largest first: at most 256 sequences and a
+    power-of-two partition size derive the order in each workgroup, more
+    sequences or another size take the list kernel (partition 80 here).
+    Lognormal lengths, some contexts set to 0 and to exact multiples of the
+    partition size on the device; every row against the oracle, empty ones
+    zero."""
     need_gpu()
     w = workloads.make(3, S=S, H=G * Hkv, Hkv=Hkv, D=D, bs=16, len_median=120, len_cap=700)
     announce("dispatch list", S, Hkv, G, D, kv)
@@ -187,7 +190,7 @@ def test_grouped_decode_dispatch_list(S, Hkv, G, D, kv):
     dw.context_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
     ref = A.decode_ref(w.query, kc, vc, st.block_tables, np.maximum(lens, 1), w.scale, w.bs, w.dtype,
                        **kw)
-    for ps in (part, -1):
+    for ps in (part, 80, -1):
         out = torch.full(w.query_shape, float("nan"), dtype=torch.float32, device="cuda")
         nbytes = P.pa_decode_workspace_size(w.S, w.H, w.D, dw.max_context_len, ps)
         ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")  # stale bytes
