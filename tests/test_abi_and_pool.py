@@ -203,21 +203,20 @@ def _pool_and_model(nb, bs, order):
 def test_auto_partition_policy():
     """Host policy only (no device needed; without one 256 compute units are
     assumed): the per-head kernel splits at 512, the grouped kernel takes the
-    largest partition that keeps about two workgroups per resident slot."""
+    largest partition that keeps about four workgroups per compute unit."""
     ap = P.pa_decode_auto_partition
     assert ap(64, 32, 32, P.PA_BF16, 512, 0) == 0          # short contexts: one pass
     assert ap(64, 32, 32, P.PA_BF16, 2035, 75661) == 512   # MHA: per-head kernel
     assert ap(4, 8, 8, P.PA_F32, 300, 448) == 0
     assert ap(4, 64, 8, P.PA_F32, 4000, 0) == 512          # fp32 never takes the grouped kernel
-    # 16-bit caches: 2 resident workgroups per compute unit, so at least
-    # 2 * 2 * 256 = 1024 workgroups: kv heads * (total / ps + num_seqs / 2)
+    # at least 4 * 256 = 1024 workgroups: kv heads * (total / ps + num_seqs / 2)
     assert ap(128, 64, 8, P.PA_BF16, 8192, 207090) == 2048  # lognormal GQA batch: 8 * (101 + 64)
     assert ap(8, 64, 8, P.PA_BF16, 131072, 8 * 131072) == 8192  # 8 * (128 + 4) = 1056
     # unknown total: num_seqs * max_context_len is assumed
     assert ap(8, 64, 8, P.PA_BF16, 131072, 0) == 8192
-    # FP8 caches: 3 per compute unit, at least 1536 workgroups
-    assert ap(8, 64, 8, P.PA_FP8_E4M3, 131072, 8 * 131072) == 4096  # 8 * (256 + 4) = 2080
-    assert ap(128, 64, 8, P.PA_FP8_E4M3, 8192, 207090) == 1024    # 2048 gives 1320
+    # FP8 caches: the same target
+    assert ap(8, 64, 8, P.PA_FP8_E4M3, 131072, 8 * 131072) == 8192
+    assert ap(128, 64, 8, P.PA_FP8_E4M3, 8192, 207090) == 2048
     for args in [(1, 8, 1, P.PA_BF16, 600, 0), (3, 48, 3, P.PA_F16, 100000, 0)]:
         ps = ap(*args)
         assert ps >= 512 and ps % 16 == 0
