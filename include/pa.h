@@ -186,9 +186,10 @@ pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
  *                   -1 = chosen by the library from the shape
  *   workspace    (device) >= pa_decode_workspace_size(...) bytes when split-K
  *                is used (may be NULL for partition_size 0): the partials
- *                and, for the grouped kernels, the partition kernel's
- *                dispatch list (largest partitions first); no content is
- *                needed on entry
+ *                and, for the grouped kernels over more than 256
+ *                sequences or with a partition size that is not a power of
+ *                two, the partition kernel's dispatch list (largest
+ *                partitions first); no content is needed on entry
  * Supported: head_size 64 or 128; num_heads / num_kv_heads in {1,2,4,8,16};
  * block_size a power of two in [1, 1024]; PA_LAYOUT_NHD or PA_LAYOUT_HND.
  * Results are bitwise deterministic for a fixed launch configuration and do
@@ -202,7 +203,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
  * Partition size for this decode shape (0 = single pass): 512 for the
  * per-head kernel (group size 1 or 2, or fp32), a larger power of two for
  * the grouped kernels (group size 4, 8 or 16 with bf16, f16 or
- * PA_FP8_E4M3 caches) while about two workgroups per resident slot remain.
+ * PA_FP8_E4M3 caches) while about four workgroups per compute unit remain.
  * total_context_len is the sum of context_lens when the caller knows it
  * (<= 0: unknown, num_seqs * max_context_len is assumed); partition_size -1
  * in the decode calls resolves with it unknown.  Never below 512, so a

@@ -164,6 +164,7 @@ def test_many_partials_per_row(G, kv):
 
 @pytest.mark.parametrize("S,Hkv,G,D,kv", [
     (128, 4, 4, 64, "bf16"),   # 512 pairs, <= 256 sequences: order derived in the kernel
+    (256, 2, 8, 64, "bf16"),   # the most sequences the kernel orders itself (every lane holds one)
     (300, 2, 8, 64, "bf16"),   # 600 pairs, 300 sequences: the list kernel, batched
     (130, 4, 4, 128, "e4m3"),  # the FP8 grouped kernel, same order
 ])
