@@ -226,14 +226,17 @@ int device_cus() {
 // Grouped kernel (one workgroup reads a kv head for all G query heads, so a
 // workgroup has G times the work per token): the largest power-of-two
 // partition, at least 512 and shorter than the longest context, that still
-// leaves about four workgroups per compute unit for balance; a workgroup's
-// fixed costs (block-table window, the first tiles' latency, the merge, the
-// partial) are then spread over as many tiles as possible.  The same target
-// serves FP8 caches, though their kernel holds 3 workgroups per compute unit
-// at head size 128 rather than 2.  (Long-context batch, 16-bit: 739 / 700 /
-// 669 / 651 / 645 us at 512 / 1024 / 2048 / 4096 / 8192; 70B-like: 168 /
-// 150 / 143 us at 512 / 1024 / 2048.  FP8: 70B-like 85.4 / 80.1 us at 1024
-// / 2048, long context 336 us at both 4096 and 8192.)
+// leaves about three workgroups per compute unit (estimated) for balance; a
+// workgroup's fixed costs (block-table window, the first tiles' latency, the
+// merge, the partial, and its share of deriving the dispatch order) are then
+// spread over as many tiles as possible.  The same target serves FP8
+// caches, though their kernel holds 3 workgroups per compute unit at head
+// size 128 rather than 2.  (Long-context batch, 16-bit: 739 / 700 / 669 /
+// 651 / 645 us at 512 / 1024 / 2048 / 4096 / 8192.  70B-like lognormal
+// batch, partition span: 168 / 150 / 143 us at 512 / 1024 / 2048 with the
+// list kernel; with the order derived in the kernel 141.3-142.3 us at 2048
+// and 139.2-139.5 us at 4096, FP8 85.4 / 80.2 / 76.1 us at 1024 / 2048 /
+// 4096.  Long context FP8: 336 us at both 4096 and 8192.)
 extern "C" int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_heads,
                                             int32_t num_kv_heads, pa_dtype kv_dtype,
                                             int32_t max_context_len, int64_t total_context_len) {
@@ -241,7 +244,7 @@ extern "C" int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_heads,
   if (!pa::decode_uses_group_kernel(kv_dtype, num_heads / num_kv_heads)) return 512;
   const int64_t total = total_context_len > 0 ? total_context_len
                                               : (int64_t)num_seqs * max_context_len;
-  const int64_t want = 4 * (int64_t)pa::device_cus();
+  const int64_t want = 3 * (int64_t)pa::device_cus();
   for (int32_t ps = 8192; ps > 512; ps /= 2) {
     if (ps >= max_context_len) continue;
     const int64_t wgs = (int64_t)num_kv_heads * (total / ps + num_seqs / 2);

@@ -203,20 +203,21 @@ def _pool_and_model(nb, bs, order):
 def test_auto_partition_policy():
     """Host policy only (no device needed; without one 256 compute units are
     assumed): the per-head kernel splits at 512, the grouped kernel takes the
-    largest partition that keeps about four workgroups per compute unit."""
+    largest partition that keeps about three workgroups per compute unit."""
     ap = P.pa_decode_auto_partition
     assert ap(64, 32, 32, P.PA_BF16, 512, 0) == 0          # short contexts: one pass
     assert ap(64, 32, 32, P.PA_BF16, 2035, 75661) == 512   # MHA: per-head kernel
     assert ap(4, 8, 8, P.PA_F32, 300, 448) == 0
     assert ap(4, 64, 8, P.PA_F32, 4000, 0) == 512          # fp32 never takes the grouped kernel
-    # at least 4 * 256 = 1024 workgroups: kv heads * (total / ps + num_seqs / 2)
-    assert ap(128, 64, 8, P.PA_BF16, 8192, 207090) == 2048  # lognormal GQA batch: 8 * (101 + 64)
+    # at least 3 * 256 = 768 workgroups: kv heads * (total / ps + num_seqs / 2)
+    assert ap(128, 64, 8, P.PA_BF16, 8192, 207090) == 4096  # lognormal GQA batch: 8 * (50 + 64) = 912
+    assert ap(128, 64, 8, P.PA_BF16, 8192, 100000) == 2048  # 8 * (24 + 64) = 704 at 4096
     assert ap(8, 64, 8, P.PA_BF16, 131072, 8 * 131072) == 8192  # 8 * (128 + 4) = 1056
     # unknown total: num_seqs * max_context_len is assumed
     assert ap(8, 64, 8, P.PA_BF16, 131072, 0) == 8192
     # FP8 caches: the same target
     assert ap(8, 64, 8, P.PA_FP8_E4M3, 131072, 8 * 131072) == 8192
-    assert ap(128, 64, 8, P.PA_FP8_E4M3, 8192, 207090) == 2048
+    assert ap(128, 64, 8, P.PA_FP8_E4M3, 8192, 207090) == 4096
     for args in [(1, 8, 1, P.PA_BF16, 600, 0), (3, 48, 3, P.PA_F16, 100000, 0)]:
         ps = ap(*args)
         assert ps >= 512 and ps % 16 == 0
