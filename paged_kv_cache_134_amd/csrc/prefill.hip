@@ -56,8 +56,7 @@
 //   * FP8 (E4M3) caches: K converts exactly to the query's type and V to f16
 //     on their way into LDS, so the products are those of a 16-bit cache;
 //     k_scale is folded into the softmax scale and v_scale into the final
-//     normalisation.  Their staging registers are half as many, so outside
-//     the prefix pass they run 3 waves per SIMD (the others 2).
+//     normalisation.  Every instantiation runs 2 waves per SIMD.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -163,14 +162,15 @@ __device__ __forceinline__ void fp8x8_to_f32(const uint4& v, float* out) {
 // mask) and writes a (max, sum, unnormalised output) partial instead of a
 // normalised row.  FP8: the caches hold E4M3 codes (partials then carry
 // v_scale, as the decode kernels' partials do).
-// Waves per SIMD the register budget is set for: the FP8 kernel's staging
-// registers are half as many (one byte per element), so outside the prefix
-// pass it fits 3 waves without spilling; the others fit 2.
-template <bool PREFIX, bool FP8>
-constexpr int kPrefillMinWaves = (FP8 && !PREFIX) ? 3 : 2;
+// Waves per SIMD the register budget is set for: 2 (218-220 VGPRs at head
+// size 128).  The FP8 kernel's staging registers are half as many, but with
+// the two-term weights a 3-wave bound spills it (12 VGPRs), and it measured
+// slower than at 2 waves (5c over FP8 pools: 2.17-2.22 ms against
+// 2.06 ms).
+constexpr int kPrefillMinWaves = 2;
 
 template <pa_dtype DT, int D, bool OFF32, bool PREFIX, bool FP8>
-__global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) void prefill_kernel(
+__global__ __launch_bounds__(kPrefillThreads, kPrefillMinWaves) void prefill_kernel(
     const PrefillParams p) {
   constexpr int CB = FP8 ? 1 : 2;               // cache bytes per element
   constexpr int KS = D / 16;                    // 16-wide k-steps over the head dim (QK)
@@ -538,27 +538,17 @@ __global__ __launch_bounds__(kPrefillThreads, (kPrefillMinWaves<PREFIX, FP8>)) v
       const f16x8_t pbl = __builtin_bit_cast(
           f16x8_t, make_uint4(pl[kb][4 * jp], pl[kb][4 * jp + 1], pl[kb][4 * jp + 2], pl[kb][4 * jp + 3]));
       const int col = (kb * 32 + jp * 16) * 2 + hf * 16;
-      if constexpr (kPrefillMinWaves<PREFIX, FP8> == 2) {
-        // every block's hi product before the lo products, so no product
-        // waits on the one just issued into the same accumulator (the
-        // 3-wave FP8 kernel has no registers for the A operands meanwhile)
-        f16x8_t a[DB];
+      // every block's hi product before the lo products, so no product
+      // waits on the one just issued into the same accumulator
+      f16x8_t a[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          a[db] = __builtin_bit_cast(f16x8_t, load16(sV + (db * 32 + lq) * VROW + col));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[db], pbh, o[db], 0, 0, 0);
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[db], pbl, o[db], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const f16x8_t a = __builtin_bit_cast(f16x8_t, load16(sV + (db * 32 + lq) * VROW + col));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pbh, o[db], 0, 0, 0);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pbl, o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < DB; ++db) {
+        a[db] = __builtin_bit_cast(f16x8_t, load16(sV + (db * 32 + lq) * VROW + col));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[db], pbh, o[db], 0, 0, 0);
       }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[db], pbl, o[db], 0, 0, 0);
     }
     }  // wave has visible keys in this tile
     __syncthreads();
